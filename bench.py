@@ -1,0 +1,218 @@
+"""Benchmark of the MoE-VQ routed-expert step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b1|b32|b8mx] [--no-cpu-baseline]
+
+One step = route (router product, softmax/top-k/renormalise, worklist) -> FC1 with
+SiLU*up -> FC2 with the weighted combine, for one batch of synthetic tokens whose
+activations already sit in HBM.  The default workload is decode batch 1 of a
+DeepSeek-style layer (H=7168, I=2048, 256 experts, top-8, VQ2 experts at 2.125
+bits/weight, all resident in one HBM slot pool).  Tokens are cycled from a pool of
+256 distinct pre-drawn tokens so consecutive steps touch different experts (the
+256 MB Infinity Cache holds about two steps' experts, not the pool).
+
+Prints one JSON line.  `value` is tokens/s of the whole step timed on the host
+between two device synchronisations; `roofline` rates the dominant kernel (FC1)
+by its algorithmic code+scale bytes per launch over its mean duration measured
+with HIP events on the launch stream inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOADS = {
+    "b1": "decode batch 1: H=7168 I=2048 E=256 top-8, VQ2 2.125 b/w, bf16 x ~N(0,1), 256 experts resident",
+    "b32": "decode batch 32: H=7168 I=2048 E=256 top-8, VQ2, router logits with Zipf(1.1) expert popularity",
+    "b8mx": "decode batch 8: 52 most-routed experts MXFP4, 204 VQ2, Zipf(1.1) routing",
+}
+
+
+def expert_stream_bytes(dev, experts):
+    """Exact code+scale bytes of whole experts (gate, up, down), without alignment padding."""
+    H, I = dev.hidden, dev.inter
+    tot = 0
+    for e in experts:
+        f = int(dev.formats[e])
+        if f == 1:
+            tot += 3 * H * I // 4 + 3 * (H * I // 128) * 2
+        else:
+            tot += 3 * H * I // 2 + 3 * (H * I // 32)
+    return tot
+
+
+def fc1_exact_bytes(dev, experts):
+    H, I = dev.hidden, dev.inter
+    tot = 0
+    for e in experts:
+        f = int(dev.formats[e])
+        tot += (2 * I * H // 4 + 2 * (I * H // 128) * 2) if f == 1 else (2 * I * H // 2 + 2 * (I * H // 32))
+    return tot
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "bit_vector_quantised_amd", "csrc"))):
+        with open(os.path.join(ROOT, "bit_vector_quantised_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(syn, x_pool_np, top_k, budget_s=15.0):
+    """The fp64 oracle (as it is) on consecutive tokens of the same pool, until about
+    budget_s seconds of work; returns tokens/s and the sample description."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    t0 = time.perf_counter()
+    n = 0
+    T = syn.cfg.n_tokens
+    while True:
+        x = x_pool_np[(n * T) % x_pool_np.shape[0]:][:T]
+        oracle.forward(syn, oracle.x_value(x, "bf16"), top_k)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n * T / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{n} step(s) of {T} token(s) of the same workload in {dt:.1f} s; fp64 numpy oracle, "
+                      f"decode single-threaded, products on {blas_threads} BLAS thread(s); "
+                      f"host has {len(os.sched_getaffinity(0))} usable cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="b1", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the routed-expert step is measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from bit_vector_quantised_amd import _lib
+    from bit_vector_quantised_amd.layer import DeviceLayer, Step
+
+    torch.cuda.set_device(0)
+    cfg = synth.PRESETS[args.config]
+    T, k = cfg.n_tokens, cfg.top_k
+    print(f"[bench] building {args.config} layer ({cfg.n_experts} experts)", file=sys.stderr, flush=True)
+    syn_dev = synth.SynthLayer(cfg, cache=False)
+    dev = DeviceLayer.from_synth(syn_dev)
+    n_pool = 256 if T == 1 else max(8, 256 // T) * T
+    x_pool_np = synth.SynthLayer(cfg, cache=False).x(n=n_pool, stream=7)
+    x_pool = torch.from_numpy(x_pool_np.view(np.int16)).cuda().view(torch.bfloat16)
+    n_batches = n_pool // T
+    step = Step(dev, T)
+    stream = torch.cuda.current_stream()
+
+    def run_step(i, ev=None):
+        xb = x_pool[(i % n_batches) * T:(i % n_batches + 1) * T]
+        step.route(xb)
+        if ev is not None:
+            ev[0].record(stream)
+        step.fc1(T)
+        if ev is not None:
+            ev[1].record(stream)
+        step.fc2(T)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    st, info = step.check()
+    if st != _lib.OK:
+        raise RuntimeError(f"step status {st} ({_lib.strerror(st)}), expert {info}")
+
+    # distinct experts per step (for the algorithmic bytes), read outside the timed region
+    uniq, fc1_bytes, step_bytes = [], [], []
+    for i in range(n_batches):
+        run_step(i)
+        inf = step.info(T)
+        uniq.append(inf["n_active"])
+        fc1_bytes.append(fc1_exact_bytes(dev, inf["experts"]))
+        step_bytes.append(expert_stream_bytes(dev, inf["experts"]))
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    fc1_ms = [events[i][0].elapsed_time(events[i][1]) for i in range(args.steps)]
+    fc2_ms = [events[i][1].elapsed_time(events[i][2]) for i in range(args.steps)]
+    bidx = [(args.warmup + i) % n_batches for i in range(args.steps)]
+    fc1_b = float(np.mean([fc1_bytes[b] for b in bidx]))
+    step_b = float(np.mean([step_bytes[b] for b in bidx]))
+    fc1_avg_s = float(np.mean(fc1_ms)) * 1e-3
+    fc2_avg_s = float(np.mean(fc2_ms)) * 1e-3
+    achieved = fc1_b / fc1_avg_s / 1e9
+    code_stream = step_b / (fc1_avg_s + fc2_avg_s) / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_fc1_{args.config}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == source_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    out = {
+        "metric": "MoE-VQ layer tokens/s and code-stream HBM GB/s (% peak), batch 1 & 32",
+        "value": args.steps * T / dt,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16xfp16->fp32 (decoded VQ2 weights x fp16-staged activations, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "tokens_per_step": T, "hidden": cfg.hidden,
+                   "inter": cfg.inter, "n_experts": cfg.n_experts, "top_k": k,
+                   "unique_experts_per_step": float(np.mean([uniq[b] for b in bidx])),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "fc_kernel<16,MT,FC1> (FC1 gate/up decode + SiLU*up)",
+                     "bytes_per_launch": fc1_b, "mean_launch_us": fc1_avg_s * 1e6},
+        "code_stream": {"GBps": code_stream, "frac": code_stream / HBM_PEAK_GBPS,
+                        "fc1_us": fc1_avg_s * 1e6, "fc2_us": fc2_avg_s * 1e6, "bytes_per_step": step_b},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        syn_or = synth.SynthLayer(cfg)
+        out["cpu_baseline"] = cpu_baseline(syn_or, x_pool_np, k, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,267 @@
+// C ABI of the MoE-VQ routed-expert library: argument validation, workspace layout
+// and kernel launches.  Every check runs on the host before any HIP call; the
+// library allocates nothing and keeps no per-call state.
+#include <string.h>
+
+#include "moe_vq_internal.h"
+#include "moe_vq_launch.h"
+
+using namespace mvq;
+
+namespace {
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+// Record a failed HIP call and map it to MOE_VQ_EHIP.
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_VQ_OK;
+  g_last_hip_error = e;
+  return MOE_VQ_EHIP;
+}
+
+bool dims_ok(int H, int I, int E, int k) {
+  if (H < 128 || H > MAX_DIM || H % 128) return false;
+  if (I < 128 || I > MAX_DIM || I % 128) return false;
+  if (E < 1 || E > MAX_E) return false;
+  if (k < 1 || k > MAX_K || k > E) return false;
+  return true;
+}
+
+int check_layer(const moe_vq_layer* L) {
+  if (!L) return MOE_VQ_EINVAL;
+  if (!dims_ok(L->hidden, L->inter, L->n_experts, L->top_k)) return MOE_VQ_EINVAL;
+  if (!L->router_w || !L->codebook || !L->pool || !L->slots) return MOE_VQ_EINVAL;
+  if (((uintptr_t)L->pool & 255) || ((uintptr_t)L->codebook & 7) || ((uintptr_t)L->router_w & 15) ||
+      ((uintptr_t)L->slots & 7))
+    return MOE_VQ_EINVAL;
+  if (L->pool_bytes == 0) return MOE_VQ_EINVAL;
+  return MOE_VQ_OK;
+}
+
+int check_ws(const moe_vq_layer* L, int T, const void* ws, size_t ws_bytes) {
+  if (!ws || ((uintptr_t)ws & 255)) return MOE_VQ_EINVAL;
+  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, T);
+  if (ws_bytes < W.total) return MOE_VQ_ENOSPACE;
+  return MOE_VQ_OK;
+}
+
+// Compute units of the current device, queried once per device (idempotent cache).
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
+
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+FcArgs make_fc_args(const moe_vq_layer* L, int T, void* ws, const WsLayout& W, bool fc1) {
+  FcArgs a{};
+  a.pool = L->pool;
+  a.codebook = static_cast<const uint16_t*>(L->codebook);
+  a.hdr = at<const uint32_t>(ws, W.hdr);
+  a.act_start = at<const int32_t>(ws, W.act_start);
+  a.act_off = at<const uint64_t>(ws, W.act_off);
+  a.act_fmt = at<const uint32_t>(ws, W.act_fmt);
+  a.grp = at<const int32_t>(ws, fc1 ? W.grp1 : W.grp2);
+  a.rec = at<const GroupRec>(ws, fc1 ? W.rec1 : W.rec2);
+  a.pair_list = at<const int32_t>(ws, W.pair_list);
+  a.pair_w = at<const float>(ws, W.pair_w);
+  a.x_h = at<const uint16_t>(ws, W.x_h);
+  a.x_sc = at<const float>(ws, W.x_sc);
+  a.T = T;
+  a.H = L->hidden;
+  a.I = L->inter;
+  a.k = L->top_k;
+  a.KS = W.KS;
+  a.E = L->n_experts;
+  a.key = shape_key(T, L->n_experts, L->top_k, L->hidden, L->inter);
+  a.vq2 = slot_layout(MOE_VQ_FMT_VQ2, L->hidden, L->inter);
+  a.mx4 = slot_layout(MOE_VQ_FMT_MXFP4, L->hidden, L->inter);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_vq_expert_bytes(int format, int hidden, int inter) {
+  if (format != MOE_VQ_FMT_VQ2 && format != MOE_VQ_FMT_MXFP4) return 0;
+  if (hidden < 128 || hidden > MAX_DIM || hidden % 128 || inter < 128 || inter > MAX_DIM || inter % 128)
+    return 0;
+  return (size_t)slot_layout(format, hidden, inter).total;
+}
+
+int moe_vq_slot_layout(int format, int hidden, int inter, uint64_t offsets[7]) {
+  if (!offsets || moe_vq_expert_bytes(format, hidden, inter) == 0) return MOE_VQ_EINVAL;
+  const SlotLayout L = slot_layout(format, hidden, inter);
+  offsets[0] = L.q_gate; offsets[1] = L.q_up; offsets[2] = L.q_down;
+  offsets[3] = L.s_gate; offsets[4] = L.s_up; offsets[5] = L.s_down;
+  offsets[6] = L.total;
+  return MOE_VQ_OK;
+}
+
+size_t moe_vq_workspace_bytes(const moe_vq_layer* L, int n_tokens) {
+  if (!L || !dims_ok(L->hidden, L->inter, L->n_experts, L->top_k)) return 0;
+  if (n_tokens < 0 || n_tokens > MAX_T) return 0;
+  return ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens).total;
+}
+
+int moe_vq_route_topk(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens,
+                      int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_layer(L);
+  if (st) return st;
+  if (n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
+  if (x_dtype != MOE_VQ_F32 && x_dtype != MOE_VQ_BF16) return MOE_VQ_EINVAL;
+  if (n_tokens == 0) return MOE_VQ_OK;
+  if (!x || !topk_ids || !topk_w || ((uintptr_t)x & 15)) return MOE_VQ_EINVAL;
+  if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
+  const int E = L->n_experts, H = L->hidden, I = L->inter, k = L->top_k, T = n_tokens;
+  const WsLayout W = ws_layout(E, H, I, k, T);
+  RouteArgs ra{};
+  ra.router_w = static_cast<const uint16_t*>(L->router_w);
+  ra.x = x;
+  ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.KS = W.KS;
+  ra.logits = at<float>(ws, W.logits);
+  ra.x_h = at<uint16_t>(ws, W.x_h);
+  ra.x_sc = at<float>(ws, W.x_sc);
+  ra.topk_ids = topk_ids;
+  ra.topk_w = topk_w;
+  ra.pair_w = at<float>(ws, W.pair_w);
+  WorklistArgs wa{};
+  wa.topk_ids = topk_ids;
+  wa.slots = L->slots;
+  wa.pool_bytes = L->pool_bytes;
+  wa.T = T; wa.E = E; wa.k = k; wa.H = H; wa.I = I;
+  wa.MT1 = W.MT1;
+  wa.MT2 = W.MT2;
+  wa.rec1 = at<GroupRec>(ws, W.rec1);
+  wa.rec2 = at<GroupRec>(ws, W.rec2);
+  wa.G1 = W.G1;
+  wa.G2 = W.G2;
+  wa.hdr = at<uint32_t>(ws, W.hdr);
+  wa.act_expert = at<int32_t>(ws, W.act_expert);
+  wa.act_start = at<int32_t>(ws, W.act_start);
+  wa.act_off = at<uint64_t>(ws, W.act_off);
+  wa.act_fmt = at<uint32_t>(ws, W.act_fmt);
+  wa.grp1 = at<int32_t>(ws, W.grp1);
+  wa.grp2 = at<int32_t>(ws, W.grp2);
+  wa.pair_list = at<int32_t>(ws, W.pair_list);
+  wa.key = shape_key(T, E, k, H, I);
+  return hip_status(launch_route(ra, x_dtype, wa, static_cast<hipStream_t>(stream)));
+}
+
+int moe_vq_fc1_silu(const moe_vq_layer* L, int n_tokens, void* ws, size_t ws_bytes, float* h, void* stream) {
+  int st = check_layer(L);
+  if (st) return st;
+  if (n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
+  if (n_tokens == 0) return MOE_VQ_OK;
+  if (!h || ((uintptr_t)h & 15)) return MOE_VQ_EINVAL;
+  if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
+  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens);
+  FcArgs a = make_fc_args(L, n_tokens, ws, W, true);
+  a.out = h;
+  a.max_groups = W.G1;
+  return hip_status(launch_fc1(a, W.MT1, W.G1, device_cu_count(), static_cast<hipStream_t>(stream)));
+}
+
+int moe_vq_fc2_combine(const moe_vq_layer* L, const float* h, int n_tokens, void* ws, size_t ws_bytes,
+                       float* y, void* stream) {
+  int st = check_layer(L);
+  if (st) return st;
+  if (n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
+  if (n_tokens == 0) return MOE_VQ_OK;
+  if (!h || !y || ((uintptr_t)h & 15) || ((uintptr_t)y & 15)) return MOE_VQ_EINVAL;
+  if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
+  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens);
+  FcArgs a = make_fc_args(L, n_tokens, ws, W, false);
+  a.h_in = h;
+  a.out = at<float>(ws, W.o_buf);
+  a.y = y;
+  a.max_groups = W.G2;
+  return hip_status(launch_fc2(a, W.MT2, W.G2, device_cu_count(), static_cast<hipStream_t>(stream)));
+}
+
+int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens, void* ws,
+                        size_t ws_bytes, float* y, void* stream) {
+  int st = check_layer(L);
+  if (st) return st;
+  if (n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
+  if (x_dtype != MOE_VQ_F32 && x_dtype != MOE_VQ_BF16) return MOE_VQ_EINVAL;
+  if (n_tokens == 0) return MOE_VQ_OK;
+  if (!x || !y) return MOE_VQ_EINVAL;
+  if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
+  (void)stream;
+  return MOE_VQ_EUNSUPPORTED;
+}
+
+int moe_vq_decode_expert(const moe_vq_layer* L, int expert, int matrix, int out_dtype, void* out,
+                         int32_t* status_dev, void* stream) {
+  int st = check_layer(L);
+  if (st) return st;
+  if (expert < 0 || expert >= L->n_experts) return MOE_VQ_EINVAL;
+  if (matrix < MOE_VQ_MAT_GATE || matrix > MOE_VQ_MAT_DOWN) return MOE_VQ_EINVAL;
+  if (out_dtype != MOE_VQ_F32 && out_dtype != MOE_VQ_BF16) return MOE_VQ_EINVAL;
+  if (!out || ((uintptr_t)out & 15)) return MOE_VQ_EINVAL;
+  return hip_status(launch_decode_expert(L->pool, L->slots, L->pool_bytes,
+                                         static_cast<const uint16_t*>(L->codebook), L->hidden, L->inter,
+                                         expert, matrix, out_dtype, out, status_dev,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int moe_vq_check(const void* ws, void* stream, int32_t* info) {
+  if (!ws) return MOE_VQ_EINVAL;
+  uint32_t hdr[2] = {0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = hip_status(hipStreamSynchronize(s));
+  if (st) return st;
+  if ((st = hip_status(hipMemcpy(hdr, ws, sizeof(hdr), hipMemcpyDeviceToHost)))) return st;
+  if (info) *info = (int32_t)hdr[1];
+  return (int)hdr[0];
+}
+
+int moe_vq_step_info(const moe_vq_layer* L, int n_tokens, const void* ws, int32_t summary[4],
+                     int32_t* experts, void* stream) {
+  if (!L || !dims_ok(L->hidden, L->inter, L->n_experts, L->top_k)) return MOE_VQ_EINVAL;
+  if (!ws || !summary || n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
+  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens);
+  uint32_t hdr[HDR_WORDS];
+  int st = hip_status(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  if (st) return st;
+  if ((st = hip_status(hipMemcpy(hdr, static_cast<const char*>(ws) + W.hdr, sizeof(hdr), hipMemcpyDeviceToHost))))
+    return st;
+  summary[0] = (int32_t)hdr[HDR_STATUS];
+  summary[1] = (int32_t)hdr[HDR_INFO];
+  summary[2] = (int32_t)hdr[HDR_N_ACTIVE];
+  summary[3] = (int32_t)hdr[HDR_N_PAIRS];
+  if (experts && hdr[HDR_N_ACTIVE] > 0) {
+    const size_t n = hdr[HDR_N_ACTIVE] <= (uint32_t)L->n_experts ? hdr[HDR_N_ACTIVE] : (size_t)L->n_experts;
+    if ((st = hip_status(hipMemcpy(experts, static_cast<const char*>(ws) + W.act_expert, n * 4,
+                                   hipMemcpyDeviceToHost))))
+      return st;
+  }
+  return MOE_VQ_OK;
+}
+
+const char* moe_vq_last_hip_error(void) {
+  return g_last_hip_error == hipSuccess ? "" : hipGetErrorString(g_last_hip_error);
+}
+
+const char* moe_vq_strerror(int status) {
+  switch (status) {
+    case MOE_VQ_OK: return "ok";
+    case MOE_VQ_EINVAL: return "invalid argument";
+    case MOE_VQ_EUNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_VQ_ENOSPACE: return "workspace too small";
+    case MOE_VQ_EHIP: return "HIP runtime error";
+    case MOE_VQ_ENOTRESIDENT: return "selected expert not resident in the slot pool";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

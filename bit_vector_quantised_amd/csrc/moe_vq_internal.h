@@ -1,0 +1,212 @@
+// Internal definitions shared by the MoE-VQ HIP kernels and the C-ABI host code.
+// Target: AMD Instinct MI355X (gfx950, CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_vq.h"
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef short bf16x2_t __attribute__((ext_vector_type(2)));
+
+namespace mvq {
+
+// Activations are staged for the decode products as fp16 with one power-of-two
+// factor per token and per SLICE consecutive columns (exact for bf16 inputs).
+constexpr int SLICE = 1024;
+constexpr int MAX_E = 1024;
+constexpr int MAX_K = 32;
+constexpr int MAX_T = 65536;
+constexpr int MAX_DIM = 16384;
+
+// Signed codebook table in LDS: 256 entries (word b -> sgn(b) * CB[b & 0x7F]) of four
+// fp16 values, replicated TAB_COPIES times so that lane l reads copy (l & 31) and
+// every lane of a half-wave hits its own pair of banks:
+//     byte address(b, lane) = b * 256 + (lane & 31) * 8
+// The address is one v_perm_b32: the word's byte goes to bits 8..15, the lane
+// offset (< 256) stays in bits 0..7.
+constexpr int TAB_COPIES = 32;
+constexpr int TAB_BYTES = 256 * TAB_COPIES * 8;  // 64 KiB
+
+// Workspace header words.
+enum HdrField {
+  HDR_STATUS = 0,     // first device error (moe_vq_status), 0 = OK
+  HDR_INFO = 1,       // offending expert id or -1
+  HDR_N_ACTIVE = 2,   // number of distinct selected experts
+  HDR_N_PAIRS = 3,    // routed (token, expert) pairs placed in the worklist
+  HDR_N_TOKENS = 4,
+  HDR_GROUPS1 = 5,    // FC1 token groups (sum over active experts of ceil(m / MT1))
+  HDR_GROUPS2 = 6,    // FC2 token groups
+  HDR_MT1 = 7,
+  HDR_MT2 = 8,
+  HDR_KEY = 9,        // shape key of the step that built the worklist
+  HDR_WORDS = 64
+};
+
+// Shape key written by the worklist and checked by the FC kernels, so that a workspace
+// that was never routed (or was routed for other shapes) is rejected instead of read.
+__host__ __device__ inline uint32_t shape_key(int T, int E, int k, int H, int I) {
+  uint32_t h = 2166136261u;
+  const int v[5] = {T, E, k, H, I};
+  for (int i = 0; i < 5; ++i) { h ^= (uint32_t)v[i]; h *= 16777619u; }
+  return h | 1u;
+}
+
+__host__ __device__ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Byte offsets of the six blocks of one expert slot (relative to the slot start).
+struct SlotLayout {
+  uint64_t q_gate, q_up, q_down, s_gate, s_up, s_down, total;
+};
+
+__host__ __device__ inline SlotLayout slot_layout(int fmt, int H, int I) {
+  SlotLayout L{};
+  uint64_t qg, qd, sg, sd;
+  if (fmt == MOE_VQ_FMT_VQ2) {
+    qg = (uint64_t)I * (H / 4); qd = (uint64_t)H * (I / 4);
+    sg = (uint64_t)I * (H / 128) * 2; sd = (uint64_t)H * (I / 128) * 2;
+  } else {  // MXFP4
+    qg = (uint64_t)I * (H / 2); qd = (uint64_t)H * (I / 2);
+    sg = (uint64_t)I * (H / 32); sd = (uint64_t)H * (I / 32);
+  }
+  uint64_t off = 0;
+  L.q_gate = off; off = align256(off + qg);
+  L.q_up = off;   off = align256(off + qg);
+  L.q_down = off; off = align256(off + qd);
+  L.s_gate = off; off = align256(off + sg);
+  L.s_up = off;   off = align256(off + sg);
+  L.s_down = off; off = align256(off + sd);
+  L.total = off;
+  return L;
+}
+
+__host__ __device__ inline int n_slices(int n) { return (n + SLICE - 1) / SLICE; }
+
+// One token group of one expert, as the FC kernels consume it: a tile is (group, block
+// of rows), so a tile reads one record to know where its codes and tokens are.
+struct GroupRec {
+  uint64_t slot_off;  // byte offset of the expert's slot in the pool
+  int32_t p0;         // first entry of the group in pair_list
+  int32_t mcount;     // tokens in the group (1..MT)
+  uint32_t fmt;       // slot format (MOE_VQ_FMT_ABSENT when not resident)
+  int32_t expert;
+  int32_t pad[2];
+};
+
+// FC decode-path geometry shared by host and kernels.
+constexpr int FC_THREADS = 256;
+constexpr int LDS_LIMIT = 160 * 1024;
+
+__host__ __device__ inline size_t fc_lds_bytes(int MT, int K) {
+  return (size_t)TAB_BYTES + (size_t)MT * K * 2 + (size_t)MT * n_slices(K) * 4 + 256;
+}
+
+// Tokens of one expert that share one pass over its codes.
+__host__ __device__ inline int fc_group_tokens(int n_tokens, int K) {
+  int mt = n_tokens <= 1 ? 1 : 4;
+  while (mt > 1 && fc_lds_bytes(mt, K) > (size_t)LDS_LIMIT) mt >>= 1;
+  return mt;
+}
+
+// Upper bound on the token groups the worklist can produce.
+__host__ __device__ inline int fc_max_groups(int T, int k, int E, int MT) {
+  const long P = (long)T * k;
+  const long act = P < E ? P : E;
+  return (int)((P + act * (MT - 1)) / MT);
+}
+
+// Workspace layout for (E, H, I, k, T).
+struct WsLayout {
+  size_t hdr, logits, x_h, x_sc, act_expert, act_start, act_off, act_fmt, grp1, grp2, rec1, rec2,
+      pair_list, pair_w, o_buf, total;
+  int KS;  // number of activation slices of H
+  int MT1, MT2, G1, G2;
+};
+
+inline WsLayout ws_layout(int E, int H, int I, int k, int T) {
+  WsLayout L{};
+  size_t P = (size_t)T * k;
+  L.KS = n_slices(H);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  L.hdr = take(HDR_WORDS * 4);
+  L.logits = take((size_t)((L.KS + 3) & ~3) * T * E * 4);  // [T][E][KS rounded to 4]
+  L.x_h = take((size_t)T * H * 2);
+  L.x_sc = take((size_t)T * L.KS * 4);
+  L.act_expert = take((size_t)E * 4);
+  L.act_start = take((size_t)(E + 1) * 4);
+  L.act_off = take((size_t)E * 8);
+  L.act_fmt = take((size_t)E * 4);
+  L.grp1 = take((size_t)(E + 1) * 4);
+  L.grp2 = take((size_t)(E + 1) * 4);
+  L.MT1 = fc_group_tokens(T, H);
+  L.MT2 = fc_group_tokens(T, I);
+  L.G1 = fc_max_groups(T, k, E, L.MT1);
+  L.G2 = fc_max_groups(T, k, E, L.MT2);
+  L.rec1 = take((size_t)L.G1 * sizeof(GroupRec));
+  L.rec2 = take((size_t)L.G2 * sizeof(GroupRec));
+  L.pair_list = take(P * 4);
+  L.pair_w = take(P * 4);
+  L.o_buf = take(P * H * 4);
+  L.total = off;
+  return L;
+}
+
+// Kernel argument bundles -------------------------------------------------------------
+
+struct RouteArgs {
+  const uint16_t* router_w;  // bf16 [E][H]
+  const void* x;             // [T][H] f32 or bf16
+  int T, H, E, k, KS;
+  float* logits;             // [T][E][KSP] partial sums, KSP = KS rounded up to 4
+  uint16_t* x_h;             // [T][H] fp16 bits
+  float* x_sc;               // [T][KS]
+  int32_t* topk_ids;         // [T][k]
+  float* topk_w;             // [T][k]
+  float* pair_w;             // [T][k]
+};
+
+struct WorklistArgs {
+  const int32_t* topk_ids;
+  const moe_vq_slot* slots;
+  uint64_t pool_bytes;
+  int T, E, k, H, I, MT1, MT2;
+  uint32_t* hdr;
+  int32_t* act_expert;
+  int32_t* act_start;
+  uint64_t* act_off;
+  uint32_t* act_fmt;
+  int32_t* grp1;
+  int32_t* grp2;
+  GroupRec* rec1;
+  GroupRec* rec2;
+  int G1, G2;
+  int32_t* pair_list;
+  uint32_t key;
+};
+
+struct FcArgs {
+  const uint8_t* pool;
+  const uint16_t* codebook;  // fp16 [128][4]
+  const uint32_t* hdr;
+  const int32_t* act_start;
+  const uint64_t* act_off;
+  const uint32_t* act_fmt;
+  const int32_t* grp;        // group prefix for this kernel's MT
+  const GroupRec* rec;       // group records for this kernel's MT
+  const int32_t* pair_list;
+  const float* pair_w;
+  const uint16_t* x_h;       // FC1: staged activations [T][H] fp16
+  const float* x_sc;         // FC1: [T][KS]
+  const float* h_in;         // FC2: [P][I] fp32
+  float* out;                // FC1: h [P][I]; FC2: o_buf [P][H]
+  float* y;                  // FC2: [T][H]
+  int T, H, I, k, KS, E;
+  uint32_t key;
+  int max_groups;            // upper bound on token groups for this T
+  SlotLayout vq2, mx4;
+};
+
+}  // namespace mvq

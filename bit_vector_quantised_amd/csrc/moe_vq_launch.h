@@ -1,0 +1,19 @@
+// Host-side launch entry points of the kernel translation units.
+#pragma once
+
+#include "moe_vq_internal.h"
+
+namespace mvq {
+
+hipError_t launch_route(const RouteArgs& ra, int x_dtype, const WorklistArgs& wa, hipStream_t st);
+
+// FC1 / FC2 (+ combine) of the decode path; MT = token-group size, max_groups = the
+// worst-case number of token groups for this n_tokens, n_cu = compute units.
+hipError_t launch_fc1(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st);
+hipError_t launch_fc2(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st);
+
+hipError_t launch_decode_expert(const uint8_t* pool, const moe_vq_slot* slots, uint64_t pool_bytes,
+                                const uint16_t* codebook, int H, int I, int expert, int matrix,
+                                int out_dtype, void* out, int32_t* status_dev, hipStream_t st);
+
+}  // namespace mvq

@@ -1,0 +1,368 @@
+// Routing kernels: router product, softmax / top-k / renormalise, expert worklist.
+//
+// Sources: the routed experts of a DeepSeek-style MoE layer are chosen per token
+// from the router logits (Tandem-vLLM 0.2.0 announcement, "How it works"; vLLM-Moet
+// README, "What we changed against official vLLM", row "MoE at decode": router ->
+// FC1 -> FC2).  Routing reading: softmax over all experts, the k largest logits
+// (equal logits -> lower expert id), weights renormalised over the chosen k.
+#include "moe_vq_device.h"
+#include "moe_vq_launch.h"
+
+namespace mvq {
+
+constexpr int RT_EXPERTS = 8;   // experts per router workgroup (two per wave)
+constexpr int RT_TOKENS = 32;   // tokens per router workgroup
+
+// Partial router logits over one SLICE of H for RT_EXPERTS experts and up to
+// RT_TOKENS tokens; lane l covers 16 consecutive columns.  Partials are stored
+// [T][E][KSP] (slice fastest) so the top-k stage sums them with two 16-byte loads.
+// Workgroups of expert group 0 also stage x as fp16 with a power-of-two factor per
+// (token, slice): x = x_h * x_sc exactly for bf16 inputs (|x_h| < 2^15).
+template <bool XF32>
+__global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s = blockIdx.y;
+  const int c0 = s * SLICE + lane * 16;
+  const bool col_ok = c0 < a.H;  // H % 128 == 0, so a lane's 16 columns are all in or all out
+  const int e0 = blockIdx.x * RT_EXPERTS + wave * 2;
+  const int t0 = blockIdx.z * RT_TOKENS;
+  const int t1 = min(a.T, t0 + RT_TOKENS);
+  const int KSP = (a.KS + 3) & ~3;
+
+  uint4 w[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + j;
+    if (col_ok && e < a.E) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.router_w + (size_t)e * a.H + c0);
+      w[j][0] = p[0];
+      w[j][1] = p[1];
+    } else {
+      w[j][0] = w[j][1] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  const bool stage = (blockIdx.x == 0);
+
+  for (int t = t0; t < t1; ++t) {
+    float d[2] = {0.f, 0.f};
+    float xf[16];
+    if (col_ok) {
+      if (XF32) {
+        const float4* px = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)t * a.H + c0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float4 v = px[q];
+          xf[4 * q + 0] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t* wj = reinterpret_cast<const uint32_t*>(&w[j][0]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            d[j] = fmaf(bf16_bits_to_f32(wj[q] & 0xFFFFu), xf[2 * q], d[j]);
+            d[j] = fmaf(bf16_bits_to_f32(wj[q] >> 16), xf[2 * q + 1], d[j]);
+          }
+        }
+      } else {
+        const uint4* px = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * a.H + c0);
+        uint4 xv[2] = {px[0], px[1]};
+        const uint32_t* xw = reinterpret_cast<const uint32_t*>(xv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          xf[2 * q] = bf16_bits_to_f32(xw[q] & 0xFFFFu);
+          xf[2 * q + 1] = bf16_bits_to_f32(xw[q] >> 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t* wj = reinterpret_cast<const uint32_t*>(&w[j][0]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            d[j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wj[q]),
+                                                   __builtin_bit_cast(bf16x2_t, xw[q]), d[j], false);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) xf[q] = 0.f;
+    }
+    const float s0 = wave_sum(d[0]);
+    const float s1 = wave_sum(d[1]);
+    if (lane == 0) {
+      float* dst = a.logits + (size_t)t * a.E * KSP;
+      if (e0 < a.E) dst[(size_t)e0 * KSP + s] = s0;
+      if (e0 + 1 < a.E) dst[(size_t)(e0 + 1) * KSP + s] = s1;
+      if (s == a.KS - 1) {  // zero the padding slices once
+        for (int z = a.KS; z < KSP; ++z) {
+          if (e0 < a.E) dst[(size_t)e0 * KSP + z] = 0.f;
+          if (e0 + 1 < a.E) dst[(size_t)(e0 + 1) * KSP + z] = 0.f;
+        }
+      }
+    }
+    if (stage && wave == (t & 3)) {
+      float m = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(xf[q]));
+      m = wave_max(m);
+      int ex = 0;
+      if (m > 0.f && m == m) {
+        int e2;
+        frexpf(m, &e2);  // m < 2^e2
+        ex = e2 - 15;    // |x| * 2^-ex < 2^15
+      }
+      if (col_ok) {
+        uint32_t packed[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const _Float16 lo = (_Float16)ldexpf(xf[2 * q], -ex);
+          const _Float16 hi = (_Float16)ldexpf(xf[2 * q + 1], -ex);
+          packed[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(a.x_h + (size_t)t * a.H + c0);
+        dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      }
+      if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = ldexpf(1.0f, ex);
+    }
+  }
+}
+
+// Top-k of one token by one wave: sum the slice partials (in slice order), then k
+// rounds of argmax (greater logit, or equal logit and lower id).  Weights are
+// exp(l_i - l_max) / sum_j exp(l_j - l_max) over the chosen k, which equals the
+// softmax over all experts renormalised over the chosen k.  Lane i < k returns the
+// i-th chosen id (in *id) and writes ids / weights to the outputs.
+template <int NPL>
+__device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, int* id_out) {
+  const int KSP = (a.KS + 3) & ~3;
+  float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    float acc = -INFINITY;
+    if (e < a.E) {
+      const float4* src = reinterpret_cast<const float4*>(a.logits + ((size_t)t * a.E + e) * KSP);
+      acc = 0.f;
+      for (int q = 0; q < KSP / 4; ++q) {
+        const float4 f = src[q];
+        acc += f.x; acc += f.y; acc += f.z; acc += f.w;
+      }
+      if (acc != acc) acc = -INFINITY;  // NaN never wins
+    }
+    v[i] = acc;
+  }
+  uint32_t taken = 0;
+  float my_l = -INFINITY, lmax = 0.f;
+  int my_id = 0;
+  for (int j = 0; j < a.k; ++j) {
+    float best = -INFINITY;
+    int bid = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < a.E && !(taken & (1u << i)) && (v[i] > best || (v[i] == best && e < bid))) {
+        best = v[i];
+        bid = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(bid, o);
+      if (ob > best || (ob == best && oi < bid)) { best = ob; bid = oi; }
+    }
+    if (lane == (bid & 63)) taken |= 1u << (bid >> 6);
+    if (j == 0) lmax = best;
+    if (lane == j) { my_l = best; my_id = bid; }
+  }
+  const float p = (lane < a.k) ? expf(my_l - lmax) : 0.f;
+  const float tot = wave_sum(p);
+  if (lane < a.k) {
+    const float w = p / tot;
+    a.topk_ids[(size_t)t * a.k + lane] = my_id;
+    a.topk_w[(size_t)t * a.k + lane] = w;
+    a.pair_w[(size_t)t * a.k + lane] = w;
+    *id_out = my_id;
+  }
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  int id;
+  topk_token<NPL>(a, t, lane, &id);
+}
+
+// Exclusive block scan of four ints per thread over 1024 threads.
+__device__ int4 block_scan_excl4(int4 v, int4* wave_tot, int4* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int4 inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int nx = __shfl_up(inc.x, o), ny = __shfl_up(inc.y, o), nz = __shfl_up(inc.z, o), nw = __shfl_up(inc.w, o);
+    if (lane >= o) { inc.x += nx; inc.y += ny; inc.z += nz; inc.w += nw; }
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int4 run = make_int4(0, 0, 0, 0);
+    for (int w = 0; w < 16; ++w) {
+      const int4 c = wave_tot[w];
+      wave_tot[w] = run;
+      run.x += c.x; run.y += c.y; run.z += c.z; run.w += c.w;
+    }
+    *total = run;
+  }
+  __syncthreads();
+  const int4 b = wave_tot[wave];
+  const int4 r = make_int4(b.x + inc.x - v.x, b.y + inc.y - v.y, b.z + inc.z - v.z, b.w + inc.w - v.w);
+  __syncthreads();
+  return r;
+}
+
+constexpr int FUSED_TOPK_MAX_T = 64;
+
+// Single workgroup: (optionally the top-k of every token, one wave per token), then
+// group the routed pairs by expert (stable: ascending pair index p = t*k + i within an
+// expert), list the distinct experts in ascending id with their slot lookups, write
+// the FC token-group records, and validate every selected slot.
+template <bool FUSED, int NPL>
+__global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistArgs a) {
+  __shared__ int cnt[16 * MAX_E];
+  __shared__ int ids_lds[FUSED ? FUSED_TOPK_MAX_T * MAX_K : 1];
+  __shared__ int4 wave_tot[16];
+  __shared__ int4 s_total;
+  __shared__ int s_bad_expert;
+  __shared__ int s_bad_id;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int E = a.E, T = a.T, k = a.k;
+  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
+  if (tid == 0) { s_bad_expert = 0x7FFFFFFF; s_bad_id = 0; }
+  if (FUSED) {
+    for (int t = wave; t < T; t += 16) {
+      int id = 0;
+      topk_token<NPL>(ra, t, lane, &id);
+      if (lane < k) ids_lds[t * k + lane] = id;
+    }
+  }
+  __syncthreads();
+  auto id_of = [&](int p) -> int { return FUSED ? ids_lds[p] : a.topk_ids[p]; };
+  const int C = (T + 15) / 16;
+  const int tb = min(T, wave * C), te = min(T, tb + C);
+  for (int p = tb * k + lane; p < te * k; p += 64) {
+    const int e = id_of(p);
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave * E + e], 1);
+    else s_bad_id = 1;
+  }
+  __syncthreads();
+  int tot = 0;
+  if (tid < E)
+    for (int w = 0; w < 16; ++w) tot += cnt[w * E + tid];
+  const int g1 = (tot + a.MT1 - 1) / a.MT1;
+  const int g2 = (tot + a.MT2 - 1) / a.MT2;
+  const int4 sc = block_scan_excl4(make_int4(tot, tot > 0 ? 1 : 0, g1, g2), wave_tot, &s_total);
+  const int start = sc.x, rank = sc.y, gs1 = sc.z, gs2 = sc.w;
+  if (tid < E && tot > 0) {
+    const moe_vq_slot sl = a.slots[tid];
+    uint32_t fmt = sl.format;
+    const uint64_t off = sl.byte_offset;
+    uint64_t need = 0;
+    if (fmt == MOE_VQ_FMT_VQ2 || fmt == MOE_VQ_FMT_MXFP4) need = slot_layout((int)fmt, a.H, a.I).total;
+    const bool ok = need != 0 && (off & 255) == 0 && off <= a.pool_bytes && need <= a.pool_bytes - off;
+    if (!ok) {
+      fmt = MOE_VQ_FMT_ABSENT;
+      atomicMin(&s_bad_expert, tid);
+    }
+    a.act_expert[rank] = tid;
+    a.act_start[rank] = start;
+    a.act_off[rank] = off;
+    a.act_fmt[rank] = fmt;
+    a.grp1[rank] = gs1;
+    a.grp2[rank] = gs2;
+    for (int gi = 0; gi < g1 && gs1 + gi < a.G1; ++gi) {
+      GroupRec r;
+      r.slot_off = off; r.p0 = start + gi * a.MT1; r.mcount = min(a.MT1, tot - gi * a.MT1);
+      r.fmt = fmt; r.expert = tid; r.pad[0] = r.pad[1] = 0;
+      a.rec1[gs1 + gi] = r;
+    }
+    for (int gi = 0; gi < g2 && gs2 + gi < a.G2; ++gi) {
+      GroupRec r;
+      r.slot_off = off; r.p0 = start + gi * a.MT2; r.mcount = min(a.MT2, tot - gi * a.MT2);
+      r.fmt = fmt; r.expert = tid; r.pad[0] = r.pad[1] = 0;
+      a.rec2[gs2 + gi] = r;
+    }
+  }
+  if (tid == 0) {
+    const int n_active = s_total.y;
+    a.act_start[n_active] = s_total.x;
+    a.grp1[n_active] = s_total.z;
+    a.grp2[n_active] = s_total.w;
+  }
+  // per-wave bases: cnt[w][e] <- start[e] + sum_{w' < w} cnt[w'][e]
+  if (tid < E) {
+    int run = start;
+    for (int w = 0; w < 16; ++w) {
+      const int c = cnt[w * E + tid];
+      cnt[w * E + tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // stable placement: each wave walks its tokens in order; the k experts of one token
+  // are distinct, so the k lanes never collide on a counter.
+  for (int t = tb; t < te; ++t) {
+    if (lane < k) {
+      const int p = t * k + lane;
+      const int e = id_of(p);
+      if ((unsigned)e < (unsigned)E) {
+        const int pos = atomicAdd(&cnt[wave * E + e], 1);
+        a.pair_list[pos] = p;
+      }
+    }
+  }
+  if (tid == 0) {
+    uint32_t status = MOE_VQ_OK;
+    int info = -1;
+    if (s_bad_expert != 0x7FFFFFFF) { status = MOE_VQ_ENOTRESIDENT; info = s_bad_expert; }
+    if (s_bad_id) { status = MOE_VQ_EINVAL; }
+    a.hdr[HDR_STATUS] = status;
+    a.hdr[HDR_INFO] = (uint32_t)info;
+    a.hdr[HDR_N_ACTIVE] = s_total.y;
+    a.hdr[HDR_N_PAIRS] = s_total.x;
+    a.hdr[HDR_N_TOKENS] = T;
+    a.hdr[HDR_GROUPS1] = s_total.z;
+    a.hdr[HDR_GROUPS2] = s_total.w;
+    a.hdr[HDR_MT1] = a.MT1;
+    a.hdr[HDR_MT2] = a.MT2;
+    a.hdr[HDR_KEY] = a.key;
+  }
+}
+
+template <int NPL>
+static void launch_topk_worklist(const RouteArgs& ra, const WorklistArgs& wa, hipStream_t st) {
+  if (ra.T <= FUSED_TOPK_MAX_T) {
+    worklist_kernel<true, NPL><<<1, 1024, 0, st>>>(ra, wa);
+  } else {
+    topk_kernel<NPL><<<(ra.T + 3) / 4, 256, 0, st>>>(ra);
+    worklist_kernel<false, NPL><<<1, 1024, 0, st>>>(ra, wa);
+  }
+}
+
+hipError_t launch_route(const RouteArgs& ra, int x_dtype, const WorklistArgs& wa, hipStream_t st) {
+  (void)hipGetLastError();  // start from a clean error state: report only our own launches
+  dim3 g1((ra.E + RT_EXPERTS - 1) / RT_EXPERTS, ra.KS, (ra.T + RT_TOKENS - 1) / RT_TOKENS);
+  if (x_dtype == MOE_VQ_F32)
+    router_gemv_kernel<true><<<g1, 256, 0, st>>>(ra);
+  else
+    router_gemv_kernel<false><<<g1, 256, 0, st>>>(ra);
+  const int npl = (ra.E + 63) / 64;
+  if (npl <= 1) launch_topk_worklist<1>(ra, wa, st);
+  else if (npl <= 2) launch_topk_worklist<2>(ra, wa, st);
+  else if (npl <= 4) launch_topk_worklist<4>(ra, wa, st);
+  else if (npl <= 8) launch_topk_worklist<8>(ra, wa, st);
+  else launch_topk_worklist<16>(ra, wa, st);
+  return hipGetLastError();
+}
+
+}  // namespace mvq

@@ -1,0 +1,146 @@
+"""Device-resident MoE-VQ layer and step buffers on top of the C ABI.
+
+PyTorch provides device memory and the stream; every step of the computation runs
+in the HIP library.  This module only places bytes (the slot pool, the slot table)
+and passes pointers.
+"""
+from __future__ import annotations
+
+from typing import Callable, Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+
+PAYLOAD_KEYS = {
+    _lib.FMT_VQ2: ("codes_g", "codes_u", "codes_d", "scales_g", "scales_u", "scales_d"),
+    _lib.FMT_MXFP4: ("nib_g", "nib_u", "nib_d", "e8m0_g", "e8m0_u", "e8m0_d"),
+}
+
+
+def pack_slot(expert: Dict[str, np.ndarray], hidden: int, inter: int) -> np.ndarray:
+    """The bytes of one expert slot (layout of include/moe_vq.h, offsets from the library)."""
+    fmt = int(expert["format"])
+    offs = _lib.slot_layout(fmt, hidden, inter)
+    buf = np.zeros(offs[6], dtype=np.uint8)
+    for key, off in zip(PAYLOAD_KEYS[fmt], offs[:6]):
+        raw = np.ascontiguousarray(expert[key]).view(np.uint8).reshape(-1)
+        buf[off:off + raw.size] = raw
+    return buf
+
+
+class DeviceLayer:
+    """Slot pool + slot table + router weights + codebook in device memory.
+
+    experts(e) returns expert e's storage arrays (see synth); formats[e] gives its
+    format, MOE_VQ_FMT_ABSENT leaving the slot empty (not resident).
+    """
+
+    def __init__(self, hidden: int, inter: int, n_experts: int, top_k: int, codebook: np.ndarray,
+                 router_w_bits: np.ndarray, experts: Callable[[int], Dict[str, np.ndarray]],
+                 formats: Sequence[int], device: str = "cuda"):
+        self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
+        self.device = torch.device(device)
+        offsets = np.zeros(n_experts, dtype=np.uint64)
+        total = 0
+        for e in range(n_experts):
+            f = int(formats[e])
+            if f == _lib.FMT_ABSENT:
+                continue
+            offsets[e] = total
+            total += _lib.expert_bytes(f, hidden, inter)
+        self.pool_bytes = max(total, 256)
+        self.pool = torch.empty(self.pool_bytes, dtype=torch.uint8, device=self.device)
+        for e in range(n_experts):
+            f = int(formats[e])
+            if f == _lib.FMT_ABSENT:
+                continue
+            buf = pack_slot(experts(e), hidden, inter)
+            o = int(offsets[e])
+            self.pool[o:o + buf.size].copy_(torch.from_numpy(buf))
+        slots = np.zeros(n_experts, dtype=[("byte_offset", "<u8"), ("format", "<u4"), ("reserved", "<u4")])
+        slots["byte_offset"] = offsets
+        slots["format"] = np.asarray(formats, dtype=np.uint32)
+        self.slot_offsets = offsets
+        self.formats = np.asarray(formats, dtype=np.int32)
+        self.slots = torch.from_numpy(slots.view(np.uint8).copy()).to(self.device)
+        self.router_w = torch.from_numpy(np.ascontiguousarray(router_w_bits).view(np.int16)).to(self.device)
+        self.codebook = torch.from_numpy(np.ascontiguousarray(codebook).view(np.int16)).to(self.device)
+        self.c = _lib.Layer(hidden, inter, n_experts, top_k, self.router_w.data_ptr(), self.codebook.data_ptr(),
+                            self.pool.data_ptr(), self.pool_bytes, self.slots.data_ptr())
+
+    @classmethod
+    def from_synth(cls, syn, device: str = "cuda", formats: Optional[Sequence[int]] = None):
+        cfg = syn.cfg
+        fm = syn.formats if formats is None else formats
+        return cls(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, syn.codebook, syn.router_w,
+                   syn.expert, fm, device)
+
+    def set_slots(self, offsets: np.ndarray, formats: Sequence[int]) -> None:
+        """Rewrite the slot table (e.g. to mark experts absent)."""
+        slots = np.zeros(self.n_experts, dtype=[("byte_offset", "<u8"), ("format", "<u4"), ("reserved", "<u4")])
+        slots["byte_offset"] = offsets
+        slots["format"] = np.asarray(formats, dtype=np.uint32)
+        self.slots.copy_(torch.from_numpy(slots.view(np.uint8).copy()))
+
+
+def x_dtype_code(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return _lib.BF16
+    if x.dtype == torch.float32:
+        return _lib.F32
+    raise TypeError(f"activations must be bf16 or fp32, got {x.dtype}")
+
+
+class Step:
+    """Buffers for one routed-expert step of up to max_tokens tokens, and the calls."""
+
+    def __init__(self, layer: DeviceLayer, max_tokens: int):
+        self.layer = layer
+        self.max_tokens = max_tokens
+        dev = layer.device
+        k, H, I = layer.top_k, layer.hidden, layer.inter
+        self.ws_bytes = _lib.workspace_bytes(layer.c, max_tokens)
+        if self.ws_bytes == 0:
+            raise ValueError("invalid layer shape")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.ids = torch.empty((max_tokens, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((max_tokens, k), dtype=torch.float32, device=dev)
+        self.h = torch.empty((max_tokens * k, I), dtype=torch.float32, device=dev)
+        self.y = torch.empty((max_tokens, H), dtype=torch.float32, device=dev)
+
+    def stream(self) -> int:
+        return torch.cuda.current_stream(self.layer.device).cuda_stream
+
+    def route(self, x: torch.Tensor) -> None:
+        T = x.shape[0]
+        assert x.is_contiguous() and x.shape[1] == self.layer.hidden and T <= self.max_tokens
+        _lib.route_topk(self.layer.c, x.data_ptr(), x_dtype_code(x), T, self.ids.data_ptr(), self.w.data_ptr(),
+                        self.ws.data_ptr(), self.ws_bytes, self.stream())
+
+    def fc1(self, T: int) -> None:
+        _lib.fc1_silu(self.layer.c, T, self.ws.data_ptr(), self.ws_bytes, self.h.data_ptr(), self.stream())
+
+    def fc2(self, T: int) -> None:
+        _lib.fc2_combine(self.layer.c, self.h.data_ptr(), T, self.ws.data_ptr(), self.ws_bytes,
+                         self.y.data_ptr(), self.stream())
+
+    def prefill(self, x: torch.Tensor) -> None:
+        T = x.shape[0]
+        _lib.prefill_gemm(self.layer.c, x.data_ptr(), x_dtype_code(x), T, self.ws.data_ptr(), self.ws_bytes,
+                          self.y.data_ptr(), self.stream())
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        """route -> FC1 -> FC2; returns a view of y [T, H] (valid until the next call)."""
+        T = x.shape[0]
+        self.route(x)
+        self.fc1(T)
+        self.fc2(T)
+        return self.y[:T]
+
+    def check(self):
+        return _lib.check(self.ws.data_ptr(), self.stream())
+
+    def info(self, T: int):
+        return _lib.step_info(self.layer.c, T, self.ws.data_ptr(), self.stream())

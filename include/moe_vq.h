@@ -1,0 +1,166 @@
+/*
+ * moe_vq.h -- C ABI of the MoE-VQ routed-expert step on AMD Instinct MI355X (gfx950).
+ *
+ * One call sequence computes, for n_tokens activations x [T, H]:
+ *   route      l = W_r x; p = softmax(l); S = top-k(l); w = p_S / sum p_S
+ *   FC1        g = W_g,e x, u = W_u,e x, h = silu(g) * u      (per selected expert e)
+ *   FC2        o = W_d,e h
+ *   combine    y[t] = sum_i w[t,i] o[t,i]
+ * with every expert matrix stored as 2-bit sign-symmetric vector codes (VQ2) or as
+ * MXFP4, decoded on the fly.  Sources: the Tandem-vLLM 0.2.0 announcement ("How it
+ * works": routed experts kept as 2-bit vector codes, about 2.1 bits per weight, a
+ * GPU cache of the most-used experts, nothing skipped or substituted; "Quality vs
+ * the official FP4 checkpoint": the 52 most-routed experts per layer kept in FP4)
+ * and the vLLM-Moet README ("2-bit experts on vLLM v0.24.0": the codebook is
+ * sign-symmetric; "What we changed against official vLLM", row "MoE at decode":
+ * router -> FC1 -> FC2 without padding the experts; "Qwen3.8-Flash-Next-FP8": the
+ * routed-expert GEMV with silu*up fused).
+ *
+ * VQ2 format.  A weight matrix [rows][in] is stored as u8 words [rows][in/4] and
+ * fp16 scales [rows][in/128].  Word b encodes four consecutive weights of one row:
+ *     W[n, 4j+d] = S[n, (4j+d)/128] * (b & 0x80 ? -1 : +1) * CB[b & 0x7F][d]
+ * with CB the per-layer fp16 codebook [128][4] (2 + 16/128 = 2.125 bits/weight).
+ * MXFP4 format.  u8 [rows][in/2] holding E2M1 elements (low nibble = even index)
+ * and u8 E8M0 exponents [rows][in/32]:  W[n,k] = E2M1(q) * 2^(e-127).
+ *
+ * Slot pool.  All experts live in one device buffer (the pool).  slots[e] gives
+ * expert e's byte offset in the pool and its format.  A slot holds six row-major
+ * blocks, each starting on a 256-byte boundary relative to the slot start:
+ *     VQ2:   codes_gate [I][H/4] | codes_up [I][H/4] | codes_down [H][I/4] |
+ *            scales_gate [I][H/128] | scales_up [I][H/128] | scales_down [H][I/128]
+ *     MXFP4: q_gate [I][H/2] | q_up [I][H/2] | q_down [H][I/2] |
+ *            e8m0_gate [I][H/32] | e8m0_up [I][H/32] | e8m0_down [H][I/32]
+ * moe_vq_expert_bytes() returns the slot size.  byte_offset must be a multiple of 256.
+ *
+ * Conventions.
+ *  - Pointers are device memory unless marked [host].  The caller owns every buffer
+ *    (pool, slots, router weights, codebook, x, h, y, workspace); the library
+ *    allocates and frees nothing and keeps no mutable global state.
+ *  - stream is a hipStream_t (NULL = the default stream).  Every compute call only
+ *    enqueues work on it and returns; nothing synchronises except moe_vq_check().
+ *  - Argument errors are returned synchronously, before any HIP call is made.
+ *  - Errors found on the device (an absent expert, a slot outside the pool) are
+ *    recorded in the workspace's status word; the affected contribution is left
+ *    out of y and moe_vq_check() reports it.  Nothing is ever silently skipped.
+ *  - Calls on one workspace must be stream-ordered: a workspace holds one step.
+ *  - Results are deterministic: repeated calls on the same inputs give the same bits.
+ */
+#ifndef MOE_VQ_H
+#define MOE_VQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_vq_status {
+  MOE_VQ_OK = 0,
+  MOE_VQ_EINVAL = 1,        /* bad argument (null pointer, bad size, bad enum)            */
+  MOE_VQ_EUNSUPPORTED = 2,  /* shape or dtype this build does not implement               */
+  MOE_VQ_ENOSPACE = 3,      /* workspace smaller than moe_vq_workspace_bytes()            */
+  MOE_VQ_EHIP = 4,          /* a HIP runtime call or kernel launch failed                 */
+  MOE_VQ_ENOTRESIDENT = 5   /* (device) a selected expert's slot is absent or out of pool */
+};
+
+enum moe_vq_dtype { MOE_VQ_F32 = 0, MOE_VQ_BF16 = 1 };
+
+enum moe_vq_format { MOE_VQ_FMT_ABSENT = 0, MOE_VQ_FMT_VQ2 = 1, MOE_VQ_FMT_MXFP4 = 2 };
+
+enum moe_vq_matrix { MOE_VQ_MAT_GATE = 0, MOE_VQ_MAT_UP = 1, MOE_VQ_MAT_DOWN = 2 };
+
+/* Expert slot table entry, device array [n_experts]. */
+typedef struct moe_vq_slot {
+  uint64_t byte_offset;  /* offset of the slot in the pool, multiple of 256 */
+  uint32_t format;       /* enum moe_vq_format                              */
+  uint32_t reserved;     /* must be 0                                       */
+} moe_vq_slot;
+
+/* [host] Layer descriptor; its pointers are device buffers. */
+typedef struct moe_vq_layer {
+  int32_t hidden;              /* H, multiple of 128, 128..16384            */
+  int32_t inter;               /* I, multiple of 128, 128..16384            */
+  int32_t n_experts;           /* E, 1..1024                                */
+  int32_t top_k;               /* k, 1..min(E, 32)                          */
+  const void *router_w;        /* bf16 [E][H], row-major                    */
+  const void *codebook;        /* fp16 [128][4], one per layer              */
+  const uint8_t *pool;         /* slot pool                                 */
+  uint64_t pool_bytes;         /* size of the pool in bytes                 */
+  const moe_vq_slot *slots;    /* [E] expert id -> slot                     */
+} moe_vq_layer;
+
+/* [host] Bytes of one expert slot of the given format, 0 if an argument is invalid. */
+size_t moe_vq_expert_bytes(int format, int hidden, int inter);
+
+/* [host] Byte offsets, relative to the slot start, of the six blocks of a slot of the
+ * given format: offsets[0..2] = gate, up, down payload (VQ2 words or MXFP4 nibbles),
+ * offsets[3..5] = gate, up, down scales (fp16 or E8M0), offsets[6] = slot size.
+ * Returns MOE_VQ_EINVAL (offsets untouched) for an invalid format or shape. */
+int moe_vq_slot_layout(int format, int hidden, int inter, uint64_t offsets[7]);
+
+/* [host] Workspace bytes needed for n_tokens tokens with this layer, 0 if the layer
+ * descriptor's sizes are invalid (pointers are not inspected).  The workspace holds
+ * the routing worklist, staged activations, per-pair FC2 outputs and the status word. */
+size_t moe_vq_workspace_bytes(const moe_vq_layer *layer, int n_tokens);
+
+/* Route n_tokens tokens: router product (bf16 weights, fp32 accumulation), softmax
+ * over all experts, top-k (descending logit, equal logits -> lower expert id),
+ * renormalised weights, and the per-expert worklist with slot lookups, all on the
+ * device.  x: [n_tokens][H] in x_dtype.  Outputs topk_ids [n_tokens][k] (int32)
+ * and topk_w [n_tokens][k] (fp32).  Also stages x for FC1 in the workspace and
+ * resets the status word.  n_tokens == 0 is a no-op.  n_tokens <= 65536. */
+int moe_vq_route_topk(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
+                      int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* FC1 of every routed (token, expert) pair with SiLU*up fused: for pair p = t*k + i
+ * (expert topk_ids[t][i]), h[p][:] = silu(W_g x_t) * (W_u x_t), fp32 [n_tokens*k][I].
+ * Uses the activations and worklist staged by moe_vq_route_topk in ws. */
+int moe_vq_fc1_silu(const moe_vq_layer *layer, int n_tokens, void *ws, size_t ws_bytes,
+                    float *h, void *stream);
+
+/* FC2 and the weighted combine: y[t][:] = sum_i topk_w[t][i] * (W_d h[t*k+i]),
+ * fp32 [n_tokens][H], overwritten.  h as written by moe_vq_fc1_silu. */
+int moe_vq_fc2_combine(const moe_vq_layer *layer, const float *h, int n_tokens,
+                       void *ws, size_t ws_bytes, float *y, void *stream);
+
+/* Prefill form of FC1 + FC2 + combine for large n_tokens: tokens grouped per expert,
+ * decoded weight tiles feed bf16 matrix-core (MFMA) products with fp32 accumulation;
+ * SiLU*up fused into the FC1 epilogue, the routing weight into the FC2 epilogue.
+ * Requires moe_vq_route_topk on the same x first.  y [n_tokens][H] fp32, overwritten. */
+int moe_vq_prefill_gemm(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
+                        void *ws, size_t ws_bytes, float *y, void *stream);
+
+/* Test hook: decode one matrix (enum moe_vq_matrix) of one expert into out, [rows][in]
+ * row-major.  out_dtype MOE_VQ_F32 gives the exact decoded values, MOE_VQ_BF16 their
+ * round-to-nearest-even.  It uses the same LDS decode tables as the FC kernels.  The
+ * slot is read on the device: if it is absent or lies outside the pool, out is left
+ * untouched and *status_dev (a device int32, may be NULL) is set to
+ * MOE_VQ_ENOTRESIDENT, otherwise to MOE_VQ_OK. */
+int moe_vq_decode_expert(const moe_vq_layer *layer, int expert, int matrix, int out_dtype,
+                         void *out, int32_t *status_dev, void *stream);
+
+/* Synchronise stream, then return the device-side status of the last step run on ws
+ * (MOE_VQ_OK or MOE_VQ_ENOTRESIDENT).  If info is not NULL, *info receives the
+ * first offending expert id (or -1). */
+int moe_vq_check(const void *ws, void *stream, int32_t *info);
+
+/* Synchronise stream and copy the routing summary of the last step on ws to the host:
+ * summary[0] = device status, summary[1] = offending expert or -1, summary[2] = number
+ * of distinct selected experts (n_active), summary[3] = routed pairs placed.  If
+ * experts is not NULL it receives the n_active distinct expert ids in ascending order
+ * (room for n_experts entries).  layer and n_tokens must match the route call. */
+int moe_vq_step_info(const moe_vq_layer *layer, int n_tokens, const void *ws, int32_t summary[4],
+                     int32_t *experts, void *stream);
+
+/* [host] Text of the last HIP runtime error seen by a call of this library on the
+ * calling thread (the reason behind MOE_VQ_EHIP), or "" if none. */
+const char *moe_vq_last_hip_error(void);
+
+/* [host] Static description of a status code. */
+const char *moe_vq_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_VQ_H */

@@ -1,0 +1,151 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every declared
+symbol, computes sizes and layouts, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_vq.h")
+
+mvq = pytest.importorskip("bit_vector_quantised_amd")
+from bit_vector_quantised_amd import _lib  # noqa: E402
+from bit_vector_quantised_amd.layer import pack_slot  # noqa: E402
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_vq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "moe_vq_route_topk" in names and "moe_vq_fc1_silu" in names and len(names) >= 10
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_expert_bytes():
+    assert _lib.expert_bytes(_lib.FMT_VQ2, 7168, 2048) == 11_698_176
+    assert _lib.expert_bytes(_lib.FMT_MXFP4, 7168, 2048) == 23_396_352
+    assert _lib.expert_bytes(_lib.FMT_VQ2, 256, 128) == 26_112
+    assert _lib.expert_bytes(_lib.FMT_ABSENT, 256, 128) == 0
+    assert _lib.expert_bytes(_lib.FMT_VQ2, 100, 128) == 0
+    assert _lib.expert_bytes(_lib.FMT_VQ2, 256, 0) == 0
+    assert _lib.expert_bytes(7, 256, 128) == 0
+
+
+@pytest.mark.parametrize("fmt", [_lib.FMT_VQ2, _lib.FMT_MXFP4])
+@pytest.mark.parametrize("dims", [(256, 128), (7168, 2048), (384, 640)])
+def test_slot_layout_matches_oracle_reading(fmt, dims):
+    H, I = dims
+    offs = _lib.slot_layout(fmt, H, I)
+    blocks, total = oracle.slot_blocks(fmt, H, I)
+    assert offs[6] == total == _lib.expert_bytes(fmt, H, I)
+    assert offs[:6] == [b[3] for b in blocks]
+    assert all(o % 256 == 0 for o in offs)
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_VQ2, synth.FMT_MXFP4])
+def test_packed_slot_reads_back(fmt):
+    cfg = synth.PRESETS["tiny"]
+    ex = synth.draw_expert(cfg, 2, fmt)
+    buf = pack_slot(ex, cfg.hidden, cfg.inter)
+    pool = np.zeros(512 + buf.size, dtype=np.uint8)
+    pool[512:] = buf
+    back = oracle.read_slot(pool, 512, fmt, cfg.hidden, cfg.inter)
+    for key, val in ex.items():
+        if key == "format":
+            continue
+        assert np.array_equal(back[key].view(np.uint8), np.asarray(val).view(np.uint8)), key
+
+
+def fake_layer(H=256, I=128, E=8, k=2, pool=1 << 20):
+    # pointer values are never dereferenced by the paths exercised here
+    return _lib.Layer(H, I, E, k, 0x10000, 0x20000, 0x100000, pool, 0x30000)
+
+
+def test_workspace_bytes():
+    L = fake_layer()
+    a = _lib.workspace_bytes(L, 4)
+    b = _lib.workspace_bytes(L, 64)
+    assert 0 < a < b and a % 256 == 0
+    assert _lib.workspace_bytes(fake_layer(H=100), 4) == 0
+    assert _lib.workspace_bytes(fake_layer(k=9), 4) == 0
+    assert _lib.workspace_bytes(L, -1) == 0
+    assert _lib.workspace_bytes(L, 65537) == 0
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_route_rejects_bad_arguments_before_any_hip_call():
+    raw = _lib.raw()
+    L = fake_layer()
+    ws_ok = _lib.workspace_bytes(L, 4)
+    P = ctypes.byref
+    X, IDS, W, WS = 0x40000, 0x50000, 0x60000, 0x700000
+    route = raw.moe_vq_route_topk
+    assert route(None, X, _lib.F32, 4, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+    assert route(P(fake_layer(H=100)), X, _lib.F32, 4, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+    assert route(P(fake_layer(I=129)), X, _lib.F32, 4, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+    assert route(P(fake_layer(k=9)), X, _lib.F32, 4, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+    assert route(P(fake_layer(E=0)), X, _lib.F32, 4, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+    assert route(P(L), X, 7, 4, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+    assert route(P(L), X, _lib.F32, -1, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+    assert route(P(L), X, _lib.F32, 4, IDS, W, None, ws_ok, None) == _lib.EINVAL
+    assert route(P(L), X, _lib.F32, 4, IDS, W, WS + 8, ws_ok, None) == _lib.EINVAL
+    assert route(P(L), X, _lib.F32, 4, IDS, W, WS, ws_ok - 1, None) == _lib.ENOSPACE
+    assert route(P(L), None, _lib.F32, 4, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+    assert route(P(L), X, _lib.F32, 4, None, W, WS, ws_ok, None) == _lib.EINVAL
+    # no tokens: a no-op that touches nothing
+    assert route(P(L), X, _lib.F32, 0, IDS, W, WS, ws_ok, None) == _lib.OK
+    bad_pool = _lib.Layer(256, 128, 8, 2, 0x10000, 0x20000, 0x100010, 1 << 20, 0x30000)
+    assert route(P(bad_pool), X, _lib.F32, 4, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+
+
+def test_fc_and_prefill_and_decode_reject_bad_arguments():
+    raw = _lib.raw()
+    L = fake_layer()
+    P = ctypes.byref
+    ws_ok = _lib.workspace_bytes(L, 4)
+    WS, H_, Y = 0x700000, 0x800000, 0x900000
+    assert raw.moe_vq_fc1_silu(P(L), 4, WS, ws_ok - 256, H_, None) == _lib.ENOSPACE
+    assert raw.moe_vq_fc1_silu(P(L), 4, WS, ws_ok, None, None) == _lib.EINVAL
+    assert raw.moe_vq_fc1_silu(P(L), 0, WS, ws_ok, H_, None) == _lib.OK
+    assert raw.moe_vq_fc2_combine(P(L), H_, 4, WS, ws_ok, None, None) == _lib.EINVAL
+    assert raw.moe_vq_fc2_combine(P(L), None, 4, WS, ws_ok, Y, None) == _lib.EINVAL
+    assert raw.moe_vq_fc2_combine(P(L), H_, 4, None, ws_ok, Y, None) == _lib.EINVAL
+    assert raw.moe_vq_prefill_gemm(P(L), 0x40000, 3, 4, WS, ws_ok, Y, None) == _lib.EINVAL
+    assert raw.moe_vq_prefill_gemm(P(L), 0x40000, _lib.BF16, 4, WS, 0, Y, None) == _lib.ENOSPACE
+    assert raw.moe_vq_decode_expert(P(L), 8, 0, _lib.F32, Y, None, None) == _lib.EINVAL
+    assert raw.moe_vq_decode_expert(P(L), -1, 0, _lib.F32, Y, None, None) == _lib.EINVAL
+    assert raw.moe_vq_decode_expert(P(L), 0, 3, _lib.F32, Y, None, None) == _lib.EINVAL
+    assert raw.moe_vq_decode_expert(P(L), 0, 0, 5, Y, None, None) == _lib.EINVAL
+    assert raw.moe_vq_decode_expert(P(L), 0, 0, _lib.F32, None, None, None) == _lib.EINVAL
+    assert raw.moe_vq_check(None, None, None) == _lib.EINVAL
+    assert raw.moe_vq_step_info(None, 4, WS, None, None, None) == _lib.EINVAL
+
+
+def test_strerror():
+    assert _lib.strerror(_lib.OK) == "ok"
+    assert "resident" in _lib.strerror(_lib.ENOTRESIDENT)
+    assert "workspace" in _lib.strerror(_lib.ENOSPACE)
+    assert _lib.strerror(99) == "unknown status"
+
+
+def test_single_hip_runtime_in_process():
+    """The library binds the HIP runtime that PyTorch loaded (one libamdhip64 mapped),
+    so torch's streams and allocations are valid for it."""
+    maps = open("/proc/self/maps").read().splitlines()
+    libs = sorted({ln.split()[-1] for ln in maps if "libamdhip64" in ln})
+    assert len(libs) == 1, libs
