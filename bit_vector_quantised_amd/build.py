@@ -4,10 +4,19 @@
 
 Every kernel is compiled with hipcc for gfx950 only.  Packed-fp32 VALU forms are
 disabled (-packed-fp32-ops): scalar and float2 code stays on plain fp32 ops.
+Only the moe_vq_* C entry points are exported (hidden visibility elsewhere, and
+-Bsymbolic), so another copy of the library loaded into the same process cannot
+take over its internal functions.
+
+The build fails when a kernel uses scratch (private) memory: on this stack every
+launch of such a kernel pays a set-up cost of about 17 us, more than the decode-batch
+kernels themselves take.  The compiler's per-kernel resource report is written to
+_build/kernel_resources.txt.
 """
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -32,7 +41,25 @@ def hipcc() -> str:
 def flags():
     return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-I", INCLUDE, "-I", CSRC,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-result"]
+            "-fvisibility=hidden", "-Wno-unused-result", "-Rpass-analysis=kernel-resource-usage"]
+
+
+def kernel_resources(text: str):
+    """(kernel, {field: value}) from hipcc's kernel-resource-usage remarks."""
+    out, cur = [], None
+    for line in text.splitlines():
+        m = re.search(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                      r"LDS Size \[bytes/block\]|Dynamic Stack): (\S+)", line)
+        if not m:
+            continue
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = (val, {})
+            out.append(cur)
+        elif cur is not None:
+            cur[1][key.split()[0] if key != "Dynamic Stack" else "DynamicStack"] = (
+                val == "True" if key == "Dynamic Stack" else int(val))
+    return out
 
 
 def build(verbose: bool = False) -> str:
@@ -44,18 +71,28 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(objdir, src + ".o")
         cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
-        out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                        if "is not a recognized feature for this target" not in l)
+        text = r.stdout + r.stderr
+        out = "\n".join(l for l in text.splitlines()
+                        if "is not a recognized feature for this target" not in l and "remark:" not in l
+                        and "-Rpass-analysis" not in l)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{out}")
         if verbose and out.strip():
             print(out)
-        return obj
+        return obj, kernel_resources(text)
 
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+        results = list(ex.map(compile_one, SOURCES))
+    objs = [o for o, _ in results]
+    res = [k for _, ks in results for k in ks]
+    with open(os.path.join(objdir, "kernel_resources.txt"), "w") as f:
+        for name, v in res:
+            f.write(f"{name} " + " ".join(f"{k}={x}" for k, x in v.items()) + "\n")
+    spilling = [name for name, v in res if v.get("ScratchSize", 0) > 0 or v.get("DynamicStack")]
+    if spilling:
+        raise RuntimeError("kernels use scratch memory: " + ", ".join(spilling))
     tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-Bsymbolic", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")

@@ -20,11 +20,11 @@
 // tokens of the group, so each code byte is read from HBM once per token group.
 //
 // Two kernels:
-//  * fc_tile_kernel (K a multiple of 1024, K <= 8192): one workgroup per tile.  The
-//    workgroup first issues the codebook load, its staging loads and ALL code/scale
-//    loads of its rows, then builds the LDS table while the code stream is in flight
-//    and consumes the loads in issue order (vmcnt is in order), so every wave keeps
-//    ~14 x 16 B per lane in flight from its first cycle.
+//  * fc_stream_kernel (K = 1024, 2048 or 7168): a persistent grid; each
+//    workgroup walks a contiguous run of tiles with two register buffers, issuing the
+//    next tile's 14 x 16-byte loads per lane before decoding the current tile, so the
+//    code stream stays in flight while the LDS lookups run.  The decode table and the
+//    staged activations are built once and restaged only when the token group changes.
 //  * fc_generic_kernel (any K multiple of 128): a persistent grid that prefetches one
 //    chunk ahead; used for the shapes the tile kernel does not cover.
 #include "moe_vq_device.h"
@@ -61,22 +61,31 @@ __device__ __forceinline__ bool ws_ok(const FcArgs& a, bool fc1, int MT) {
          a.hdr[fc1 ? HDR_MT1 : HDR_MT2] == (uint32_t)MT;
 }
 
+// Four VQ2 words (one dword of codes) against their 16 fp16 activations (8 dwords),
+// added to p in order.  A 16-byte chunk is four such steps.
+__device__ __forceinline__ float vq2_dword_dot(const uint2* tab, uint32_t wd, uint32_t laneoff,
+                                               const uint32_t* xw, float p) {
+  uint2 e0 = tab_lookup(tab, tab_addr<0>(wd, laneoff));
+  uint2 e1 = tab_lookup(tab, tab_addr<1>(wd, laneoff));
+  uint2 e2 = tab_lookup(tab, tab_addr<2>(wd, laneoff));
+  uint2 e3 = tab_lookup(tab, tab_addr<3>(wd, laneoff));
+  p = dot2(e0.x, xw[0], p); p = dot2(e0.y, xw[1], p);
+  p = dot2(e1.x, xw[2], p); p = dot2(e1.y, xw[3], p);
+  p = dot2(e2.x, xw[4], p); p = dot2(e2.y, xw[5], p);
+  p = dot2(e3.x, xw[6], p); p = dot2(e3.y, xw[7], p);
+  return p;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& q, int i) {
+  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
+}
+
 // 16 VQ2 words of one 16-byte chunk against 64 fp16 activations (32 dwords).
 __device__ __forceinline__ float vq2_chunk_dot(const uint2* tab, const uint4& q, uint32_t laneoff,
                                                const uint32_t* xw) {
   float p = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t wd = i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
-    uint2 e0 = tab_lookup(tab, tab_addr<0>(wd, laneoff));
-    uint2 e1 = tab_lookup(tab, tab_addr<1>(wd, laneoff));
-    uint2 e2 = tab_lookup(tab, tab_addr<2>(wd, laneoff));
-    uint2 e3 = tab_lookup(tab, tab_addr<3>(wd, laneoff));
-    p = dot2(e0.x, xw[8 * i + 0], p); p = dot2(e0.y, xw[8 * i + 1], p);
-    p = dot2(e1.x, xw[8 * i + 2], p); p = dot2(e1.y, xw[8 * i + 3], p);
-    p = dot2(e2.x, xw[8 * i + 4], p); p = dot2(e2.y, xw[8 * i + 5], p);
-    p = dot2(e3.x, xw[8 * i + 6], p); p = dot2(e3.y, xw[8 * i + 7], p);
-  }
+  for (int i = 0; i < 4; ++i) p = vq2_dword_dot(tab, dword_of(q, i), laneoff, xw + 8 * i, p);
   return p;
 }
 
@@ -95,28 +104,109 @@ __device__ __forceinline__ float mx4_chunk_dot(const uint4& q, const uint32_t* x
 }
 
 // -------------------------------------------------------------------------------------
-// fc_tile_kernel: K = 1024 * CPL, LPR = 16, one workgroup per (group, row block)
+// fc_stream_kernel: K = 1024 * CPL, LPR = 16, persistent and software-pipelined
 // -------------------------------------------------------------------------------------
 
-template <int CPL, bool FC1>
+template <int CPL, int MT, bool FC1>
 struct TileGeom {
   static constexpr int NM = FC1 ? 2 : 1;
   static constexpr int RPL_RAW = FC1 ? LB_VQ / (2 * CPL) : LB_VQ / CPL;
-  static constexpr int RPL = RPL_RAW < 1 ? 1 : RPL_RAW;           // rows per lane
+  // a token group of MT > 1 holds NM * RPL * MT accumulators: fewer rows per lane
+  static constexpr int RPL_CAP = MT > 1 ? 4 : (CPL == 1 ? 8 / NM : 16);
+  static constexpr int RPL = RPL_RAW < 1 ? 1 : (RPL_RAW > RPL_CAP ? RPL_CAP : RPL_RAW);  // rows per lane
   static constexpr int ROWS = 16 * RPL;                              // rows per tile
   static constexpr int MXC = 2 * CPL;                                // MXFP4 chunks per lane per row
   static constexpr int RPP_MX_RAW = LB_MX / (NM * MXC);
   static constexpr int RPP_MX = RPP_MX_RAW < 1 ? 1 : (RPP_MX_RAW > RPL ? RPL : RPP_MX_RAW);
 };
 
+// The fields of a GroupRec a tile needs, held in scalar registers (uniform per workgroup).
+struct RecS {
+  uint64_t slot_off;
+  int32_t mcount;
+  uint32_t fmt;
+  int32_t pair[MAX_MT];
+};
+
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// v through an empty asm statement: the compiler cannot treat what is derived from it
+// as loop-invariant.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+static_assert(offsetof(GroupRec, mcount) == 12 && offsetof(GroupRec, fmt) == 16 &&
+              offsetof(GroupRec, pair) == 24, "GroupRec layout");
+
+__device__ __forceinline__ RecS load_rec(const GroupRec* recs, int g) {
+  const int4* p = reinterpret_cast<const int4*>(recs + g);
+  const int4 w0 = p[0], w1 = p[1];
+  RecS r;
+  r.slot_off = ((uint64_t)(uint32_t)uni(w0.y) << 32) | (uint32_t)uni(w0.x);
+  r.mcount = uni(w0.w);
+  r.fmt = (uint32_t)uni(w1.x);
+  const int* wi = reinterpret_cast<const int*>(recs + g);
+#pragma unroll
+  for (int j = 0; j < MAX_MT; ++j) r.pair[j] = uni(wi[6 + j]);
+  return r;
+}
+
+// The code words and scales one lane reads for one VQ2 tile.
 template <int CPL, int MT, bool FC1>
-__global__ __launch_bounds__(FC_THREADS, 2) void fc_tile_kernel(FcArgs a) {
-  using G = TileGeom<CPL, FC1>;
+struct VqBuf {
+  uint4 q[TileGeom<CPL, MT, FC1>::RPL][TileGeom<CPL, MT, FC1>::NM][CPL];
+  uint32_t s[TileGeom<CPL, MT, FC1>::RPL][TileGeom<CPL, MT, FC1>::NM][CPL];
+};
+
+template <int CPL, int MT, bool FC1>
+__device__ __forceinline__ void issue_vq(VqBuf<CPL, MT, FC1>& b, const FcArgs& a, const RecS& r, int rb,
+                                         int NROWS, int wave, int rg, int sub) {
+  using G = TileGeom<CPL, MT, FC1>;
+  constexpr int K = 1024 * CPL;
+  // uniform matrix bases + one 32-bit per-lane row offset; the chunk offset j*256 (and
+  // the scale offset j*16) is an immediate of the load instruction
+  const uint8_t* slot = a.pool + r.slot_off;
+  const uint8_t* qb0 = slot + (FC1 ? a.vq2.q_gate : a.vq2.q_down);
+  const uint8_t* qb1 = slot + a.vq2.q_up;
+  const uint8_t* sb0 = slot + (FC1 ? a.vq2.s_gate : a.vq2.s_down);
+  const uint8_t* sb1 = slot + a.vq2.s_up;
+#pragma unroll
+  for (int rr = 0; rr < G::RPL; ++rr) {
+    // rows past the end (ragged shapes only) re-read the last row; finish() drops them
+    const int n = min(rb * G::ROWS + rr * 16 + wave * 4 + rg, NROWS - 1);
+    const uint32_t qo = (uint32_t)n * (K / 4) + (uint32_t)sub * 16;
+    const uint32_t so = (uint32_t)n * (K / 64) + (uint32_t)(sub >> 1) * 2;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+      for (int m = 0; m < G::NM; ++m) {
+        b.q[rr][m][j] = *reinterpret_cast<const uint4*>((m == 0 ? qb0 : qb1) + qo + j * 256);
+        b.s[rr][m][j] = *reinterpret_cast<const uint16_t*>((m == 0 ? sb0 : sb1) + so + j * 16);
+      }
+  }
+}
+
+// Same tokens (FC1: the token of every pair; FC2: the pair itself, whose h is staged).
+template <int MT, bool FC1>
+__device__ __forceinline__ bool same_inputs(const RecS& x, const RecS& y, int k) {
+  if (x.mcount != y.mcount) return false;
+  bool eq = true;
+#pragma unroll
+  for (int j = 0; j < MT; ++j) eq = eq && (FC1 ? (x.pair[j] / k == y.pair[j] / k) : (x.pair[j] == y.pair[j]));
+  return eq;
+}
+
+template <int CPL, int MT, bool FC1>
+__global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
+  using G = TileGeom<CPL, MT, FC1>;
   constexpr int NM = G::NM, RPL = G::RPL, ROWS = G::ROWS;
   constexpr int K = 1024 * CPL;
   constexpr int KS = CPL;  // activation slices
+  constexpr int XT = (K / 64) * XCHUNK_UNITS;  // padded 16-byte units per token
   __shared__ uint2 tab[256 * TAB_COPIES];
-  __shared__ uint4 xs[MT * K / 8];
+  __shared__ uint4 xs[MT * XT];
   __shared__ float xsc[MT * KS];
   __shared__ float red[4][MT * KS];
 
@@ -125,226 +215,263 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_tile_kernel(FcArgs a) {
   const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
   const int NROWS = FC1 ? a.I : a.H;
   const int RB = (NROWS + ROWS - 1) / ROWS;
-  const int g = blockIdx.x / RB, rb = blockIdx.x % RB;
 
-  // (1) loads that do not depend on the worklist contents
   const uint2 cbv = reinterpret_cast<const uint2*>(a.codebook)[tid & 127];
   if (!ws_ok(a, FC1, MT)) return;
-  const int n_groups = (int)a.hdr[FC1 ? HDR_GROUPS1 : HDR_GROUPS2];
-  if (g >= n_groups) return;
-  const GroupRec rec = a.rec[g];
-  const int mcount = rec.mcount;
-  const uint32_t fmt = rec.fmt;
-  const uint8_t* slot = a.pool + rec.slot_off;
+  const int n_tiles = (int)a.hdr[FC1 ? HDR_GROUPS1 : HDR_GROUPS2] * RB;
+  // a contiguous run of tiles per workgroup: consecutive tiles share the token group
+  const int t_begin = (int)(((long)blockIdx.x * n_tiles) / gridDim.x);
+  const int t_end = (int)(((long)(blockIdx.x + 1) * n_tiles) / gridDim.x);
+  if (t_begin >= t_end) return;
 
-  // (2) staging loads: FC1 reads the fp16 activations of the group's tokens, FC2 the
-  // fp32 h of its pairs (thread tid covers columns 4*tid..4*tid+3 of every slice)
-  int pair[MT];
+  // Stage the activations of record r into LDS (FC1: fp16 x of its tokens; FC2: h of
+  // its pairs scaled to fp16 with one power-of-two factor per 1024-column slice).
+  auto stage = [&](const RecS& r) __attribute__((always_inline)) {
+    // 16-byte units of one token per thread (K / 8 units over FC_THREADS threads)
+    constexpr int XU = FC1 ? (K / 8 + FC_THREADS - 1) / FC_THREADS : 1;
+    // staging runs once per token group: its per-lane addresses are recomputed here
+    // rather than hoisted out of the tile loop and held in registers across it
+    const int tid = opaque(threadIdx.x);
+    const int wave = tid >> 6, lane = tid & 63;
+    if (FC1) {
+      // the token loop is unrolled so that every pair index is read with a constant
+      // index (a per-lane index would put the record in scratch memory)
+      uint4 xv[MT][XU];
+      float scv[MT];
 #pragma unroll
-  for (int j = 0; j < MT; ++j) pair[j] = a.pair_list[rec.p0 + (j < mcount ? j : 0)];
-  constexpr int XV = FC1 ? (MT * K / 8 + FC_THREADS - 1) / FC_THREADS : 1;
-  uint4 xv[XV];
-  float4 hv[FC1 ? 1 : MT * KS];
-  float scv = 1.f;
-  if (FC1) {
+      for (int j = 0; j < MT; ++j) {
+        const bool live = j < r.mcount;
+        const size_t tok = live ? (size_t)(r.pair[j] / a.k) : 0;
+        const uint4* src = reinterpret_cast<const uint4*>(a.x_h + tok * K);
 #pragma unroll
-    for (int i = 0; i < XV; ++i) {
-      const int idx = tid + i * FC_THREADS;
-      const int j = idx / (K / 8), o = idx % (K / 8);
-      if (idx < MT * K / 8 && j < mcount)
-        xv[i] = reinterpret_cast<const uint4*>(a.x_h + (size_t)(pair[j] / a.k) * K)[o];
-      else
-        xv[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < XU; ++i) {
+          const int o = tid + i * FC_THREADS;
+          xv[j][i] = (live && o < K / 8) ? src[o] : make_uint4(0, 0, 0, 0);
+        }
+        scv[j] = (live && tid < KS) ? a.x_sc[tok * KS + tid] : 1.f;
+      }
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+#pragma unroll
+        for (int i = 0; i < XU; ++i) {
+          const int o = tid + i * FC_THREADS;
+          if (o < K / 8) xs[j * XT + x_unit(o)] = xv[j][i];
+        }
+        if (tid < KS) xsc[j * KS + tid] = scv[j];
+      }
+    } else {
+      float4 hv[MT * KS];
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          hv[j * KS + s] = j < r.mcount ? reinterpret_cast<const float4*>(a.h_in + (size_t)r.pair[j] * K)[s * 256 + tid]
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int js = 0; js < MT * KS; ++js) {
+        const float4 v = hv[js];
+        float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        m = wave_max(m);
+        if (lane == 0) red[wave][js] = m;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int js = 0; js < MT * KS; ++js) {
+        const float m = fmaxf(fmaxf(red[0][js], red[1][js]), fmaxf(red[2][js], red[3][js]));
+        int ex = 0;
+        if (m > 0.f && m == m) ex = frexp_exponent(m) - 15;
+        const float4 v = hv[js];
+        const int j = js / KS, s = js % KS;
+        const uint2 pk = make_uint2(pack_half2(ldexp2(v.x, -ex), ldexp2(v.y, -ex)),
+                                    pack_half2(ldexp2(v.z, -ex), ldexp2(v.w, -ex)));
+        const int u = (s * SLICE + 4 * tid) / 8;  // 16-byte unit within the token
+        reinterpret_cast<uint2*>(xs)[(j * XT + x_unit(u)) * 2 + (tid & 1)] = pk;
+        if (tid == 0) xsc[js] = ldexp2(1.0f, ex);
+      }
     }
-    if (tid < MT * KS) {
-      const int j = tid / KS, s = tid % KS;
-      scv = j < mcount ? a.x_sc[(size_t)(pair[j] / a.k) * KS + s] : 1.f;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < MT; ++j)
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        hv[j * KS + s] = j < mcount ? reinterpret_cast<const float4*>(a.h_in + (size_t)pair[j] * K)[s * 256 + tid]
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  };
 
-  // (3) row coordinates and the code/scale loads of the first pass
-  int nrow[RPL];
-  bool rok[RPL];
+  // One tile's outputs from its accumulators (16 lanes of a row reduced first).
+  auto finish = [&](float (&acc)[NM][RPL][MT], const RecS& r, int rb) __attribute__((always_inline)) {
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    nrow[r] = rb * ROWS + r * 16 + wave * 4 + rg;
-    rok[r] = nrow[r] < NROWS;
-  }
-  float acc[NM][RPL][MT];
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
+      for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
-    for (int r = 0; r < RPL; ++r)
+        for (int t = 0; t < MT; ++t) acc[m][rr][t] = group_sum<16>(acc[m][rr][t]);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[m][r][t] = 0.f;
-
-  const bool is_vq = fmt == MOE_VQ_FMT_VQ2;
-  const bool is_mx = fmt == MOE_VQ_FMT_MXFP4;
-  uint4 q[RPL][NM][CPL];
-  uint32_t sq[RPL][NM][CPL];
-  if (is_vq) {
-    const uint8_t* qb0 = slot + (FC1 ? a.vq2.q_gate : a.vq2.q_down);
-    const uint8_t* qb1 = slot + a.vq2.q_up;
-    const uint16_t* sb0 = reinterpret_cast<const uint16_t*>(slot + (FC1 ? a.vq2.s_gate : a.vq2.s_down));
-    const uint16_t* sb1 = reinterpret_cast<const uint16_t*>(slot + a.vq2.s_up);
+    for (int rr = 0; rr < RPL; ++rr) {
+      const int n = rb * ROWS + rr * 16 + wave * 4 + rg;
 #pragma unroll
-    for (int r = 0; r < RPL; ++r)
-#pragma unroll
-      for (int j = 0; j < CPL; ++j)
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const int c = sub + 16 * j;
-          if (rok[r]) {
-            q[r][m][j] = ldg16((m == 0 ? qb0 : qb1) + (size_t)nrow[r] * (K / 4) + c * 16);
-            sq[r][m][j] = (m == 0 ? sb0 : sb1)[(size_t)nrow[r] * (K / 128) + (c >> 1)];
+      for (int t = 0; t < MT; ++t) {
+        if (((rr * MT + t) & 15) == sub && t < r.mcount && n < NROWS) {
+          const int p = r.pair[t];
+          if (FC1) {
+            const float gv = acc[0][rr][t], uv = acc[NM - 1][rr][t];
+            a.out[(size_t)p * a.I + n] = silu_fast(gv) * uv;
           } else {
-            q[r][m][j] = make_uint4(0, 0, 0, 0);
-            sq[r][m][j] = 0;
+            a.out[(size_t)p * a.H + n] = a.pair_w[p] * acc[0][rr][t];
           }
         }
-  }
+      }
+    }
+  };
 
-  // (4) LDS: decode table and staged activations
-  write_table_entry(tab, cbv, tid);
-  if (FC1) {
+  // VQ2 tile from a filled buffer.
+  auto compute_vq = [&](const VqBuf<CPL, MT, FC1>& b, const RecS& r, int rb) __attribute__((always_inline)) {
+    // one base register plus immediate offsets for the factor reads (constant
+    // addresses would each be held in a register across the tile loop)
+    const float* xscb = xsc + opaque(0);
+    float acc[NM][RPL][MT];
 #pragma unroll
-    for (int i = 0; i < XV; ++i) {
-      const int idx = tid + i * FC_THREADS;
-      if (idx < MT * K / 8) xs[idx] = xv[i];
-    }
-    if (tid < MT * KS) xsc[tid] = scv;
-  } else {
-    // one power-of-two factor per (pair, 1024-column slice): block-wide max first
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int js = 0; js < MT * KS; ++js) {
-      const float4 v = hv[js];
-      float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-      m = wave_max(m);
-      if (lane == 0) red[wave][js] = m;
-    }
-    __syncthreads();
+      for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
-    for (int js = 0; js < MT * KS; ++js) {
-      const float m = fmaxf(fmaxf(red[0][js], red[1][js]), fmaxf(red[2][js], red[3][js]));
-      int ex = 0;
-      if (m > 0.f && m == m) { int e2; frexpf(m, &e2); ex = e2 - 15; }
-      const float4 v = hv[js];
-      const int j = js / KS, s = js % KS;
-      uint2 pk = make_uint2(pack_half2(ldexpf(v.x, -ex), ldexpf(v.y, -ex)), pack_half2(ldexpf(v.z, -ex), ldexpf(v.w, -ex)));
-      reinterpret_cast<uint2*>(xs)[(j * K + s * SLICE) / 4 + tid] = pk;
-      if (tid == 0) xsc[js] = ldexpf(1.0f, ex);
-    }
-  }
-  __syncthreads();
-
-  // (5) compute, consuming the loads in issue order
-  if (is_vq) {
+        for (int t = 0; t < MT; ++t) acc[m][rr][t] = 0.f;
 #pragma unroll
-    for (int r = 0; r < RPL; ++r)
+    for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         const int c = sub + 16 * j;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          if (t < mcount) {
-            const uint4* xp = xs + t * (K / 8) + c * 8;
-            uint4 xr[8];
+          if (t < r.mcount) {
+            // the chunk's 64 activations are read 16 at a time, each shared by the
+            // NM matrices, which keeps 8 registers (not 32) of activations live
+            const uint4* xp = xs + t * XT + c * XCHUNK_UNITS;
+            float pr[NM];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) xr[i] = xp[i];
-            const uint32_t* xw = reinterpret_cast<const uint32_t*>(xr);
-            const float f = xsc[t * KS + j];
+            for (int m = 0; m < NM; ++m) pr[m] = 0.f;
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              const float p = vq2_chunk_dot(tab, q[r][m][j], laneoff, xw);
-              acc[m][r][t] = fmaf(f16_bits_to_f32(sq[r][m][j]) * f, p, acc[m][r][t]);
+            for (int i = 0; i < 4; ++i) {
+              const uint4 xr[2] = {xp[2 * i], xp[2 * i + 1]};
+              const uint32_t* xw = reinterpret_cast<const uint32_t*>(xr);
+#pragma unroll
+              for (int m = 0; m < NM; ++m) pr[m] = vq2_dword_dot(tab, dword_of(b.q[rr][m][j], i), laneoff, xw, pr[m]);
             }
+            const float f = xscb[t * KS + j];
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+              acc[m][rr][t] = fmaf(f16_bits_to_f32(b.s[rr][m][j]) * f, pr[m], acc[m][rr][t]);
           }
         }
       }
-  } else if (is_mx) {
-    constexpr int MXC = G::MXC, RPP = G::RPP_MX;
-    const uint8_t* qb0 = slot + (FC1 ? a.mx4.q_gate : a.mx4.q_down);
-    const uint8_t* qb1 = slot + a.mx4.q_up;
-    const uint8_t* sb0 = slot + (FC1 ? a.mx4.s_gate : a.mx4.s_down);
-    const uint8_t* sb1 = slot + a.mx4.s_up;
+    finish(acc, r, rb);
+  };
+
+  // MXFP4 tile (loads and compute, not pipelined), or an absent expert (zeros).  The
+  // tile's (row, matrix) units of MXC 16-byte loads are processed UPP at a time.
+  auto compute_mx = [&](const RecS& r, int rb) __attribute__((always_inline)) {
+    const float* xscb = xsc + opaque(0);
+    constexpr int MXC = G::MXC;
+    constexpr int NU = RPL * NM;                                   // units per tile
+    constexpr int UPP_RAW = LB_MX / MXC;
+    constexpr int UPP = UPP_RAW < 1 ? 1 : (UPP_RAW > NU ? NU : UPP_RAW);
+    float acc[NM][RPL][MT];
 #pragma unroll
-    for (int r0 = 0; r0 < RPL; r0 += RPP) {
-      uint4 qm[RPP][NM][MXC];
-      uint32_t em[RPP][NM][MXC];
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int rr = 0; rr < RPP; ++rr)
+      for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
-        for (int j = 0; j < MXC; ++j)
+        for (int t = 0; t < MT; ++t) acc[m][rr][t] = 0.f;
+    if (r.fmt == MOE_VQ_FMT_MXFP4) {
+      const uint8_t* slot = a.pool + r.slot_off;
+      const uint8_t* qb0 = slot + (FC1 ? a.mx4.q_gate : a.mx4.q_down);
+      const uint8_t* qb1 = slot + a.mx4.q_up;
+      const uint8_t* sb0 = slot + (FC1 ? a.mx4.s_gate : a.mx4.s_down);
+      const uint8_t* sb1 = slot + a.mx4.s_up;
 #pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            const int r = r0 + rr;
-            const int c = sub + 16 * j;
-            if (r < RPL && rok[r < RPL ? r : 0]) {
-              const int n = nrow[r < RPL ? r : 0];
-              qm[rr][m][j] = ldg16((m == 0 ? qb0 : qb1) + (size_t)n * (K / 2) + c * 16);
-              em[rr][m][j] = (m == 0 ? sb0 : sb1)[(size_t)n * (K / 32) + c];
+      for (int u0 = 0; u0 < NU; u0 += UPP) {
+        uint4 qm[UPP][MXC];
+        uint32_t em[UPP][MXC];
+#pragma unroll
+        for (int uu = 0; uu < UPP; ++uu) {
+          const int u = u0 + uu, rr = u / NM, m = u % NM;
+          const int n = min(rb * ROWS + rr * 16 + wave * 4 + rg, NROWS - 1);
+          const uint32_t qo = (uint32_t)n * (K / 2) + (uint32_t)sub * 16;
+          const uint32_t eo = (uint32_t)n * (K / 32) + (uint32_t)sub;
+#pragma unroll
+          for (int j = 0; j < MXC; ++j) {
+            if (u < NU) {
+              qm[uu][j] = *reinterpret_cast<const uint4*>((m == 0 ? qb0 : qb1) + qo + j * 256);
+              em[uu][j] = ((m == 0 ? sb0 : sb1) + eo)[j * 16];
             } else {
-              qm[rr][m][j] = make_uint4(0, 0, 0, 0);
-              em[rr][m][j] = 127;
+              qm[uu][j] = make_uint4(0, 0, 0, 0);
+              em[uu][j] = 127;
             }
           }
+        }
 #pragma unroll
-      for (int rr = 0; rr < RPP; ++rr) {
-        if (r0 + rr >= RPL) break;
+        for (int uu = 0; uu < UPP; ++uu) {
+          const int u = u0 + uu, rr = u / NM, m = u % NM;
+          if (u >= NU) break;
 #pragma unroll
-        for (int j = 0; j < MXC; ++j) {
-          const int c = sub + 16 * j;
+          for (int j = 0; j < MXC; ++j) {
+            const int c = sub + 16 * j;
 #pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            if (t < mcount) {
-              const uint4* xp = xs + t * (K / 8) + c * 4;
-              uint4 xr[4];
+            for (int t = 0; t < MT; ++t) {
+              if (t < r.mcount) {
+                const uint4* xp = xs + t * XT + (c >> 1) * XCHUNK_UNITS + (c & 1) * 4;
+                uint4 xr[4];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) xr[i] = xp[i];
-              const uint32_t* xw = reinterpret_cast<const uint32_t*>(xr);
-              const float f = xsc[t * KS + (c >> 5)];
-#pragma unroll
-              for (int m = 0; m < NM; ++m) {
-                const float p = mx4_chunk_dot(qm[rr][m][j], xw);
-                acc[m][r0 + rr][t] = fmaf(e8m0_to_f32(em[rr][m][j]) * f, p, acc[m][r0 + rr][t]);
+                for (int i = 0; i < 4; ++i) xr[i] = xp[i];
+                const uint32_t* xw = reinterpret_cast<const uint32_t*>(xr);
+                const float f = xscb[t * KS + (c >> 5)];
+                const float pr = mx4_chunk_dot(qm[uu][j], xw);
+                acc[m][rr][t] = fmaf(e8m0_to_f32(em[uu][j]) * f, pr, acc[m][rr][t]);
               }
             }
           }
         }
       }
     }
-  }
-  // (an absent expert leaves acc at zero: h / pair outputs are written as 0 and the
-  //  worklist has recorded MOE_VQ_ENOTRESIDENT in the status word)
+    // (an absent expert keeps acc at zero: its outputs are written as 0 and the
+    //  worklist has recorded MOE_VQ_ENOTRESIDENT in the status word)
+    finish(acc, r, rb);
+  };
 
-  // (6) reduce the 16 lanes of each row and write
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int r = 0; r < RPL; ++r)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[m][r][t] = group_sum<16>(acc[m][r][t]);
-#pragma unroll
-  for (int r = 0; r < RPL; ++r)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      if (((r * MT + t) & 15) == sub && t < mcount && rok[r]) {
-        const int p = pair[t];
-        if (FC1) {
-          const float gv = acc[0][r][t], uv = acc[NM - 1][r][t];
-          a.out[(size_t)p * a.I + nrow[r]] = gv / (1.0f + expf(-gv)) * uv;
-        } else {
-          a.out[(size_t)p * a.H + nrow[r]] = a.pair_w[p] * acc[0][r][t];
-        }
-      }
+  // ---- prologue: first tile's record, its code loads, activations and the table
+  int t = t_begin;
+  RecS rc = load_rec(a.rec, t / RB);
+  RecS rn = (t + 1 < t_end) ? load_rec(a.rec, (t + 1) / RB) : rc;
+  VqBuf<CPL, MT, FC1> A, B;
+  stage(rc);  // staging loads are issued before the code loads
+  if (rc.fmt == MOE_VQ_FMT_VQ2) issue_vq(A, a, rc, t % RB, NROWS, wave, rg, sub);
+  write_table_entry(tab, cbv, tid);
+  __syncthreads();
+
+  // ---- steady state: the next tile's loads are in flight while this tile decodes.
+  // `pending` says whether the other buffer already holds the next tile's loads.
+  auto step = [&](VqBuf<CPL, MT, FC1>& cur, VqBuf<CPL, MT, FC1>& nxt) __attribute__((always_inline)) -> bool {
+    const int tn = t + 1;
+    const bool more = tn < t_end;
+    const bool same = more && same_inputs<MT, FC1>(rn, rc, a.k);
+    // prefetch only between VQ2 tiles of the same token group (an MXFP4 tile uses the
+    // register budget of both buffers itself)
+    const bool prefetch = more && same && rn.fmt == MOE_VQ_FMT_VQ2 && rc.fmt == MOE_VQ_FMT_VQ2;
+    if (prefetch) issue_vq(nxt, a, rn, tn % RB, NROWS, wave, rg, sub);
+    const RecS rnn = (tn + 1 < t_end) ? load_rec(a.rec, (tn + 1) / RB) : rn;
+    if (rc.fmt == MOE_VQ_FMT_VQ2) compute_vq(cur, rc, t % RB);
+    else compute_mx(rc, t % RB);
+    if (!more) return false;
+    if (!same) {
+      __syncthreads();  // every wave is done with the staged activations
+      stage(rn);
+      if (rn.fmt == MOE_VQ_FMT_VQ2) issue_vq(nxt, a, rn, tn % RB, NROWS, wave, rg, sub);
+      __syncthreads();
+    } else if (!prefetch && rn.fmt == MOE_VQ_FMT_VQ2) {
+      issue_vq(nxt, a, rn, tn % RB, NROWS, wave, rg, sub);
     }
+    rc = rn;
+    rn = rnn;
+    t = tn;
+    return true;
+  };
+  for (;;) {
+    if (!step(A, B)) break;
+    if (!step(B, A)) break;
+  }
 }
 
 // -------------------------------------------------------------------------------------
@@ -376,8 +503,9 @@ __global__ __launch_bounds__(FC_THREADS) void fc_generic_kernel(FcArgs a) {
   const int K = FC1 ? a.H : a.I;
   const int NROWS = FC1 ? a.I : a.H;
   const int KS = n_slices(K);
+  const int XT = (int)fc_x_units(K);
   uint4* xs = dyn;
-  float* xsc = reinterpret_cast<float*>(dyn + (size_t)MT * (K / 8));
+  float* xsc = reinterpret_cast<float*>(dyn + (size_t)MT * XT);
 
   const uint2 cbv = reinterpret_cast<const uint2*>(a.codebook)[tid & 127];
   if (!ws_ok(a, FC1, MT)) return;
@@ -400,7 +528,7 @@ __global__ __launch_bounds__(FC_THREADS) void fc_generic_kernel(FcArgs a) {
         for (int j = 0; j < mcount; ++j) {
           const int t = a.pair_list[p0 + j] / a.k;
           const uint4* src = reinterpret_cast<const uint4*>(a.x_h + (size_t)t * K);
-          for (int i = tid; i < K / 8; i += FC_THREADS) xs[j * (K / 8) + i] = src[i];
+          for (int i = tid; i < K / 8; i += FC_THREADS) xs[j * XT + x_unit(i)] = src[i];
           for (int i = tid; i < KS; i += FC_THREADS) xsc[j * KS + i] = a.x_sc[(size_t)t * KS + i];
         }
       } else {
@@ -422,16 +550,15 @@ __global__ __launch_bounds__(FC_THREADS) void fc_generic_kernel(FcArgs a) {
           }
           m = wave_max(m);
           int ex = 0;
-          if (m > 0.f && m == m) { int e2; frexpf(m, &e2); ex = e2 - 15; }
+          if (m > 0.f && m == m) ex = frexp_exponent(m) - 15;
           if (c0 < K) {
             uint32_t pk[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) pk[q] = pack_half2(ldexpf(v[2 * q], -ex), ldexpf(v[2 * q + 1], -ex));
-            uint4* dst = xs + j * (K / 8) + c0 / 8;
-            dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-            dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+            for (int q = 0; q < 8; ++q) pk[q] = pack_half2(ldexp2(v[2 * q], -ex), ldexp2(v[2 * q + 1], -ex));
+            xs[j * XT + x_unit(c0 / 8)] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            xs[j * XT + x_unit(c0 / 8 + 1)] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
           }
-          if (lane == 0) xsc[j * KS + s] = ldexpf(1.0f, ex);
+          if (lane == 0) xsc[j * KS + s] = ldexp2(1.0f, ex);
         }
       }
       __syncthreads();
@@ -470,7 +597,7 @@ __global__ __launch_bounds__(FC_THREADS) void fc_generic_kernel(FcArgs a) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           if (t < mcount) {
-            const uint4* xp = xs + t * (K / 8) + c * 8;
+            const uint4* xp = xs + t * XT + c * XCHUNK_UNITS;
             uint4 xr[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) xr[i] = xp[i];
@@ -502,7 +629,7 @@ __global__ __launch_bounds__(FC_THREADS) void fc_generic_kernel(FcArgs a) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           if (t < mcount) {
-            const uint4* xp = xs + t * (K / 8) + c * 4;
+            const uint4* xp = xs + t * XT + (c >> 1) * XCHUNK_UNITS + (c & 1) * 4;
             uint4 xr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) xr[i] = xp[i];
@@ -532,7 +659,7 @@ __global__ __launch_bounds__(FC_THREADS) void fc_generic_kernel(FcArgs a) {
           const int p = a.pair_list[p0 + t];
           if (FC1) {
             const float gv = acc[0][r][t], uv = acc[NM - 1][r][t];
-            a.out[(size_t)p * a.I + nrow[r]] = gv / (1.0f + expf(-gv)) * uv;
+            a.out[(size_t)p * a.I + nrow[r]] = silu_fast(gv) * uv;
           } else {
             a.out[(size_t)p * a.H + nrow[r]] = a.pair_w[p] * acc[0][r][t];
           }
@@ -562,23 +689,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // -------------------------------------------------------------------------------------
 
 template <bool FC1>
-static hipError_t launch_tile(const FcArgs& a, int K, int MT, int max_groups, hipStream_t st, bool* done) {
+static hipError_t launch_stream(const FcArgs& a, int K, int MT, int max_groups, int n_cu, hipStream_t st,
+                                bool* done) {
   *done = false;
   if (K % 1024 != 0) return hipSuccess;
   const int cpl = K / 1024;
   const int nrows = FC1 ? a.I : a.H;
-#define MVQ_TILE_CASE(C, M)                                                                  \
+  const size_t lds = fc_lds_bytes(MT, K);
+  int per_cu = (int)(LDS_LIMIT / lds);
+  per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+  // FC2 at K = 7168 with one token per group needs more registers than a wave of
+  // this kernel has (it would spill to scratch memory, whose set-up costs more per
+  // launch than the kernel's own run): the generic kernel takes that shape.
+#define MVQ_STREAM_CASE(C, M)                                                                \
+  if constexpr (FC1 || C != 7 || M != 1)                                                     \
   if (cpl == C && MT == M) {                                                                 \
-    constexpr int ROWS = TileGeom<C, FC1>::ROWS;                                             \
-    const long grid = (long)max_groups * ((nrows + ROWS - 1) / ROWS);                       \
+    constexpr int ROWS = TileGeom<C, M, FC1>::ROWS;                                           \
+    const long tiles = (long)max_groups * ((nrows + ROWS - 1) / ROWS);                      \
+    long grid = (long)n_cu * per_cu;                                                         \
+    if (tiles < grid) grid = tiles;                                                          \
     *done = true;                                                                            \
     if (grid <= 0) return hipSuccess;                                                        \
-    fc_tile_kernel<C, M, FC1><<<(unsigned)grid, FC_THREADS, 0, st>>>(a);                     \
+    fc_stream_kernel<C, M, FC1><<<(unsigned)grid, FC_THREADS, 0, st>>>(a);                   \
     return hipGetLastError();                                                                \
   }
-  MVQ_TILE_CASE(1, 1) MVQ_TILE_CASE(2, 1) MVQ_TILE_CASE(4, 1) MVQ_TILE_CASE(7, 1) MVQ_TILE_CASE(8, 1)
-  MVQ_TILE_CASE(1, 4) MVQ_TILE_CASE(2, 4) MVQ_TILE_CASE(4, 4) MVQ_TILE_CASE(7, 4)
-#undef MVQ_TILE_CASE
+  MVQ_STREAM_CASE(1, 1) MVQ_STREAM_CASE(2, 1) MVQ_STREAM_CASE(7, 1)
+  MVQ_STREAM_CASE(1, 4) MVQ_STREAM_CASE(2, 4) MVQ_STREAM_CASE(7, 4)
+#undef MVQ_STREAM_CASE
   return hipSuccess;
 }
 
@@ -594,7 +731,7 @@ static hipError_t launch_generic(const FcArgs& a, int K, int MT, int max_groups,
   long grid = (long)n_cu * per_cu;
   if (tiles < grid) grid = tiles;
   if (grid < 1) grid = 1;
-  const size_t dyn = (size_t)MT * K * 2 + (size_t)MT * n_slices(K) * 4;
+  const size_t dyn = (size_t)MT * fc_x_units(K) * 16 + (size_t)MT * n_slices(K) * 4;
   // The dynamic-LDS limit is raised once per kernel instance to the largest size any
   // call can ask for (idempotent, so a racing second call is harmless).
 #define MVQ_GEN_CASE(L, M)                                                                   \
@@ -621,7 +758,7 @@ static hipError_t launch_generic(const FcArgs& a, int K, int MT, int max_groups,
 hipError_t launch_fc1(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st) {
   (void)hipGetLastError();  // start from a clean error state: report only our own launches
   bool done = false;
-  hipError_t e = launch_tile<true>(a, a.H, MT, max_groups, st, &done);
+  hipError_t e = launch_stream<true>(a, a.H, MT, max_groups, n_cu, st, &done);
   if (e != hipSuccess || done) return e;
   return launch_generic<true>(a, a.H, MT, max_groups, n_cu, st);
 }
@@ -629,7 +766,7 @@ hipError_t launch_fc1(const FcArgs& a, int MT, int max_groups, int n_cu, hipStre
 hipError_t launch_fc2(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st) {
   (void)hipGetLastError();  // start from a clean error state: report only our own launches
   bool done = false;
-  hipError_t e = launch_tile<false>(a, a.I, MT, max_groups, st, &done);
+  hipError_t e = launch_stream<false>(a, a.I, MT, max_groups, n_cu, st, &done);
   if (e == hipSuccess && !done) e = launch_generic<false>(a, a.I, MT, max_groups, n_cu, st);
   if (e != hipSuccess) return e;
   const size_t n4 = (size_t)a.T * a.H / 4;

@@ -5,24 +5,97 @@
 
 namespace mvq {
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// Cross-lane reductions with DPP lane moves (VALU, no LDS traffic).  Every lane of the
+// wave must be active.  Control words: quad_perm [1,0,3,2] and [2,3,0,1] exchange
+// lanes 1 and 2 apart within a quad; row_half_mirror maps lane i to 7-i within each 8
+// lanes and row_mirror maps i to 15-i within each 16, so after the four moves every
+// lane of a 16-lane row holds the row's result.  Rows are combined through readlane.
+namespace dpp {
+constexpr int QUAD_XOR1 = 0xB1;
+constexpr int QUAD_XOR2 = 0x4E;
+constexpr int ROW_HALF_MIRROR = 0x141;
+constexpr int ROW_MIRROR = 0x140;
+}  // namespace dpp
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_i32<CTRL>(__builtin_bit_cast(int, v)));
 }
 
-// Sum over aligned groups of W consecutive lanes (W a power of two <= 64).
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over aligned groups of W consecutive lanes (W = 2, 4, 8, 16 or 64); every lane
+// of a group receives the group's sum.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 64, "group width");
+  v += dpp_f32<dpp::QUAD_XOR1>(v);
+  if (W >= 4) v += dpp_f32<dpp::QUAD_XOR2>(v);
+  if (W >= 8) v += dpp_f32<dpp::ROW_HALF_MIRROR>(v);
+  if (W >= 16) v += dpp_f32<dpp::ROW_MIRROR>(v);
+  if (W == 64) v = (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
   return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<dpp::QUAD_XOR1>(v));
+  v = fmaxf(v, dpp_f32<dpp::QUAD_XOR2>(v));
+  v = fmaxf(v, dpp_f32<dpp::ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f32<dpp::ROW_MIRROR>(v));
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+
+// Inclusive prefix sum over the 64 lanes: row_shr by 1, 2, 4 and 8 within each
+// 16-lane row (lanes with no source in the row add 0), then the totals of the rows
+// below through readlane.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// (value, index) ordered by larger value, then smaller index.
+__device__ __forceinline__ bool arg_beats(float ov, int oi, float v, int i) {
+  return ov > v || (ov == v && oi < i);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = dpp_f32<CTRL>(v);
+  const int oi = dpp_i32<CTRL>(i);
+  if (arg_beats(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// Arg-max over the 64 lanes of the wave; every lane receives the winner.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<dpp::QUAD_XOR1>(v, i);
+  argmax_step<dpp::QUAD_XOR2>(v, i);
+  argmax_step<dpp::ROW_HALF_MIRROR>(v, i);
+  argmax_step<dpp::ROW_MIRROR>(v, i);
+  float bv = lane_f32(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) {
+    const float ov = lane_f32(v, r);
+    const int oi = __builtin_amdgcn_readlane(i, r);
+    if (arg_beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  v = bv;
+  i = bi;
 }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
@@ -42,9 +115,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // E8M0 shared exponent -> 2^(e-127) as fp32 (e = 0 gives the subnormal 2^-127, 255 NaN).
+// v_ldexp_f32 of 1.0 needs no literal constants; 255 gives 2^128 = inf, and inf - inf
+// is the NaN that code encodes.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  uint32_t bits = (e == 0) ? 0x00400000u : (e == 255 ? 0x7FC00000u : (e << 23));
-  return __builtin_bit_cast(float, bits);
+  const float v = __builtin_amdgcn_ldexpf(1.0f, (int)e - 127);
+  return e == 255 ? v - v : v;
 }
 
 // Fill the LDS decode table (see TAB_COPIES): entry b holds sgn(b) * CB[b & 0x7F] as
@@ -84,6 +159,15 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ float dot2h(half2_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(half2_t, b), c, false);
 }
+
+// Exponent e with m = f * 2^e, f in [0.5, 1) (one v_frexp_exp_i32_f32; 0 for zero).
+__device__ __forceinline__ int frexp_exponent(float m) { return __builtin_amdgcn_frexp_expf(m); }
+
+// x * 2^e (one v_ldexp_f32).
+__device__ __forceinline__ float ldexp2(float x, int e) { return __builtin_amdgcn_ldexpf(x, e); }
+
+// SiLU with the hardware exponential (v_exp_f32 of x * log2(e)).
+__device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(-g)); }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 

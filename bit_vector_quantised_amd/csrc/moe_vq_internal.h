@@ -84,23 +84,37 @@ __host__ __device__ inline SlotLayout slot_layout(int fmt, int H, int I) {
 
 __host__ __device__ inline int n_slices(int n) { return (n + SLICE - 1) / SLICE; }
 
+constexpr int MAX_MT = 4;  // largest token group of the decode-path FC kernels
+
 // One token group of one expert, as the FC kernels consume it: a tile is (group, block
 // of rows), so a tile reads one record to know where its codes and tokens are.
-struct GroupRec {
-  uint64_t slot_off;  // byte offset of the expert's slot in the pool
-  int32_t p0;         // first entry of the group in pair_list
-  int32_t mcount;     // tokens in the group (1..MT)
-  uint32_t fmt;       // slot format (MOE_VQ_FMT_ABSENT when not resident)
+struct __align__(16) GroupRec {
+  uint64_t slot_off;      // byte offset of the expert's slot in the pool
+  int32_t p0;             // first entry of the group in pair_list
+  int32_t mcount;         // tokens in the group (1..MT)
+  uint32_t fmt;           // slot format (MOE_VQ_FMT_ABSENT when not resident)
   int32_t expert;
-  int32_t pad[2];
+  int32_t pair[MAX_MT];   // the group's pair indices p = t*k + i (repeats the last when short)
+  int32_t pad[4];
 };
 
 // FC decode-path geometry shared by host and kernels.
 constexpr int FC_THREADS = 256;
 constexpr int LDS_LIMIT = 160 * 1024;
 
+// Staged activations in LDS: each 64-value fp16 chunk (128 B) is padded to 144 B so
+// that the 16 lanes of a row, which read 16 consecutive chunks, hit 16 distinct groups
+// of 4 banks.
+constexpr int XCHUNK_UNITS = 9;  // 16-byte units per padded chunk
+__host__ __device__ inline size_t fc_x_units(int K) { return (size_t)(K / 64) * XCHUNK_UNITS; }
+__host__ __device__ inline int x_unit(int u) { return (u >> 3) * XCHUNK_UNITS + (u & 7); }
+
+// LDS of one FC workgroup: table, padded activations, their slice factors and the
+// per-wave reduction slots, rounded up to the 512-byte allocation granularity.
 __host__ __device__ inline size_t fc_lds_bytes(int MT, int K) {
-  return (size_t)TAB_BYTES + (size_t)MT * K * 2 + (size_t)MT * n_slices(K) * 4 + 256;
+  const size_t b = (size_t)TAB_BYTES + (size_t)MT * fc_x_units(K) * 16 + (size_t)MT * n_slices(K) * 4 +
+                   (size_t)4 * MT * n_slices(K) * 4;
+  return (b + 511) & ~(size_t)511;
 }
 
 // Tokens of one expert that share one pass over its codes.

@@ -134,21 +134,36 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
 template <int NPL>
 __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, int* id_out) {
   const int KSP = (a.KS + 3) & ~3;
+  const int NQ = KSP / 4;                      // 16-byte partial groups per expert
+  constexpr int QMAX = MAX_DIM / SLICE / 4;    // at most 16 slices
+  constexpr int IB = NPL < 4 ? NPL : (NPL >= 16 ? 2 : 4);  // experts per lane batched
   float v[NPL];
+  // every partial of a batch is loaded before any is summed: a loop over the run-time
+  // slice count would wait for each load in turn
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    float acc = -INFINITY;
-    if (e < a.E) {
+  for (int i0 = 0; i0 < NPL; i0 += IB) {
+    float4 f[IB][QMAX];
+#pragma unroll
+    for (int ii = 0; ii < IB; ++ii) {
+      const int e = lane + 64 * (i0 + ii);
       const float4* src = reinterpret_cast<const float4*>(a.logits + ((size_t)t * a.E + e) * KSP);
-      acc = 0.f;
-      for (int q = 0; q < KSP / 4; ++q) {
-        const float4 f = src[q];
-        acc += f.x; acc += f.y; acc += f.z; acc += f.w;
-      }
-      if (acc != acc) acc = -INFINITY;  // NaN never wins
+#pragma unroll
+      for (int q = 0; q < QMAX; ++q)
+        f[ii][q] = (e < a.E && q < NQ) ? src[q] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    v[i] = acc;
+#pragma unroll
+    for (int ii = 0; ii < IB; ++ii) {
+      const int e = lane + 64 * (i0 + ii);
+      float acc = -INFINITY;
+      if (e < a.E) {
+        acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < QMAX; ++q)
+          if (q < NQ) { acc += f[ii][q].x; acc += f[ii][q].y; acc += f[ii][q].z; acc += f[ii][q].w; }
+        if (acc != acc) acc = -INFINITY;  // NaN never wins
+      }
+      v[i0 + ii] = acc;
+    }
   }
   uint32_t taken = 0;
   float my_l = -INFINITY, lmax = 0.f;
@@ -164,12 +179,7 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
         bid = e;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int oi = __shfl_xor(bid, o);
-      if (ob > best || (ob == best && oi < bid)) { best = ob; bid = oi; }
-    }
+    wave_argmax(best, bid);
     if (lane == (bid & 63)) taken |= 1u << (bid >> 6);
     if (j == 0) lmax = best;
     if (lane == j) { my_l = best; my_id = bid; }
@@ -194,25 +204,18 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   topk_token<NPL>(a, t, lane, &id);
 }
 
-// Exclusive block scan of four ints per thread over 1024 threads.
+// Exclusive block scan of four ints per thread over 1024 threads: DPP scans within
+// each wave, then one over the 16 wave totals in wave 0.
 __device__ int4 block_scan_excl4(int4 v, int4* wave_tot, int4* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int4 inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int nx = __shfl_up(inc.x, o), ny = __shfl_up(inc.y, o), nz = __shfl_up(inc.z, o), nw = __shfl_up(inc.w, o);
-    if (lane >= o) { inc.x += nx; inc.y += ny; inc.z += nz; inc.w += nw; }
-  }
+  const int4 inc = make_int4(wave_incl_scan(v.x), wave_incl_scan(v.y), wave_incl_scan(v.z), wave_incl_scan(v.w));
   if (lane == 63) wave_tot[wave] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int4 run = make_int4(0, 0, 0, 0);
-    for (int w = 0; w < 16; ++w) {
-      const int4 c = wave_tot[w];
-      wave_tot[w] = run;
-      run.x += c.x; run.y += c.y; run.z += c.z; run.w += c.w;
-    }
-    *total = run;
+  if (wave == 0) {
+    const int4 c = lane < 16 ? wave_tot[lane] : make_int4(0, 0, 0, 0);
+    const int4 w = make_int4(wave_incl_scan(c.x), wave_incl_scan(c.y), wave_incl_scan(c.z), wave_incl_scan(c.w));
+    if (lane < 16) wave_tot[lane] = make_int4(w.x - c.x, w.y - c.y, w.z - c.z, w.w - c.w);
+    if (lane == 15) *total = w;
   }
   __syncthreads();
   const int4 b = wave_tot[wave];
@@ -222,6 +225,7 @@ __device__ int4 block_scan_excl4(int4 v, int4* wave_tot, int4* total) {
 }
 
 constexpr int FUSED_TOPK_MAX_T = 64;
+constexpr int PL_LDS = 2048;  // pair lists up to this length are also kept in LDS
 
 // Single workgroup: (optionally the top-k of every token, one wave per token), then
 // group the routed pairs by expert (stable: ascending pair index p = t*k + i within an
@@ -235,9 +239,21 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   __shared__ int4 s_total;
   __shared__ int s_bad_expert;
   __shared__ int s_bad_id;
+  __shared__ int pl_lds[PL_LDS];
+  // per active expert, by rank: first pair, pair count, group prefixes, slot
+  __shared__ int r_start[MAX_E], r_tot[MAX_E], r_gs1[MAX_E], r_gs2[MAX_E], r_expert[MAX_E];
+  __shared__ uint32_t r_fmt[MAX_E];
+  __shared__ uint64_t r_off[MAX_E];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int E = a.E, T = a.T, k = a.k;
-  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
+  // the slot of expert tid is read first, so that its latency overlaps the top-k
+  moe_vq_slot sl{};
+  if (tid < E) sl = a.slots[tid];
+  // counting waves: wave w takes tokens [w*C, (w+1)*C), with as many waves as tokens
+  // (up to 16), so that the per-expert totals sum over no more waves than needed
+  const int NWC = T < 16 ? (T > 1 ? T : 1) : 16;
+  const int C = (T + NWC - 1) / NWC;
+  for (int i = tid; i < NWC * E; i += 1024) cnt[i] = 0;
   if (tid == 0) { s_bad_expert = 0x7FFFFFFF; s_bad_id = 0; }
   if (FUSED) {
     for (int t = wave; t < T; t += 16) {
@@ -248,7 +264,6 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   }
   __syncthreads();
   auto id_of = [&](int p) -> int { return FUSED ? ids_lds[p] : a.topk_ids[p]; };
-  const int C = (T + 15) / 16;
   const int tb = min(T, wave * C), te = min(T, tb + C);
   for (int p = tb * k + lane; p < te * k; p += 64) {
     const int e = id_of(p);
@@ -258,13 +273,12 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   __syncthreads();
   int tot = 0;
   if (tid < E)
-    for (int w = 0; w < 16; ++w) tot += cnt[w * E + tid];
+    for (int w = 0; w < NWC; ++w) tot += cnt[w * E + tid];
   const int g1 = (tot + a.MT1 - 1) / a.MT1;
   const int g2 = (tot + a.MT2 - 1) / a.MT2;
   const int4 sc = block_scan_excl4(make_int4(tot, tot > 0 ? 1 : 0, g1, g2), wave_tot, &s_total);
   const int start = sc.x, rank = sc.y, gs1 = sc.z, gs2 = sc.w;
   if (tid < E && tot > 0) {
-    const moe_vq_slot sl = a.slots[tid];
     uint32_t fmt = sl.format;
     const uint64_t off = sl.byte_offset;
     uint64_t need = 0;
@@ -280,18 +294,8 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
     a.act_fmt[rank] = fmt;
     a.grp1[rank] = gs1;
     a.grp2[rank] = gs2;
-    for (int gi = 0; gi < g1 && gs1 + gi < a.G1; ++gi) {
-      GroupRec r;
-      r.slot_off = off; r.p0 = start + gi * a.MT1; r.mcount = min(a.MT1, tot - gi * a.MT1);
-      r.fmt = fmt; r.expert = tid; r.pad[0] = r.pad[1] = 0;
-      a.rec1[gs1 + gi] = r;
-    }
-    for (int gi = 0; gi < g2 && gs2 + gi < a.G2; ++gi) {
-      GroupRec r;
-      r.slot_off = off; r.p0 = start + gi * a.MT2; r.mcount = min(a.MT2, tot - gi * a.MT2);
-      r.fmt = fmt; r.expert = tid; r.pad[0] = r.pad[1] = 0;
-      a.rec2[gs2 + gi] = r;
-    }
+    r_start[rank] = start; r_tot[rank] = tot; r_gs1[rank] = gs1; r_gs2[rank] = gs2;
+    r_expert[rank] = tid; r_fmt[rank] = fmt; r_off[rank] = off;
   }
   if (tid == 0) {
     const int n_active = s_total.y;
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   // per-wave bases: cnt[w][e] <- start[e] + sum_{w' < w} cnt[w'][e]
   if (tid < E) {
     int run = start;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < NWC; ++w) {
       const int c = cnt[w * E + tid];
       cnt[w * E + tid] = run;
       run += c;
@@ -318,8 +322,41 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
       if ((unsigned)e < (unsigned)E) {
         const int pos = atomicAdd(&cnt[wave * E + e], 1);
         a.pair_list[pos] = p;
+        pl_lds[pos < PL_LDS ? pos : 0] = p;
       }
     }
+  }
+  __syncthreads();
+  // token-group records: group g of a list belongs to the active expert of largest
+  // rank whose group prefix is <= g (found by bisection over the LDS prefixes)
+  const int n_act = s_total.y, G1n = s_total.z, G2n = s_total.w;
+  const bool pl_in_lds = T * k <= PL_LDS;
+  for (int gg = tid; gg < G1n + G2n; gg += 1024) {
+    const bool one = gg < G1n;
+    const int g = one ? gg : gg - G1n;
+    if (g >= (one ? a.G1 : a.G2)) continue;
+    const int* gs = one ? r_gs1 : r_gs2;
+    const int MT = one ? a.MT1 : a.MT2;
+    int lo = 0, hi = n_act - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gs[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    const int gi = g - gs[lo];
+    GroupRec r;
+    r.slot_off = r_off[lo];
+    r.p0 = r_start[lo] + gi * MT;
+    r.mcount = min(MT, r_tot[lo] - gi * MT);
+    r.fmt = r_fmt[lo];
+    r.expert = r_expert[lo];
+#pragma unroll
+    for (int j = 0; j < MAX_MT; ++j) {
+      const int q = r.p0 + (j < r.mcount ? j : r.mcount - 1);
+      r.pair[j] = pl_in_lds ? pl_lds[q] : a.pair_list[q];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.pad[j] = 0;
+    (one ? a.rec1 : a.rec2)[g] = r;
   }
   if (tid == 0) {
     uint32_t status = MOE_VQ_OK;

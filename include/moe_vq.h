@@ -51,6 +51,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Only the moe_vq_* entry points are exported from the shared library; it is built
+ * with hidden visibility for everything else. */
+#if defined(__GNUC__)
+#pragma GCC visibility push(default)
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -162,5 +168,9 @@ const char *moe_vq_strerror(int status);
 
 #ifdef __cplusplus
 }
+#endif
+
+#if defined(__GNUC__)
+#pragma GCC visibility pop
 #endif
 #endif /* MOE_VQ_H */

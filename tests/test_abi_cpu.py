@@ -33,6 +33,20 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(_lib.EXPORTS)
 
 
+def test_only_the_c_api_is_exported():
+    """Internal (C++) functions stay hidden: a second copy of the library in the same
+    process cannot take them over."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    funcs = sorted({ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] in "TW"})
+    assert funcs and all(f.startswith("moe_vq_") for f in funcs), [f for f in funcs if not f.startswith("moe_vq_")][:10]
+    assert set(funcs) == set(declared_functions())
+
+
 def test_expert_bytes():
     assert _lib.expert_bytes(_lib.FMT_VQ2, 7168, 2048) == 11_698_176
     assert _lib.expert_bytes(_lib.FMT_MXFP4, 7168, 2048) == 23_396_352
