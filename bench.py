@@ -1,6 +1,8 @@
 """Benchmark of the MoE-VQ routed-expert step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b1|b32|b8mx] [--no-cpu-baseline]
+    python bench.py --copy-probe                 # plain device copy of known size (counter scale)
+    python bench.py --traffic-from DIR [--config C]   # counter CSVs -> profiles/traffic_fc1_C.json
 
 One step = route (router product, softmax/top-k/renormalise, worklist) -> FC1 with
 SiLU*up -> FC2 with the weighted combine, for one batch of synthetic tokens whose
@@ -14,6 +16,13 @@ Prints one JSON line.  `value` is tokens/s of the whole step timed on the host
 between two device synchronisations; `roofline` rates the dominant kernel (FC1)
 by its algorithmic code+scale bytes per launch over its mean duration measured
 with HIP events on the launch stream inside the timed region.
+
+`roofline.traffic` is the FC1 kernel's HBM traffic per launch as the hardware
+counters saw it: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc
+run each) scaled by what the same counters read for a plain device copy of known
+size (--copy-probe).  --traffic-from turns the four runs' CSV files into
+profiles/traffic_fc1_<config>.json, tagged with a hash of the kernel sources; the
+figure is reported only while the sources still match it.
 """
 from __future__ import annotations
 
@@ -65,6 +74,67 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+COPY_PROBE_BYTES = 256 << 20
+
+
+def copy_probe():
+    """A plain device-to-device copy of COPY_PROBE_BYTES, five times: under a counter run
+    its FETCH_SIZE / WRITE_SIZE per dispatch give the scale of those counters."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 5}), flush=True)
+
+
+def _counter_rows(d, counter):
+    """(kernel name, value) of every dispatch in rocprofv3 counter CSVs under d."""
+    import csv
+    rows = []
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(root, fn)) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_from(d, config):
+    """Combine four counter runs (d/fc1_fetch, d/fc1_write, d/copy_fetch, d/copy_write)
+    into the FC1 traffic record read by the benchmark."""
+    import statistics
+
+    def fc1(rows):
+        v = [x for n, x in rows if "fc_" in n and "true>" in n]
+        return statistics.median(v), len(v), sorted({n for n, x in rows if "fc_" in n and "true>" in n})
+
+    def copy(rows):
+        # the largest dispatch of the copy run is the copy of COPY_PROBE_BYTES
+        return max(x for n, x in rows)
+
+    fetch, nf, names = fc1(_counter_rows(os.path.join(d, "fc1_fetch"), "FETCH_SIZE"))
+    write, nw, _ = fc1(_counter_rows(os.path.join(d, "fc1_write"), "WRITE_SIZE"))
+    c_fetch = copy(_counter_rows(os.path.join(d, "copy_fetch"), "FETCH_SIZE"))
+    c_write = copy(_counter_rows(os.path.join(d, "copy_write"), "WRITE_SIZE"))
+    f_scale = COPY_PROBE_BYTES / c_fetch   # bytes per counter unit, from the copy
+    w_scale = COPY_PROBE_BYTES / c_write
+    rec = {"source_hash": source_hash(), "config": config, "kernels": names,
+           "fetch_counter_per_launch": fetch, "write_counter_per_launch": write,
+           "copy_fetch_counter": c_fetch, "copy_write_counter": c_write,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "bytes_per_launch": fetch * f_scale + write * w_scale,
+           "dispatches": [nf, nw]}
+    out = os.path.join(ROOT, "profiles", f"traffic_fc1_{config}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(syn, x_pool_np, top_k, budget_s=15.0):
     """The fp64 oracle (as it is) on consecutive tokens of the same pool, until about
     budget_s seconds of work; returns tokens/s and the sample description."""
@@ -99,11 +169,20 @@ def main():
     ap.add_argument("--config", default="b1", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--traffic-from", default=None)
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from, args.config)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the routed-expert step is measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import numpy as np
     import torch
@@ -200,7 +279,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "fc_kernel<16,MT,FC1> (FC1 gate/up decode + SiLU*up)",
+                     "kernel": "fc_stream_kernel FC1 (gate/up VQ2 decode + SiLU*up)",
                      "bytes_per_launch": fc1_b, "mean_launch_us": fc1_avg_s * 1e6},
         "code_stream": {"GBps": code_stream, "frac": code_stream / HBM_PEAK_GBPS,
                         "fc1_us": fc1_avg_s * 1e6, "fc2_us": fc2_avg_s * 1e6, "bytes_per_step": step_b},

@@ -68,34 +68,38 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// (value, index) ordered by larger value, then smaller index.
-__device__ __forceinline__ bool arg_beats(float ov, int oi, float v, int i) {
-  return ov > v || (ov == v && oi < i);
+// Order-preserving map of a float to uint32 (larger float -> larger key, -0 == +0;
+// NaN must be excluded by the caller) and its inverse.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f + 0.0f);  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  const float ov = dpp_f32<CTRL>(v);
-  const int oi = dpp_i32<CTRL>(i);
-  if (arg_beats(ov, oi, v, i)) { v = ov; i = oi; }
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v, uint64_t old) {
+  const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)old, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(old >> 32), (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// Arg-max over the 64 lanes of the wave; every lane receives the winner.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_step<dpp::QUAD_XOR1>(v, i);
-  argmax_step<dpp::QUAD_XOR2>(v, i);
-  argmax_step<dpp::ROW_HALF_MIRROR>(v, i);
-  argmax_step<dpp::ROW_MIRROR>(v, i);
-  float bv = lane_f32(v, 0);
-  int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16) {
-    const float ov = lane_f32(v, r);
-    const int oi = __builtin_amdgcn_readlane(i, r);
-    if (arg_beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
-  v = bv;
-  i = bi;
+// Unsigned 64-bit maximum over the 64 lanes, returned to every lane.  After the four
+// in-row moves every lane of a row holds the row maximum; row_bcast:15 then brings
+// row 0 into row 1 and row 2 into row 3, row_bcast:31 brings row 1 into rows 2-3, so
+// lane 63 ends with the maximum of all rows.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<dpp::QUAD_XOR1>(v, 0); v = o > v ? o : v;
+  o = dpp_u64<dpp::QUAD_XOR2>(v, 0); v = o > v ? o : v;
+  o = dpp_u64<dpp::ROW_HALF_MIRROR>(v, 0); v = o > v ? o : v;
+  o = dpp_u64<dpp::ROW_MIRROR>(v, 0); v = o > v ? o : v;
+  o = dpp_u64<0x142, 0xA>(v, v); v = o > v ? o : v;  // row_bcast:15 into rows 1 and 3
+  o = dpp_u64<0x143, 0xC>(v, v); v = o > v ? o : v;  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {

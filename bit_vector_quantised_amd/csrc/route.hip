@@ -165,24 +165,29 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
       v[i0 + ii] = acc;
     }
   }
-  uint32_t taken = 0;
+  // Each candidate is one 64-bit key: the order-preserving logit bits above, ~id
+  // below, so that the unsigned maximum is the larger logit and, among equal logits,
+  // the lower id.  Key 0 (below every real key) marks a taken or missing expert.
+  uint64_t key[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < a.E ? ((uint64_t)f32_order_key(v[i]) << 32) | (uint32_t)~e : 0ull;
+  }
   float my_l = -INFINITY, lmax = 0.f;
   int my_id = 0;
   for (int j = 0; j < a.k; ++j) {
-    float best = -INFINITY;
-    int bid = 0x7FFFFFFF;
+    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + 64 * i;
-      if (e < a.E && !(taken & (1u << i)) && (v[i] > best || (v[i] == best && e < bid))) {
-        best = v[i];
-        bid = e;
-      }
-    }
-    wave_argmax(best, bid);
-    if (lane == (bid & 63)) taken |= 1u << (bid >> 6);
-    if (j == 0) lmax = best;
-    if (lane == j) { my_l = best; my_id = bid; }
+    for (int i = 0; i < NPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int bid = (int)~(uint32_t)best;
+    const float bl = f32_from_order_key((uint32_t)(best >> 32));
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + 64 * i == bid) key[i] = 0;
+    if (j == 0) lmax = bl;
+    if (lane == j) { my_l = bl; my_id = bid; }
   }
   const float p = (lane < a.k) ? expf(my_l - lmax) : 0.f;
   const float tot = wave_sum(p);
