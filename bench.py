@@ -41,7 +41,10 @@ WORKLOADS = {
     "b1": "decode batch 1: H=7168 I=2048 E=256 top-8, VQ2 2.125 b/w, bf16 x ~N(0,1), 256 experts resident",
     "b32": "decode batch 32: H=7168 I=2048 E=256 top-8, VQ2, router logits with Zipf(1.1) expert popularity",
     "b8mx": "decode batch 8: 52 most-routed experts MXFP4, 204 VQ2, Zipf(1.1) routing",
+    "p4096": "prefill chunk of 4096 tokens: H=7168 I=2048 E=256 top-8, VQ2, grouped fp16 MFMA GEMMs",
 }
+PREFILL = {"p4096"}
+MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
 def expert_stream_bytes(dev, experts):
@@ -135,7 +138,7 @@ def traffic_from(d, config):
     print(json.dumps(rec))
 
 
-def cpu_baseline(syn, x_pool_np, top_k, budget_s=15.0):
+def cpu_baseline(syn, x_pool_np, top_k, budget_s=15.0, tokens_per_call=None):
     """The fp64 oracle (as it is) on consecutive tokens of the same pool, until about
     budget_s seconds of work; returns tokens/s and the sample description."""
     import numpy as np
@@ -147,7 +150,7 @@ def cpu_baseline(syn, x_pool_np, top_k, budget_s=15.0):
         blas_threads = 1
     t0 = time.perf_counter()
     n = 0
-    T = syn.cfg.n_tokens
+    T = tokens_per_call or syn.cfg.n_tokens
     while True:
         x = x_pool_np[(n * T) % x_pool_np.shape[0]:][:T]
         oracle.forward(syn, oracle.x_value(x, "bf16"), top_k)
@@ -197,7 +200,8 @@ def main():
     print(f"[bench] building {args.config} layer ({cfg.n_experts} experts)", file=sys.stderr, flush=True)
     syn_dev = synth.SynthLayer(cfg, cache=False)
     dev = DeviceLayer.from_synth(syn_dev)
-    n_pool = 256 if T == 1 else max(8, 256 // T) * T
+    prefill = args.config in PREFILL
+    n_pool = 256 if T == 1 else (max(8, 256 // T) * T if T <= 256 else 2 * T)
     x_pool_np = synth.SynthLayer(cfg, cache=False).x(n=n_pool, stream=7)
     x_pool = torch.from_numpy(x_pool_np.view(np.int16)).cuda().view(torch.bfloat16)
     n_batches = n_pool // T
@@ -209,6 +213,12 @@ def main():
         step.route(xb)
         if ev is not None:
             ev[0].record(stream)
+        if prefill:
+            step.prefill(xb)
+            if ev is not None:
+                ev[1].record(stream)
+                ev[2].record(stream)
+            return
         step.fc1(T)
         if ev is not None:
             ev[1].record(stream)
@@ -277,17 +287,30 @@ def main():
                    "inter": cfg.inter, "n_experts": cfg.n_experts, "top_k": k,
                    "unique_experts_per_step": float(np.mean([uniq[b] for b in bidx])),
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "fc_stream_kernel FC1 (gate/up VQ2 decode + SiLU*up)",
-                     "bytes_per_launch": fc1_b, "mean_launch_us": fc1_avg_s * 1e6},
-        "code_stream": {"GBps": code_stream, "frac": code_stream / HBM_PEAK_GBPS,
-                        "fc1_us": fc1_avg_s * 1e6, "fc2_us": fc2_avg_s * 1e6, "bytes_per_step": step_b},
     }
+    if prefill:
+        # FC1 + FC2 as grouped MFMA GEMMs: 2 * 3 * H * I flops per routed pair
+        flops = 2.0 * 3 * cfg.hidden * cfg.inter * T * k
+        pf_s = fc1_avg_s  # the events bracket the whole prefill call (stage, GEMMs, combine)
+        tflops = flops / pf_s / 1e12
+        out["dtype"] = "fp16 MFMA (decoded weights x fp16-staged activations), fp32 accumulate"
+        out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                           "kernel": "moe_vq_prefill_gemm (prefill_fc_kernel FC1 + FC2, grouped fp16 MFMA)",
+                           "flops_per_launch": flops, "mean_launch_us": pf_s * 1e6}
+        out["prefill"] = {"ms": pf_s * 1e3, "code_bytes_per_step": step_b}
+    else:
+        out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                           "kernel": "fc_stream_kernel FC1 (gate/up VQ2 decode + SiLU*up)",
+                           "bytes_per_launch": fc1_b, "mean_launch_us": fc1_avg_s * 1e6}
+        out["code_stream"] = {"GBps": code_stream, "frac": code_stream / HBM_PEAK_GBPS,
+                              "fc1_us": fc1_avg_s * 1e6, "fc2_us": fc2_avg_s * 1e6, "bytes_per_step": step_b}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         syn_or = synth.SynthLayer(cfg)
-        out["cpu_baseline"] = cpu_baseline(syn_or, x_pool_np, k, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(syn_or, x_pool_np, k, args.cpu_budget,
+                                           tokens_per_call=8 if prefill else None)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -194,10 +194,32 @@ int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n
   if (n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
   if (x_dtype != MOE_VQ_F32 && x_dtype != MOE_VQ_BF16) return MOE_VQ_EINVAL;
   if (n_tokens == 0) return MOE_VQ_OK;
-  if (!x || !y) return MOE_VQ_EINVAL;
+  if (!x || !y || ((uintptr_t)x & 15) || ((uintptr_t)y & 15)) return MOE_VQ_EINVAL;
   if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
-  (void)stream;
-  return MOE_VQ_EUNSUPPORTED;
+  const int E = L->n_experts, H = L->hidden, I = L->inter, k = L->top_k, T = n_tokens;
+  const WsLayout W = ws_layout(E, H, I, k, T);
+  PrefillArgs a{};
+  a.pool = L->pool;
+  a.codebook = static_cast<const uint16_t*>(L->codebook);
+  a.hdr = at<const uint32_t>(ws, W.hdr);
+  a.act_start = at<const int32_t>(ws, W.act_start);
+  a.act_off = at<const uint64_t>(ws, W.act_off);
+  a.act_fmt = at<const uint32_t>(ws, W.act_fmt);
+  a.pair_list = at<const int32_t>(ws, W.pair_list);
+  a.pair_w = at<const float>(ws, W.pair_w);
+  a.x = x;
+  a.x16 = at<uint16_t>(ws, W.x16);
+  a.x16_e = at<int32_t>(ws, W.x16_e);
+  a.mt_pre = at<int32_t>(ws, W.mt_pre);
+  a.hmax = at<uint32_t>(ws, W.hmax);
+  a.h = at<float>(ws, W.h_pre);
+  a.o_buf = at<float>(ws, W.o_buf);
+  a.y = y;
+  a.T = T; a.H = H; a.I = I; a.k = k; a.E = E;
+  a.key = shape_key(T, E, k, H, I);
+  a.vq2 = slot_layout(MOE_VQ_FMT_VQ2, H, I);
+  a.mx4 = slot_layout(MOE_VQ_FMT_MXFP4, H, I);
+  return hip_status(launch_prefill(a, x_dtype, static_cast<hipStream_t>(stream)));
 }
 
 int moe_vq_decode_expert(const moe_vq_layer* L, int expert, int matrix, int out_dtype, void* out,

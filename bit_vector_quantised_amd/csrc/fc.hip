@@ -771,8 +771,12 @@ hipError_t launch_fc2(const FcArgs& a, int MT, int max_groups, int n_cu, hipStre
   if (e != hipSuccess) return e;
   const size_t n4 = (size_t)a.T * a.H / 4;
   const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
-  combine_kernel<<<blocks, 256, 0, st>>>(a.out, a.y, a.T, a.H, a.k);
+  launch_combine(a.out, a.y, a.T, a.H, a.k, blocks, st);
   return hipGetLastError();
+}
+
+void launch_combine(const float* o_buf, float* y, int T, int H, int k, int blocks, hipStream_t st) {
+  combine_kernel<<<blocks, 256, 0, st>>>(o_buf, y, T, H, k);
 }
 
 }  // namespace mvq

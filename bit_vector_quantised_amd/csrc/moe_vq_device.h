@@ -102,6 +102,26 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Exclusive block scan of four ints per thread over 1024 threads: DPP scans within
+// each wave, then one over the 16 wave totals in wave 0.
+__device__ inline int4 block_scan_excl4(int4 v, int4* wave_tot, int4* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int4 inc = make_int4(wave_incl_scan(v.x), wave_incl_scan(v.y), wave_incl_scan(v.z), wave_incl_scan(v.w));
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int4 c = lane < 16 ? wave_tot[lane] : make_int4(0, 0, 0, 0);
+    const int4 w = make_int4(wave_incl_scan(c.x), wave_incl_scan(c.y), wave_incl_scan(c.z), wave_incl_scan(c.w));
+    if (lane < 16) wave_tot[lane] = make_int4(w.x - c.x, w.y - c.y, w.z - c.z, w.w - c.w);
+    if (lane == 15) *total = w;
+  }
+  __syncthreads();
+  const int4 b = wave_tot[wave];
+  const int4 r = make_int4(b.x + inc.x - v.x, b.y + inc.y - v.y, b.z + inc.z - v.z, b.w + inc.w - v.w);
+  __syncthreads();
+  return r;
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }

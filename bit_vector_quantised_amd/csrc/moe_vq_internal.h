@@ -131,10 +131,23 @@ __host__ __device__ inline int fc_max_groups(int T, int k, int E, int MT) {
   return (int)((P + act * (MT - 1)) / MT);
 }
 
+// Prefill (grouped matrix-core GEMM) geometry.
+constexpr int PF_BM = 64;    // tokens of one expert per tile
+constexpr int PF_KG = 128;   // reduction step: one scale group
+
+__host__ __device__ inline int pf_rows_per_tile(bool fc1) { return fc1 ? 128 : 256; }
+
+// Upper bound on the prefill token tiles: each active expert adds at most one partial tile.
+__host__ __device__ inline int pf_max_mtiles(int T, int k, int E) {
+  const long P = (long)T * k;
+  const long act = P < E ? P : E;
+  return (int)(P / PF_BM + act);
+}
+
 // Workspace layout for (E, H, I, k, T).
 struct WsLayout {
   size_t hdr, logits, x_h, x_sc, act_expert, act_start, act_off, act_fmt, grp1, grp2, rec1, rec2,
-      pair_list, pair_w, o_buf, total;
+      pair_list, pair_w, o_buf, x16, x16_e, mt_pre, hmax, h_pre, total;
   int KS;  // number of activation slices of H
   int MT1, MT2, G1, G2;
 };
@@ -164,6 +177,13 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int T) {
   L.pair_list = take(P * 4);
   L.pair_w = take(P * 4);
   L.o_buf = take(P * H * 4);
+  // prefill: activations as fp16 with one power-of-two factor per token, the token-tile
+  // prefix over the active experts, the per-pair max |h| and h itself
+  L.x16 = take((size_t)T * H * 2);
+  L.x16_e = take((size_t)T * 4);
+  L.mt_pre = take((size_t)(E + 1) * 4);
+  L.hmax = take(P * 4);
+  L.h_pre = take(P * I * 4);
   L.total = off;
   return L;
 }
@@ -220,6 +240,28 @@ struct FcArgs {
   int T, H, I, k, KS, E;
   uint32_t key;
   int max_groups;            // upper bound on token groups for this T
+  SlotLayout vq2, mx4;
+};
+
+struct PrefillArgs {
+  const uint8_t* pool;
+  const uint16_t* codebook;  // fp16 [128][4]
+  const uint32_t* hdr;
+  const int32_t* act_start;  // [n_active + 1] first pair of each active expert
+  const uint64_t* act_off;
+  const uint32_t* act_fmt;
+  const int32_t* pair_list;
+  const float* pair_w;
+  const void* x;             // [T][H] f32 or bf16
+  uint16_t* x16;             // [T][H] fp16 bits
+  int32_t* x16_e;            // [T] x = x16 * 2^e
+  int32_t* mt_pre;           // [E + 1] token-tile prefix over active experts
+  uint32_t* hmax;            // [P] bits of max |h| per pair
+  float* h;                  // [P][I]
+  float* o_buf;              // [P][H]
+  float* y;                  // [T][H]
+  int T, H, I, k, E;
+  uint32_t key;
   SlotLayout vq2, mx4;
 };
 

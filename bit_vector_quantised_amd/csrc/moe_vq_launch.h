@@ -12,6 +12,12 @@ hipError_t launch_route(const RouteArgs& ra, int x_dtype, const WorklistArgs& wa
 hipError_t launch_fc1(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st);
 hipError_t launch_fc2(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st);
 
+// y[t] = sum_i o_buf[t*k + i] (the per-pair outputs, already weighted).
+void launch_combine(const float* o_buf, float* y, int T, int H, int k, int blocks, hipStream_t st);
+
+// Prefill: stage x, token tiles, FC1 and FC2 as grouped MFMA GEMMs, combine.
+hipError_t launch_prefill(const PrefillArgs& a, int x_dtype, hipStream_t st);
+
 hipError_t launch_decode_expert(const uint8_t* pool, const moe_vq_slot* slots, uint64_t pool_bytes,
                                 const uint16_t* codebook, int H, int I, int expert, int matrix,
                                 int out_dtype, void* out, int32_t* status_dev, hipStream_t st);

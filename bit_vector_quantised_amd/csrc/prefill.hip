@@ -1,0 +1,420 @@
+// Prefill form of the routed-expert step: the tokens of each expert are grouped into
+// tiles of PF_BM tokens, and FC1 (gate/up, SiLU*up fused) and FC2 (down, routing weight
+// fused) run as grouped matrix-core GEMMs (v_mfma_f32_16x16x32_f16) over expert weights
+// decoded in registers.  The per-pair FC2 outputs are summed per token by the decode
+// path's combine kernel.
+//
+// Sources: the routed experts are 2-bit vector codes with a sign-symmetric codebook,
+// decoded on the fly (Tandem-vLLM 0.2.0 announcement, "How it works"; vLLM-Moet README,
+// "2-bit experts on vLLM v0.24.0"); tokens are grouped per expert with no padding of an
+// expert to a fixed row count and no padding rows written back (vLLM-Moet README, "What
+// we changed against official vLLM", rows "MoE at decode" and "prefill").
+//
+// Operands.  A (activations) is fp16: x with one power-of-two factor per token (exact
+// for bf16 values no smaller than 2^-24 of the token's largest), h with one per pair.
+// B (weights) is decoded per lane: a VQ2 word through the LDS table of signed codebook
+// vectors, times its group scale in fp16 (one rounding, relative error <= 2^-11); MXFP4
+// bytes with the gfx950 FP4->FP16 convert and the E8M0 scale (exact within the fp16
+// range).  The contraction index is permuted the same way in A and B: within a
+// 128-wide scale group, lanes 16q..16q+15 hold k = 32q + 8s + (0..7) at MFMA step s, so
+// one lane's codes for a group are contiguous (8 VQ2 bytes or 16 MXFP4 bytes).
+//
+// MFMA lane layout (16x16x32): A lane l holds row l%16, k = 8(l/16)+0..7; B lane l holds
+// column l%16, the same k; D lane l holds column l%16, rows 4(l/16)+0..3.
+#include <type_traits>
+
+#include "moe_vq_device.h"
+#include "moe_vq_launch.h"
+
+namespace mvq {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int PF_THREADS = 256;
+constexpr int PF_AROW = PF_KG + 8;  // fp16 per staged row: 272 B, so 16 rows hit 16 bank groups
+
+template <bool FC1>
+struct PfGeom {
+  static constexpr int NM = FC1 ? 2 : 1;                 // matrices (gate, up) or (down)
+  static constexpr int NB = FC1 ? 2 : 4;                 // 16-row blocks per wave per matrix
+  static constexpr int BN = (PF_THREADS / 64) * NB * 16;  // rows per tile
+  static_assert(BN == (FC1 ? 128 : 256), "tile rows");
+};
+
+__device__ __forceinline__ bool pf_ws_ok(const PrefillArgs& a) {
+  return a.hdr[HDR_KEY] == a.key && a.hdr[HDR_N_ACTIVE] <= (uint32_t)a.E;
+}
+
+// ---------------------------------------------------------------------------------------
+// x -> fp16 with one power-of-two factor per token; zero the per-pair max |h|
+// ---------------------------------------------------------------------------------------
+
+template <bool XF32>
+__global__ __launch_bounds__(PF_THREADS) void prefill_stage_kernel(PrefillArgs a) {
+  __shared__ float red[PF_THREADS / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H;
+  auto load8 = [&](int c, float* v) {
+    if (XF32) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)t * H + c);
+      const float4 u = p[0], w = p[1];
+      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w; v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
+    } else {
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * H + c);
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = bf16_bits_to_f32(wd[q] & 0xFFFFu);
+        v[2 * q + 1] = bf16_bits_to_f32(wd[q] >> 16);
+      }
+    }
+  };
+  float m = 0.f;
+  for (int c = tid * 8; c < H; c += PF_THREADS * 8) {
+    float v[8];
+    load8(c, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+  }
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int ex = 0;
+  if (m > 0.f && m == m) ex = frexp_exponent(m) - 15;  // |x| * 2^-ex < 2^15
+  for (int c = tid * 8; c < H; c += PF_THREADS * 8) {
+    float v[8];
+    load8(c, v);
+    uint4 o;
+    uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const _Float16 lo = (_Float16)ldexp2(v[2 * q], -ex), hi = (_Float16)ldexp2(v[2 * q + 1], -ex);
+      ow[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(a.x16 + (size_t)t * H + c) = o;
+  }
+  if (tid == 0) a.x16_e[t] = ex;
+  if (tid < a.k) a.hmax[(size_t)t * a.k + tid] = 0u;
+}
+
+// ---------------------------------------------------------------------------------------
+// Token-tile prefix over the active experts (one workgroup)
+// ---------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void prefill_setup_kernel(PrefillArgs a) {
+  __shared__ int4 wave_tot[16];
+  __shared__ int4 s_total;
+  const int tid = threadIdx.x;
+  if (!pf_ws_ok(a)) return;
+  const int n_act = (int)a.hdr[HDR_N_ACTIVE];
+  const int m = tid < n_act ? a.act_start[tid + 1] - a.act_start[tid] : 0;
+  const int c = (m + PF_BM - 1) / PF_BM;
+  const int4 sc = block_scan_excl4(make_int4(c, 0, 0, 0), wave_tot, &s_total);
+  if (tid < n_act) a.mt_pre[tid] = sc.x;
+  if (tid == 0) a.mt_pre[n_act] = s_total.x;
+}
+
+// ---------------------------------------------------------------------------------------
+// Grouped GEMM tile: PF_BM tokens of one expert x BN rows
+// ---------------------------------------------------------------------------------------
+
+// Codes one lane needs for one (matrix, row block) and one scale group.
+struct PfCodes {
+  uint4 q;      // VQ2: 8 bytes in q.x, q.y; MXFP4: 16 bytes
+  uint32_t s;   // VQ2: fp16 scale bits; MXFP4: E8M0 byte
+};
+
+template <int FMT>
+__device__ __forceinline__ PfCodes pf_load_codes(const uint8_t* qb, const uint8_t* sb, int n, int K, int g, int kq) {
+  PfCodes c;
+  if (FMT == MOE_VQ_FMT_VQ2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(qb + (size_t)n * (K / 4) + g * 32 + kq * 8);
+    c.q = make_uint4(v.x, v.y, 0u, 0u);
+    c.s = *reinterpret_cast<const uint16_t*>(sb + ((size_t)n * (K / 128) + g) * 2);
+  } else if (FMT == MOE_VQ_FMT_MXFP4) {
+    c.q = *reinterpret_cast<const uint4*>(qb + (size_t)n * (K / 2) + g * 64 + kq * 16);
+    c.s = sb[(size_t)n * (K / 32) + g * 4 + kq];
+  } else {
+    c.q = make_uint4(0u, 0u, 0u, 0u);
+    c.s = 0u;
+  }
+  return c;
+}
+
+// B fragment (8 fp16 for k = 32q + 8s + 0..7) of step s.
+template <int FMT, int S>
+__device__ __forceinline__ half8_t pf_decode(const uint2* tab, const PfCodes& c, uint32_t laneoff) {
+  half8_t b;
+  if (FMT == MOE_VQ_FMT_VQ2) {
+    const uint32_t wd = (S < 2) ? c.q.x : c.q.y;
+    const uint2 e0 = tab_lookup(tab, tab_addr<(2 * S) & 3>(wd, laneoff));
+    const uint2 e1 = tab_lookup(tab, tab_addr<(2 * S + 1) & 3>(wd, laneoff));
+    const half2_t sc = __builtin_bit_cast(half2_t, (c.s & 0xFFFFu) * 0x10001u);
+    const half2_t p0 = __builtin_bit_cast(half2_t, e0.x) * sc, p1 = __builtin_bit_cast(half2_t, e0.y) * sc;
+    const half2_t p2 = __builtin_bit_cast(half2_t, e1.x) * sc, p3 = __builtin_bit_cast(half2_t, e1.y) * sc;
+    b[0] = p0[0]; b[1] = p0[1]; b[2] = p1[0]; b[3] = p1[1];
+    b[4] = p2[0]; b[5] = p2[1]; b[6] = p3[0]; b[7] = p3[1];
+  } else if (FMT == MOE_VQ_FMT_MXFP4) {
+    const uint32_t wd = S == 0 ? c.q.x : S == 1 ? c.q.y : S == 2 ? c.q.z : c.q.w;
+    const float sc = e8m0_to_f32(c.s);
+    const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 0);
+    const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 1);
+    const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 2);
+    const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 3);
+    b[0] = p0[0]; b[1] = p0[1]; b[2] = p1[0]; b[3] = p1[1];
+    b[4] = p2[0]; b[5] = p2[1]; b[6] = p3[0]; b[7] = p3[1];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) b[q] = (_Float16)0.f;
+  }
+  return b;
+}
+
+template <bool FC1>
+struct PfTile {
+  int p_lo, mcnt, nt;
+  uint32_t fmt;
+  uint64_t off;
+};
+
+// Main loop of one tile for one weight format.
+template <bool FC1, int FMT>
+__device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>& tl, const uint2* tab,
+                                        _Float16 (*As)[PF_BM * PF_AROW], f32x4_t (&acc)[PfGeom<FC1>::NM][PfGeom<FC1>::NB][4],
+                                        const int* s_pair, const float* s_fac) {
+  using G = PfGeom<FC1>;
+  constexpr int NM = G::NM, NB = G::NB, BN = G::BN;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i16 = lane & 15, kq = lane >> 4;
+  const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
+  const int K = FC1 ? a.H : a.I;
+  const int NROWS = FC1 ? a.I : a.H;
+  const int NG = K / PF_KG;
+  const SlotLayout& SL = FMT == MOE_VQ_FMT_MXFP4 ? a.mx4 : a.vq2;
+  const uint8_t* slot = a.pool + tl.off;
+  const uint8_t* qb[NM];
+  const uint8_t* sb[NM];
+  qb[0] = slot + (FC1 ? SL.q_gate : SL.q_down);
+  sb[0] = slot + (FC1 ? SL.s_gate : SL.s_down);
+  if (NM > 1) { qb[NM - 1] = slot + SL.q_up; sb[NM - 1] = slot + SL.s_up; }
+  int rows[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)  // rows past the end re-read the last row; the epilogue drops them
+    rows[nb] = min(tl.nt * BN + wave * NB * 16 + nb * 16 + i16, NROWS - 1);
+
+  // staging: thread tid stages 32 consecutive k of token row tid/4
+  const int srow = tid >> 2, skq = (tid & 3) * 32;
+  const int sp = s_pair[srow];  // -1 past the tile's tokens
+  constexpr int AV = FC1 ? 4 : 8;  // 16-byte loads per thread per group
+  auto a_load = [&](int g, uint4 (&v)[AV]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (sp >= 0) {
+      if (FC1) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.x16 + (size_t)(sp / a.k) * K + g * PF_KG + skq);
+#pragma unroll
+        for (int i = 0; i < AV; ++i) v[i] = src[i];
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(a.h + (size_t)sp * K + g * PF_KG + skq);
+#pragma unroll
+        for (int i = 0; i < AV; ++i) v[i] = src[i];
+      }
+    }
+  };
+  auto a_store = [&](int buf, const uint4 (&v)[AV]) __attribute__((always_inline)) {
+    uint4* dst = reinterpret_cast<uint4*>(&As[buf][srow * PF_AROW + skq]);
+    if (FC1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = v[i];
+    } else {
+      // fp32 h -> fp16 with the pair's power-of-two factor
+      const float f = s_fac[srow];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 u0 = __builtin_bit_cast(float4, v[2 * i]), u1 = __builtin_bit_cast(float4, v[2 * i + 1]);
+        const float w8[8] = {u0.x * f, u0.y * f, u0.z * f, u0.w * f, u1.x * f, u1.y * f, u1.z * f, u1.w * f};
+        uint4 o;
+        uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ow[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w8[2 * q]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w8[2 * q + 1]) << 16);
+        dst[i] = o;
+      }
+    }
+  };
+
+  PfCodes cur[NM][NB], nxt[NM][NB];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) cur[m][nb] = pf_load_codes<FMT>(qb[m], sb[m], rows[nb], K, 0, kq);
+  {
+    uint4 v[AV];
+    a_load(0, v);
+    a_store(0, v);
+  }
+  __syncthreads();
+
+  for (int g = 0; g < NG; ++g) {
+    const int buf = g & 1;
+    const bool more = g + 1 < NG;
+    uint4 av[AV];
+    if (more) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) nxt[m][nb] = pf_load_codes<FMT>(qb[m], sb[m], rows[nb], K, g + 1, kq);
+      a_load(g + 1, av);
+    }
+    const _Float16* Ab = As[buf];
+    auto step = [&](auto S_) __attribute__((always_inline)) {
+      constexpr int S = decltype(S_)::value;
+      half8_t af[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        af[mb] = *reinterpret_cast<const half8_t*>(&Ab[(mb * 16 + i16) * PF_AROW + 32 * kq + 8 * S]);
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const half8_t bf = pf_decode<FMT, S>(tab, cur[m][nb], laneoff);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf, acc[m][nb][mb], 0, 0, 0);
+        }
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    if (more) {
+      a_store(buf ^ 1, av);
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) cur[m][nb] = nxt[m][nb];
+    }
+    __syncthreads();
+  }
+}
+
+template <bool FC1>
+__global__ __launch_bounds__(PF_THREADS, 1) void prefill_fc_kernel(PrefillArgs a) {
+  using G = PfGeom<FC1>;
+  constexpr int NM = G::NM, NB = G::NB, BN = G::BN;
+  __shared__ uint2 tab[256 * TAB_COPIES];
+  __shared__ __align__(16) _Float16 As[2][PF_BM * PF_AROW];
+  __shared__ int s_pair[PF_BM];
+  __shared__ float s_fac[PF_BM];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i16 = lane & 15, kq = lane >> 4;
+  if (!pf_ws_ok(a)) return;
+  const int NROWS = FC1 ? a.I : a.H;
+  const int NT = (NROWS + BN - 1) / BN;
+  const int n_act = (int)a.hdr[HDR_N_ACTIVE];
+  const int mt = blockIdx.x / NT;
+  if (mt >= a.mt_pre[n_act]) return;
+  // active expert of this token tile: the last rank whose tile prefix is <= mt
+  int lo = 0, hi = n_act - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.mt_pre[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  PfTile<FC1> tl;
+  tl.nt = blockIdx.x % NT;
+  tl.p_lo = a.act_start[lo] + (mt - a.mt_pre[lo]) * PF_BM;
+  tl.mcnt = min(PF_BM, a.act_start[lo + 1] - tl.p_lo);
+  tl.fmt = a.act_fmt[lo];
+  tl.off = a.act_off[lo];
+
+  build_vq2_table(tab, a.codebook, tid, PF_THREADS);
+  if (tid < PF_BM) {
+    const int p = tid < tl.mcnt ? a.pair_list[tl.p_lo + tid] : -1;
+    s_pair[tid] = p;
+    float f = 1.f;
+    if (!FC1 && p >= 0) {
+      const float hm = __builtin_bit_cast(float, a.hmax[p]);
+      const int ex = (hm > 0.f && hm == hm) ? frexp_exponent(hm) - 15 : 0;
+      f = ldexp2(1.0f, -ex);
+    }
+    s_fac[tid] = f;
+  }
+  __syncthreads();
+
+  f32x4_t acc[NM][NB][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[m][nb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (tl.fmt == MOE_VQ_FMT_VQ2) pf_tile<FC1, MOE_VQ_FMT_VQ2>(a, tl, tab, As, acc, s_pair, s_fac);
+  else if (tl.fmt == MOE_VQ_FMT_MXFP4) pf_tile<FC1, MOE_VQ_FMT_MXFP4>(a, tl, tab, As, acc, s_pair, s_fac);
+  // (an absent expert keeps zeros; the worklist has set MOE_VQ_ENOTRESIDENT)
+
+  // epilogue: D lane holds column i16 (output row) and token rows 4*kq + 0..3 of each block
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = mb * 16 + 4 * kq + r;
+      const int p = s_pair[row];
+      float hm = 0.f;
+      if (p >= 0) {
+        if (FC1) {
+          const float f = ldexp2(1.0f, a.x16_e[p / a.k]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int n = tl.nt * BN + wave * NB * 16 + nb * 16 + i16;
+            const float gv = acc[0][nb][mb][r] * f, uv = acc[1][nb][mb][r] * f;
+            const float h = silu_fast(gv) * uv;
+            if (n < NROWS) {
+              a.h[(size_t)p * a.I + n] = h;
+              hm = fmaxf(hm, fabsf(h));
+            }
+          }
+        } else {
+          const float f = a.pair_w[p] / s_fac[row];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int n = tl.nt * BN + wave * NB * 16 + nb * 16 + i16;
+            if (n < NROWS) a.o_buf[(size_t)p * a.H + n] = acc[0][nb][mb][r] * f;
+          }
+        }
+      }
+      if (FC1) {
+        // the 16 lanes of one token row are one DPP row: reduce, then one atomic per row
+        hm = fmaxf(hm, dpp_f32<dpp::QUAD_XOR1>(hm));
+        hm = fmaxf(hm, dpp_f32<dpp::QUAD_XOR2>(hm));
+        hm = fmaxf(hm, dpp_f32<dpp::ROW_HALF_MIRROR>(hm));
+        hm = fmaxf(hm, dpp_f32<dpp::ROW_MIRROR>(hm));
+        if (i16 == 0 && p >= 0) atomicMax(&a.hmax[p], __builtin_bit_cast(uint32_t, hm));
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Host launcher
+// ---------------------------------------------------------------------------------------
+
+hipError_t launch_prefill(const PrefillArgs& a, int x_dtype, hipStream_t st) {
+  (void)hipGetLastError();  // start from a clean error state: report only our own launches
+  if (x_dtype == MOE_VQ_F32) prefill_stage_kernel<true><<<a.T, PF_THREADS, 0, st>>>(a);
+  else prefill_stage_kernel<false><<<a.T, PF_THREADS, 0, st>>>(a);
+  prefill_setup_kernel<<<1, 1024, 0, st>>>(a);
+  const long mt_max = pf_max_mtiles(a.T, a.k, a.E);
+  const long g1 = mt_max * ((a.I + pf_rows_per_tile(true) - 1) / pf_rows_per_tile(true));
+  const long g2 = mt_max * ((a.H + pf_rows_per_tile(false) - 1) / pf_rows_per_tile(false));
+  if (g1 > 0x7FFFFFFF || g2 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  prefill_fc_kernel<true><<<(unsigned)g1, PF_THREADS, 0, st>>>(a);
+  prefill_fc_kernel<false><<<(unsigned)g2, PF_THREADS, 0, st>>>(a);
+  const size_t n4 = (size_t)a.T * a.H / 4;
+  const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
+  launch_combine(a.o_buf, a.y, a.T, a.H, a.k, blocks, st);
+  return hipGetLastError();
+}
+
+}  // namespace mvq

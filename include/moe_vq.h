@@ -130,10 +130,17 @@ int moe_vq_fc1_silu(const moe_vq_layer *layer, int n_tokens, void *ws, size_t ws
 int moe_vq_fc2_combine(const moe_vq_layer *layer, const float *h, int n_tokens,
                        void *ws, size_t ws_bytes, float *y, void *stream);
 
-/* Prefill form of FC1 + FC2 + combine for large n_tokens: tokens grouped per expert,
- * decoded weight tiles feed bf16 matrix-core (MFMA) products with fp32 accumulation;
- * SiLU*up fused into the FC1 epilogue, the routing weight into the FC2 epilogue.
- * Requires moe_vq_route_topk on the same x first.  y [n_tokens][H] fp32, overwritten. */
+/* Prefill form of FC1 + FC2 + combine for large n_tokens (vLLM-Moet README, "What we
+ * changed against official vLLM", rows "MoE at decode" and "prefill": tokens grouped per
+ * expert, no padding to a fixed row count).  The routed pairs of each expert are cut into
+ * tiles of 64 tokens; FC1 (gate/up, SiLU*up fused) and FC2 (down, routing weight fused)
+ * run as fp16 matrix-core (MFMA) products with fp32 accumulation over weights decoded in
+ * registers (VQ2: codebook vector times group scale, rounded once to fp16; MXFP4: exact
+ * within the fp16 range).  x is staged as fp16 with one power-of-two factor per token, h
+ * with one per routed pair.  Requires moe_vq_route_topk on the same x and n_tokens first
+ * (it builds the worklist this call reads).  x: [n_tokens][H] in x_dtype, 16-byte
+ * aligned; y: [n_tokens][H] fp32, 16-byte aligned, overwritten.  Errors: as
+ * moe_vq_fc2_combine; an absent expert contributes 0 and is reported by moe_vq_check. */
 int moe_vq_prefill_gemm(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
                         void *ws, size_t ws_bytes, float *y, void *stream);
 

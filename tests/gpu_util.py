@@ -91,3 +91,20 @@ def decode_on_gpu(dev: DeviceLayer, e: int, mat: int, out_dtype: int):
                        torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     return out.cpu().numpy(), int(status.item())
+
+
+def run_prefill(dev: DeviceLayer, x_np: np.ndarray, x_dtype: str, step: Step = None):
+    """route -> prefill grouped GEMM; returns the step's selection, weights and y."""
+    T = x_np.shape[0]
+    st = step or Step(dev, max(T, 1))
+    xt = x_tensor(x_np, x_dtype)
+    st.route(xt)
+    st.prefill(xt)
+    torch.cuda.synchronize()
+    status, info = st.check()
+    return {
+        "ids": st.ids[:T].cpu().numpy().astype(np.int64),
+        "w": st.w[:T].cpu().numpy().astype(np.float64),
+        "y": st.y[:T].cpu().numpy().astype(np.float64),
+        "status": status, "info": info, "step": st,
+    }
