@@ -27,8 +27,7 @@
 //    staged activations are built once and restaged only when the token group changes.
 //  * fc_generic_kernel (any K multiple of 128): a persistent grid that prefetches one
 //    chunk ahead; used for the shapes the tile kernel does not cover.
-#include "moe_vq_device.h"
-#include "moe_vq_launch.h"
+#include "fc_common.h"
 
 namespace mvq {
 
@@ -38,28 +37,6 @@ constexpr int LB_MX = 14;   // same budget for MXFP4 tiles (twice the bytes per 
 // -------------------------------------------------------------------------------------
 // Shared pieces
 // -------------------------------------------------------------------------------------
-
-// Fill the table from one codebook entry per thread (threads 0..255 own words 0..255);
-// the copy index is rotated by lane so that one ds_write_b64 instruction spreads over
-// all banks.
-__device__ __forceinline__ void write_table_entry(uint2* tab, uint2 cbv, int b) {
-  const uint32_t flip = (b & 128) ? 0x80008000u : 0u;
-  const uint2 v = make_uint2(cbv.x ^ flip, cbv.y ^ flip);
-  const int rot = b & 31;
-#pragma unroll
-  for (int c = 0; c < TAB_COPIES; ++c) tab[b * TAB_COPIES + ((c + rot) & 31)] = v;
-}
-
-__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
-  const _Float16 l = (_Float16)lo, h = (_Float16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
-}
-
-__device__ __forceinline__ bool ws_ok(const FcArgs& a, bool fc1, int MT) {
-  return a.hdr[HDR_KEY] == a.key && a.hdr[HDR_N_ACTIVE] <= (uint32_t)a.E &&
-         a.hdr[fc1 ? HDR_GROUPS1 : HDR_GROUPS2] <= (uint32_t)a.max_groups &&
-         a.hdr[fc1 ? HDR_MT1 : HDR_MT2] == (uint32_t)MT;
-}
 
 // Four VQ2 words (one dword of codes) against their 16 fp16 activations (8 dwords),
 // added to p in order.  A 16-byte chunk is four such steps.
@@ -120,39 +97,6 @@ struct TileGeom {
   static constexpr int RPP_MX = RPP_MX_RAW < 1 ? 1 : (RPP_MX_RAW > RPL ? RPL : RPP_MX_RAW);
 };
 
-// The fields of a GroupRec a tile needs, held in scalar registers (uniform per workgroup).
-struct RecS {
-  uint64_t slot_off;
-  int32_t mcount;
-  uint32_t fmt;
-  int32_t pair[MAX_MT];
-};
-
-__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// v through an empty asm statement: the compiler cannot treat what is derived from it
-// as loop-invariant.
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-static_assert(offsetof(GroupRec, mcount) == 12 && offsetof(GroupRec, fmt) == 16 &&
-              offsetof(GroupRec, pair) == 24, "GroupRec layout");
-
-__device__ __forceinline__ RecS load_rec(const GroupRec* recs, int g) {
-  const int4* p = reinterpret_cast<const int4*>(recs + g);
-  const int4 w0 = p[0], w1 = p[1];
-  RecS r;
-  r.slot_off = ((uint64_t)(uint32_t)uni(w0.y) << 32) | (uint32_t)uni(w0.x);
-  r.mcount = uni(w0.w);
-  r.fmt = (uint32_t)uni(w1.x);
-  const int* wi = reinterpret_cast<const int*>(recs + g);
-#pragma unroll
-  for (int j = 0; j < MAX_MT; ++j) r.pair[j] = uni(wi[6 + j]);
-  return r;
-}
-
 // The code words and scales one lane reads for one VQ2 tile.
 template <int CPL, int MT, bool FC1>
 struct VqBuf {
@@ -186,16 +130,6 @@ __device__ __forceinline__ void issue_vq(VqBuf<CPL, MT, FC1>& b, const FcArgs& a
         b.s[rr][m][j] = *reinterpret_cast<const uint16_t*>((m == 0 ? sb0 : sb1) + so + j * 16);
       }
   }
-}
-
-// Same tokens (FC1: the token of every pair; FC2: the pair itself, whose h is staged).
-template <int MT, bool FC1>
-__device__ __forceinline__ bool same_inputs(const RecS& x, const RecS& y, int k) {
-  if (x.mcount != y.mcount) return false;
-  bool eq = true;
-#pragma unroll
-  for (int j = 0; j < MT; ++j) eq = eq && (FC1 ? (x.pair[j] / k == y.pair[j] / k) : (x.pair[j] == y.pair[j]));
-  return eq;
 }
 
 template <int CPL, int MT, bool FC1>
@@ -758,7 +692,9 @@ static hipError_t launch_generic(const FcArgs& a, int K, int MT, int max_groups,
 hipError_t launch_fc1(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st) {
   (void)hipGetLastError();  // start from a clean error state: report only our own launches
   bool done = false;
-  hipError_t e = launch_stream<true>(a, a.H, MT, max_groups, n_cu, st, &done);
+  hipError_t e = launch_mfma<true>(a, a.H, MT, max_groups, n_cu, st, &done);
+  if (e != hipSuccess || done) return e;
+  e = launch_stream<true>(a, a.H, MT, max_groups, n_cu, st, &done);
   if (e != hipSuccess || done) return e;
   return launch_generic<true>(a, a.H, MT, max_groups, n_cu, st);
 }
@@ -766,7 +702,8 @@ hipError_t launch_fc1(const FcArgs& a, int MT, int max_groups, int n_cu, hipStre
 hipError_t launch_fc2(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st) {
   (void)hipGetLastError();  // start from a clean error state: report only our own launches
   bool done = false;
-  hipError_t e = launch_stream<false>(a, a.I, MT, max_groups, n_cu, st, &done);
+  hipError_t e = launch_mfma<false>(a, a.I, MT, max_groups, n_cu, st, &done);
+  if (e == hipSuccess && !done) e = launch_stream<false>(a, a.I, MT, max_groups, n_cu, st, &done);
   if (e == hipSuccess && !done) e = launch_generic<false>(a, a.I, MT, max_groups, n_cu, st);
   if (e != hipSuccess) return e;
   const size_t n4 = (size_t)a.T * a.H / 4;

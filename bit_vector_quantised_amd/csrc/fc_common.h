@@ -1,0 +1,75 @@
+// Pieces shared by the decode-path FC kernels (vector-ALU stream/generic kernels and
+// the matrix-core kernel): table fill, workspace check, token-group records.
+#pragma once
+
+#include "moe_vq_device.h"
+#include "moe_vq_launch.h"
+
+namespace mvq {
+
+// Fill the table from one codebook entry per thread (threads 0..255 own words 0..255);
+// the copy index is rotated by lane so that one ds_write_b64 instruction spreads over
+// all banks.
+__device__ __forceinline__ void write_table_entry(uint2* tab, uint2 cbv, int b) {
+  const uint32_t flip = (b & 128) ? 0x80008000u : 0u;
+  const uint2 v = make_uint2(cbv.x ^ flip, cbv.y ^ flip);
+  const int rot = b & 31;
+#pragma unroll
+  for (int c = 0; c < TAB_COPIES; ++c) tab[b * TAB_COPIES + ((c + rot) & 31)] = v;
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+  const _Float16 l = (_Float16)lo, h = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+__device__ __forceinline__ bool ws_ok(const FcArgs& a, bool fc1, int MT) {
+  return a.hdr[HDR_KEY] == a.key && a.hdr[HDR_N_ACTIVE] <= (uint32_t)a.E &&
+         a.hdr[fc1 ? HDR_GROUPS1 : HDR_GROUPS2] <= (uint32_t)a.max_groups &&
+         a.hdr[fc1 ? HDR_MT1 : HDR_MT2] == (uint32_t)MT;
+}
+
+// The fields of a GroupRec a tile needs, held in scalar registers (uniform per workgroup).
+struct RecS {
+  uint64_t slot_off;
+  int32_t mcount;
+  uint32_t fmt;
+  int32_t pair[MAX_MT];
+};
+
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// v through an empty asm statement: the compiler cannot treat what is derived from it
+// as loop-invariant.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+static_assert(offsetof(GroupRec, mcount) == 12 && offsetof(GroupRec, fmt) == 16 &&
+              offsetof(GroupRec, pair) == 24, "GroupRec layout");
+
+__device__ __forceinline__ RecS load_rec(const GroupRec* recs, int g) {
+  const int4* p = reinterpret_cast<const int4*>(recs + g);
+  const int4 w0 = p[0], w1 = p[1];
+  RecS r;
+  r.slot_off = ((uint64_t)(uint32_t)uni(w0.y) << 32) | (uint32_t)uni(w0.x);
+  r.mcount = uni(w0.w);
+  r.fmt = (uint32_t)uni(w1.x);
+  const int* wi = reinterpret_cast<const int*>(recs + g);
+#pragma unroll
+  for (int j = 0; j < MAX_MT; ++j) r.pair[j] = uni(wi[6 + j]);
+  return r;
+}
+
+// Same tokens (FC1: the token of every pair; FC2: the pair itself, whose h is staged).
+template <int MT, bool FC1>
+__device__ __forceinline__ bool same_inputs(const RecS& x, const RecS& y, int k) {
+  if (x.mcount != y.mcount) return false;
+  bool eq = true;
+#pragma unroll
+  for (int j = 0; j < MT; ++j) eq = eq && (FC1 ? (x.pair[j] / k == y.pair[j] / k) : (x.pair[j] == y.pair[j]));
+  return eq;
+}
+
+}  // namespace mvq

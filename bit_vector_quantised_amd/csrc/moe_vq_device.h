@@ -166,6 +166,11 @@ __device__ __forceinline__ uint32_t tab_addr(uint32_t word, uint32_t laneoff) {
   return __builtin_amdgcn_perm(word, laneoff, 0x0c0c0400u + (SEL << 8));
 }
 
+// Same address with the byte selector as a value (a constant once loops are unrolled).
+__device__ __forceinline__ uint32_t tab_addr_sel(uint32_t word, uint32_t laneoff, uint32_t sel) {
+  return __builtin_amdgcn_perm(word, laneoff, 0x0c0c0400u + (sel << 8));
+}
+
 __device__ __forceinline__ uint2 tab_lookup(const uint2* tab, uint32_t addr) {
   return *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(tab) + addr);
 }
