@@ -127,6 +127,7 @@ int moe_vq_route_topk(const moe_vq_layer* L, const void* x, int x_dtype, int n_t
   ra.router_w = static_cast<const uint16_t*>(L->router_w);
   ra.x = x;
   ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.KS = W.KS;
+  ra.ksp = (W.KS + 3) & ~3;
   ra.logits = at<float>(ws, W.logits);
   ra.x_h = at<uint16_t>(ws, W.x_h);
   ra.x_sc = at<float>(ws, W.x_sc);

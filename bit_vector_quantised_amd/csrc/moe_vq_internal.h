@@ -194,7 +194,8 @@ struct RouteArgs {
   const uint16_t* router_w;  // bf16 [E][H]
   const void* x;             // [T][H] f32 or bf16
   int T, H, E, k, KS;
-  float* logits;             // [T][E][KSP] partial sums, KSP = KS rounded up to 4
+  int ksp;                   // partial sums per (token, expert): KS rounded up to 4, or 1
+  float* logits;             // [T][E][ksp] partial sums
   uint16_t* x_h;             // [T][H] fp16 bits
   float* x_sc;               // [T][KS]
   int32_t* topk_ids;         // [T][k]

@@ -32,6 +32,10 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int PF_THREADS = 256;
+// The prefill table keeps 16 copies of the 256 signed codebook vectors (32 KiB): lookups
+// are a small part of this kernel's LDS traffic, and the smaller table lets two
+// workgroups share a CU.  Lane l reads copy l & 15 at byte b * 128 + (l & 15) * 8.
+constexpr int PF_COPIES = 16;
 constexpr int PF_AROW = PF_KG + 8;  // fp16 per staged row: 272 B, so 16 rows hit 16 bank groups
 
 template <bool FC1>
@@ -149,8 +153,9 @@ __device__ __forceinline__ half8_t pf_decode(const uint2* tab, const PfCodes& c,
   half8_t b;
   if (FMT == MOE_VQ_FMT_VQ2) {
     const uint32_t wd = (S < 2) ? c.q.x : c.q.y;
-    const uint2 e0 = tab_lookup(tab, tab_addr<(2 * S) & 3>(wd, laneoff));
-    const uint2 e1 = tab_lookup(tab, tab_addr<(2 * S + 1) & 3>(wd, laneoff));
+    // v_perm puts the code byte above the doubled lane offset; halving gives the address
+    const uint2 e0 = tab_lookup(tab, tab_addr<(2 * S) & 3>(wd, laneoff) >> 1);
+    const uint2 e1 = tab_lookup(tab, tab_addr<(2 * S + 1) & 3>(wd, laneoff) >> 1);
     const half2_t sc = __builtin_bit_cast(half2_t, (c.s & 0xFFFFu) * 0x10001u);
     const half2_t p0 = __builtin_bit_cast(half2_t, e0.x) * sc, p1 = __builtin_bit_cast(half2_t, e0.y) * sc;
     const half2_t p2 = __builtin_bit_cast(half2_t, e1.x) * sc, p3 = __builtin_bit_cast(half2_t, e1.y) * sc;
@@ -188,7 +193,7 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
   constexpr int NM = G::NM, NB = G::NB, BN = G::BN;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, kq = lane >> 4;
-  const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
+  const uint32_t laneoff = (uint32_t)(lane & 15) << 4;  // doubled: see PF_COPIES
   const int K = FC1 ? a.H : a.I;
   const int NROWS = FC1 ? a.I : a.H;
   const int NG = K / PF_KG;
@@ -302,10 +307,10 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
 }
 
 template <bool FC1>
-__global__ __launch_bounds__(PF_THREADS, 1) void prefill_fc_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a) {
   using G = PfGeom<FC1>;
   constexpr int NM = G::NM, NB = G::NB, BN = G::BN;
-  __shared__ uint2 tab[256 * TAB_COPIES];
+  __shared__ uint2 tab[256 * PF_COPIES];
   __shared__ __align__(16) _Float16 As[2][PF_BM * PF_AROW];
   __shared__ int s_pair[PF_BM];
   __shared__ float s_fac[PF_BM];
@@ -330,7 +335,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_fc_kernel(PrefillArgs a
   tl.fmt = a.act_fmt[lo];
   tl.off = a.act_off[lo];
 
-  build_vq2_table(tab, a.codebook, tid, PF_THREADS);
+  {
+    const uint2* cb2 = reinterpret_cast<const uint2*>(a.codebook);
+    for (int idx = tid; idx < 256 * PF_COPIES; idx += PF_THREADS) {
+      const int b = idx / PF_COPIES;
+      const uint2 v = cb2[b & 127];
+      const uint32_t flip = (b & 128) ? 0x80008000u : 0u;
+      tab[idx] = make_uint2(v.x ^ flip, v.y ^ flip);
+    }
+  }
   if (tid < PF_BM) {
     const int p = tid < tl.mcnt ? a.pair_list[tl.p_lo + tid] : -1;
     s_pair[tid] = p;

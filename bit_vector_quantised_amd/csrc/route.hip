@@ -15,7 +15,8 @@ constexpr int RT_TOKENS = 32;   // tokens per router workgroup
 
 // Partial router logits over one SLICE of H for RT_EXPERTS experts and up to
 // RT_TOKENS tokens; lane l covers 16 consecutive columns.  Partials are stored
-// [T][E][KSP] (slice fastest) so the top-k stage sums them with two 16-byte loads.
+// [T][E][ksp] (slice fastest, ksp = slices rounded up to 4) so the top-k stage sums
+// them with 16-byte loads.  (The matrix-core router writes complete logits, ksp = 1.)
 // Workgroups of expert group 0 also stage x as fp16 with a power-of-two factor per
 // (token, slice): x = x_h * x_sc exactly for bf16 inputs (|x_h| < 2^15).
 template <bool XF32>
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
   const int e0 = blockIdx.x * RT_EXPERTS + wave * 2;
   const int t0 = blockIdx.z * RT_TOKENS;
   const int t1 = min(a.T, t0 + RT_TOKENS);
-  const int KSP = (a.KS + 3) & ~3;
+  const int KSP = a.ksp;
 
   uint4 w[2][2];
 #pragma unroll
@@ -133,8 +134,8 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
 // i-th chosen id (in *id) and writes ids / weights to the outputs.
 template <int NPL>
 __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, int* id_out) {
-  const int KSP = (a.KS + 3) & ~3;
-  const int NQ = KSP / 4;                      // 16-byte partial groups per expert
+  const int KSP = a.ksp;
+  const int NQ = KSP / 4;                      // 16-byte partial groups per expert (0: one float)
   constexpr int QMAX = MAX_DIM / SLICE / 4;    // at most 16 slices
   constexpr int IB = NPL < 4 ? NPL : (NPL >= 16 ? 2 : 4);  // experts per lane batched
   float v[NPL];
@@ -150,6 +151,8 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
 #pragma unroll
       for (int q = 0; q < QMAX; ++q)
         f[ii][q] = (e < a.E && q < NQ) ? src[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (NQ == 0)  // one complete logit per expert
+        f[ii][0].x = e < a.E ? a.logits[(size_t)t * a.E + e] : 0.f;
     }
 #pragma unroll
     for (int ii = 0; ii < IB; ++ii) {
@@ -160,6 +163,7 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
 #pragma unroll
         for (int q = 0; q < QMAX; ++q)
           if (q < NQ) { acc += f[ii][q].x; acc += f[ii][q].y; acc += f[ii][q].z; acc += f[ii][q].w; }
+        if (NQ == 0) acc = f[ii][0].x;
         if (acc != acc) acc = -INFINITY;  // NaN never wins
       }
       v[i0 + ii] = acc;
@@ -361,6 +365,108 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Many tokens: the router product on the matrix cores, and the fp16 staging of x
+// ---------------------------------------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rf32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int RM_TOKENS = 64;   // tokens per workgroup (16 per wave)
+constexpr int RM_EXPERTS = 64;  // experts per workgroup (4 blocks of 16)
+constexpr int RM_MIN_T = 64;    // from this many bf16 tokens on, the matrix-core router
+
+// logits[t][e] = sum_h W_r[e][h] x[t][h] for bf16 x with v_mfma_f32_16x16x32_bf16 (bf16
+// products are exact in fp32; fp32 accumulation).  Wave w of a workgroup takes tokens
+// 16w..16w+15 of its 64 and all 64 of its experts; both operands are read straight from
+// global memory, 16 bytes per lane and step (A: token row, B: expert row).  Rows past T
+// or E re-read the last row and are not written.
+__global__ __launch_bounds__(256) void router_mfma_kernel(RouteArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i16 = lane & 15, kq = lane >> 4;
+  const int t0 = blockIdx.x * RM_TOKENS + wave * 16;
+  const int e0 = blockIdx.y * RM_EXPERTS;
+  const int H = a.H;
+  const uint16_t* xr = static_cast<const uint16_t*>(a.x) + (size_t)min(t0 + i16, a.T - 1) * H + 8 * kq;
+  const uint16_t* wr[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) wr[nb] = a.router_w + (size_t)min(e0 + nb * 16 + i16, a.E - 1) * H + 8 * kq;
+  rf32x4_t acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < H; k += 128) {
+    bf16x8_t af[4], bf[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      af[s] = *reinterpret_cast<const bf16x8_t*>(xr + k + 32 * s);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) bf[s][nb] = *reinterpret_cast<const bf16x8_t*>(wr[nb] + k + 32 * s);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[s][nb], acc[nb], 0, 0, 0);
+  }
+  // D: lane holds expert column i16 and token rows 4*kq + 0..3 of each block
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 4 * kq + r, e = e0 + nb * 16 + i16;
+      if (t < a.T && e < a.E) a.logits[(size_t)t * a.E + e] = acc[nb][r];
+    }
+}
+
+// x as fp16 with one power-of-two factor per (token, 1024-column slice), for the
+// decode-path FC kernels (exact for bf16 x): one wave per (token, slice), 16 columns
+// per lane.
+template <bool XF32>
+__global__ __launch_bounds__(64) void stage_x_kernel(RouteArgs a) {
+  const int lane = threadIdx.x, t = blockIdx.x, s = blockIdx.y;
+  const int c0 = s * SLICE + lane * 16;
+  const bool col_ok = c0 < a.H;
+  float xf[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) xf[q] = 0.f;
+  if (col_ok) {
+    if (XF32) {
+      const float4* px = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)t * a.H + c0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = px[q];
+        xf[4 * q] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
+      }
+    } else {
+      const uint4* px = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * a.H + c0);
+      const uint4 xv[2] = {px[0], px[1]};
+      const uint32_t* xw = reinterpret_cast<const uint32_t*>(xv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        xf[2 * q] = bf16_bits_to_f32(xw[q] & 0xFFFFu);
+        xf[2 * q + 1] = bf16_bits_to_f32(xw[q] >> 16);
+      }
+    }
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(xf[q]));
+  m = wave_max(m);
+  int ex = 0;
+  if (m > 0.f && m == m) ex = frexp_exponent(m) - 15;  // |x| * 2^-ex < 2^15
+  if (col_ok) {
+    uint32_t packed[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const _Float16 lo = (_Float16)ldexp2(xf[2 * q], -ex), hi = (_Float16)ldexp2(xf[2 * q + 1], -ex);
+      packed[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(a.x_h + (size_t)t * a.H + c0);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  }
+  if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = ldexp2(1.0f, ex);
+}
+
 template <int NPL>
 static void launch_topk_worklist(const RouteArgs& ra, const WorklistArgs& wa, hipStream_t st) {
   if (ra.T <= FUSED_TOPK_MAX_T) {
@@ -373,6 +479,19 @@ static void launch_topk_worklist(const RouteArgs& ra, const WorklistArgs& wa, hi
 
 hipError_t launch_route(const RouteArgs& ra, int x_dtype, const WorklistArgs& wa, hipStream_t st) {
   (void)hipGetLastError();  // start from a clean error state: report only our own launches
+  if (x_dtype == MOE_VQ_BF16 && ra.T >= RM_MIN_T) {
+    RouteArgs rm = ra;
+    rm.ksp = 1;
+    stage_x_kernel<false><<<dim3(rm.T, rm.KS), 64, 0, st>>>(rm);
+    router_mfma_kernel<<<dim3((rm.T + RM_TOKENS - 1) / RM_TOKENS, (rm.E + RM_EXPERTS - 1) / RM_EXPERTS), 256, 0, st>>>(rm);
+    const int npl = (rm.E + 63) / 64;
+    if (npl <= 1) launch_topk_worklist<1>(rm, wa, st);
+    else if (npl <= 2) launch_topk_worklist<2>(rm, wa, st);
+    else if (npl <= 4) launch_topk_worklist<4>(rm, wa, st);
+    else if (npl <= 8) launch_topk_worklist<8>(rm, wa, st);
+    else launch_topk_worklist<16>(rm, wa, st);
+    return hipGetLastError();
+  }
   dim3 g1((ra.E + RT_EXPERTS - 1) / RT_EXPERTS, ra.KS, (ra.T + RT_TOKENS - 1) / RT_TOKENS);
   if (x_dtype == MOE_VQ_F32)
     router_gemv_kernel<true><<<g1, 256, 0, st>>>(ra);
