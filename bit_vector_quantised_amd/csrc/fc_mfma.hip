@@ -52,11 +52,11 @@ struct MfGeom {
   static constexpr int ROWS = 16 * NB;
   static constexpr int KS = CPL;       // activation slices of 1024 columns
   // MXFP4 tiles load MXG groups per pass: the largest divisor of NGQ whose codes fit in
-  // about 40 registers next to the (live) VQ2 ring
+  // about 80 registers next to the (live) VQ2 ring
   static constexpr int mxg() {
     int best = 1;
     for (int d = 1; d <= NGQ; ++d)
-      if (NGQ % d == 0 && d * NM * NB * 5 <= 40) best = d;
+      if (NGQ % d == 0 && d * NM * NB * 5 <= 80) best = d;
     return best;
   }
   static constexpr int MXG = mxg();
@@ -244,18 +244,23 @@ __global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+          // the slot is consumed (lookups, scale) before its refill is issued, so the
+          // refill can land in the same registers: no copies of in-flight loads at
+          // the loop edge (a copy would wait for the load)
           const MfCode c = ring[gi][m][nb];
-          if (refill) ring[gi][m][nb] = vq_load(dn, gi, m, nb);
-          f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
+          half8_t bfr[4];
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const uint32_t wd = s < 2 ? c.q.x : c.q.y;
             const uint2 e0 = tab_lookup(tab, tab_addr_sel(wd, laneoff, (2 * s) & 3));
             const uint2 e1 = tab_lookup(tab, tab_addr_sel(wd, laneoff, (2 * s + 1) & 3));
-            const half8_t b = __builtin_bit_cast(half8_t, make_uint4(e0.x, e0.y, e1.x, e1.y));
-            tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], b, tmp, 0, 0, 0);
+            bfr[s] = __builtin_bit_cast(half8_t, make_uint4(e0.x, e0.y, e1.x, e1.y));
           }
           const float sc = f16_bits_to_f32(c.s);
+          if (refill) ring[gi][m][nb] = vq_load(dn, gi, m, nb);
+          f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], bfr[s], tmp, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[m][nb][r] = fmaf(sc * fx[r], tmp[r], acc[m][nb][r]);
         }
@@ -347,21 +352,30 @@ __global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
     }
   };
 
-  // ---- prologue
-  int t = t_begin;
-  RecS rc = load_rec(a.rec, t / RB);
-  stage(rc);
-  bool ring_ok = false;
-  if (rc.fmt == MOE_VQ_FMT_VQ2) {
-    const MfAddr d = vq_addr(rc, t % RB);
+  // Loads of a whole ring for tile (r, rb), in the order the refills use (group,
+  // matrix, row block); the scheduling barriers keep that order, so that the count of
+  // loads in flight after each slot is the same whichever way the loop is entered.
+  auto ring_load = [&](const RecS& r, int rb) __attribute__((always_inline)) {
+    const MfAddr d = vq_addr(r, rb);
 #pragma unroll
     for (int gi = 0; gi < NGQ; ++gi)
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) ring[gi][m][nb] = vq_load(d, gi, m, nb);
-    ring_ok = true;
-  }
+        for (int nb = 0; nb < NB; ++nb) {
+          ring[gi][m][nb] = vq_load(d, gi, m, nb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+  };
+
+  // ---- prologue.  Records are read one tile ahead of their use (rn is needed for the
+  // refill addresses while this tile decodes; reading it later would wait for loads
+  // issued after it).
+  int t = t_begin;
+  RecS rc = load_rec(a.rec, t / RB);
+  RecS rn = (t + 1 < t_end) ? load_rec(a.rec, (t + 1) / RB) : rc;
+  stage(rc);  // staging loads are issued before the code loads
+  if (rc.fmt == MOE_VQ_FMT_VQ2) ring_load(rc, t % RB);
   if (tid < 256) write_table_entry(tab, cbv, tid);
   __syncthreads();
 
@@ -369,25 +383,16 @@ __global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
   for (;;) {
     const int tn = t + 1;
     const bool more = tn < t_end;
-    const RecS rn = more ? load_rec(a.rec, tn / RB) : rc;
+    const RecS rnn = (tn + 1 < t_end) ? load_rec(a.rec, (tn + 1) / RB) : rn;
+    const bool next_vq = more && rn.fmt == MOE_VQ_FMT_VQ2;
     zero_acc();
-    bool next_ring = false;
     if (rc.fmt == MOE_VQ_FMT_VQ2) {
-      if (!ring_ok) {
-        const MfAddr d = vq_addr(rc, t % RB);
-#pragma unroll
-        for (int gi = 0; gi < NGQ; ++gi)
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) ring[gi][m][nb] = vq_load(d, gi, m, nb);
-      }
-      next_ring = more && rn.fmt == MOE_VQ_FMT_VQ2;
-      compute_vq(next_ring, rn, tn % RB);
-    } else if (rc.fmt == MOE_VQ_FMT_MXFP4) {
-      compute_mx(rc, t % RB);
+      compute_vq(next_vq, rn, tn % RB);  // refills the ring with tile tn's codes
+    } else {
+      if (rc.fmt == MOE_VQ_FMT_MXFP4) compute_mx(rc, t % RB);
+      // (an absent expert keeps zeros; the worklist has recorded MOE_VQ_ENOTRESIDENT)
+      if (next_vq) ring_load(rn, tn % RB);
     }
-    // (an absent expert keeps zeros; the worklist has recorded MOE_VQ_ENOTRESIDENT)
     finish(rc, t % RB, buf);
     if (!more) break;
     if (!same_inputs<MT, FC1>(rn, rc, a.k)) {
@@ -395,8 +400,8 @@ __global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
       stage(rn);
       __syncthreads();
     }
-    ring_ok = next_ring;
     rc = rn;
+    rn = rnn;
     t = tn;
     buf ^= 1;
   }
