@@ -302,7 +302,8 @@ def main():
     else:
         out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                           "kernel": "fc_stream_kernel FC1 (gate/up VQ2 decode + SiLU*up)",
+                           "kernel": ("fc_stream_kernel" if T <= 1 else "fc_mfma_kernel")
+                           + " FC1 (gate/up code decode + SiLU*up)",
                            "bytes_per_launch": fc1_b, "mean_launch_us": fc1_avg_s * 1e6}
         out["code_stream"] = {"GBps": code_stream, "frac": code_stream / HBM_PEAK_GBPS,
                               "fc1_us": fc1_avg_s * 1e6, "fc2_us": fc2_avg_s * 1e6, "bytes_per_step": step_b}

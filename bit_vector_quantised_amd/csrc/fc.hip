@@ -159,19 +159,24 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
   if (t_begin >= t_end) return;
 
   // Stage the activations of record r into LDS (FC1: fp16 x of its tokens; FC2: h of
-  // its pairs scaled to fp16 with one power-of-two factor per 1024-column slice).
-  auto stage = [&](const RecS& r) __attribute__((always_inline)) {
-    // 16-byte units of one token per thread (K / 8 units over FC_THREADS threads)
-    constexpr int XU = FC1 ? (K / 8 + FC_THREADS - 1) / FC_THREADS : 1;
+  // its pairs scaled to fp16 with one power-of-two factor per 1024-column slice), in two
+  // halves: the loads, then (after the caller has issued the tile's code loads, so that
+  // waiting for the activations does not wait for the codes too) the LDS stores.
+  // 16-byte units of one token per thread (K / 8 units over FC_THREADS threads)
+  constexpr int XU = FC1 ? (K / 8 + FC_THREADS - 1) / FC_THREADS : 1;
+  struct StageRegs {
+    uint4 xv[FC1 ? MT : 1][XU];
+    float scv[FC1 ? MT : 1];
+    float4 hv[FC1 ? 1 : MT * KS];
+  };
+  auto stage_load = [&](const RecS& r) __attribute__((always_inline)) -> StageRegs {
+    StageRegs g;
     // staging runs once per token group: its per-lane addresses are recomputed here
     // rather than hoisted out of the tile loop and held in registers across it
     const int tid = opaque(threadIdx.x);
-    const int wave = tid >> 6, lane = tid & 63;
     if (FC1) {
       // the token loop is unrolled so that every pair index is read with a constant
       // index (a per-lane index would put the record in scratch memory)
-      uint4 xv[MT][XU];
-      float scv[MT];
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
         const bool live = j < r.mcount;
@@ -180,30 +185,37 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
 #pragma unroll
         for (int i = 0; i < XU; ++i) {
           const int o = tid + i * FC_THREADS;
-          xv[j][i] = (live && o < K / 8) ? src[o] : make_uint4(0, 0, 0, 0);
+          g.xv[j][i] = (live && o < K / 8) ? src[o] : make_uint4(0, 0, 0, 0);
         }
-        scv[j] = (live && tid < KS) ? a.x_sc[tok * KS + tid] : 1.f;
+        g.scv[j] = (live && tid < KS) ? a.x_sc[tok * KS + tid] : 1.f;
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          g.hv[j * KS + s] = j < r.mcount ? reinterpret_cast<const float4*>(a.h_in + (size_t)r.pair[j] * K)[s * 256 + tid]
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return g;
+  };
+  auto stage_store = [&](const StageRegs& g) __attribute__((always_inline)) {
+    const int tid = opaque(threadIdx.x);
+    const int wave = tid >> 6, lane = tid & 63;
+    if (FC1) {
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
 #pragma unroll
         for (int i = 0; i < XU; ++i) {
           const int o = tid + i * FC_THREADS;
-          if (o < K / 8) xs[j * XT + x_unit(o)] = xv[j][i];
+          if (o < K / 8) xs[j * XT + x_unit(o)] = g.xv[j][i];
         }
-        if (tid < KS) xsc[j * KS + tid] = scv[j];
+        if (tid < KS) xsc[j * KS + tid] = g.scv[j];
       }
     } else {
-      float4 hv[MT * KS];
-#pragma unroll
-      for (int j = 0; j < MT; ++j)
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          hv[j * KS + s] = j < r.mcount ? reinterpret_cast<const float4*>(a.h_in + (size_t)r.pair[j] * K)[s * 256 + tid]
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int js = 0; js < MT * KS; ++js) {
-        const float4 v = hv[js];
+        const float4 v = g.hv[js];
         float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
         m = wave_max(m);
         if (lane == 0) red[wave][js] = m;
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
         const float m = fmaxf(fmaxf(red[0][js], red[1][js]), fmaxf(red[2][js], red[3][js]));
         int ex = 0;
         if (m > 0.f && m == m) ex = frexp_exponent(m) - 15;
-        const float4 v = hv[js];
+        const float4 v = g.hv[js];
         const int j = js / KS, s = js % KS;
         const uint2 pk = make_uint2(pack_half2(ldexp2(v.x, -ex), ldexp2(v.y, -ex)),
                                     pack_half2(ldexp2(v.z, -ex), ldexp2(v.w, -ex)));
@@ -370,9 +382,12 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
   RecS rc = load_rec(a.rec, t / RB);
   RecS rn = (t + 1 < t_end) ? load_rec(a.rec, (t + 1) / RB) : rc;
   VqBuf<CPL, MT, FC1> A, B;
-  stage(rc);  // staging loads are issued before the code loads
-  if (rc.fmt == MOE_VQ_FMT_VQ2) issue_vq(A, a, rc, t % RB, NROWS, wave, rg, sub);
-  write_table_entry(tab, cbv, tid);
+  {
+    const StageRegs g = stage_load(rc);
+    if (rc.fmt == MOE_VQ_FMT_VQ2) issue_vq(A, a, rc, t % RB, NROWS, wave, rg, sub);
+    write_table_entry(tab, cbv, tid);
+    stage_store(g);
+  }
   __syncthreads();
 
   // ---- steady state: the next tile's loads are in flight while this tile decodes.
@@ -390,9 +405,10 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
     else compute_mx(rc, t % RB);
     if (!more) return false;
     if (!same) {
-      __syncthreads();  // every wave is done with the staged activations
-      stage(rn);
+      const StageRegs g = stage_load(rn);
       if (rn.fmt == MOE_VQ_FMT_VQ2) issue_vq(nxt, a, rn, tn % RB, NROWS, wave, rg, sub);
+      __syncthreads();  // every wave is done with the staged activations
+      stage_store(g);
       __syncthreads();
     } else if (!prefetch && rn.fmt == MOE_VQ_FMT_VQ2) {
       issue_vq(nxt, a, rn, tn % RB, NROWS, wave, rg, sub);

@@ -32,6 +32,7 @@ __device__ __forceinline__ bool ws_ok(const FcArgs& a, bool fc1, int MT) {
 // The fields of a GroupRec a tile needs, held in scalar registers (uniform per workgroup).
 struct RecS {
   uint64_t slot_off;
+  int32_t p0;
   int32_t mcount;
   uint32_t fmt;
   int32_t pair[MAX_MT];
@@ -46,7 +47,7 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
-static_assert(offsetof(GroupRec, mcount) == 12 && offsetof(GroupRec, fmt) == 16 &&
+static_assert(offsetof(GroupRec, p0) == 8 && offsetof(GroupRec, mcount) == 12 && offsetof(GroupRec, fmt) == 16 &&
               offsetof(GroupRec, pair) == 24, "GroupRec layout");
 
 __device__ __forceinline__ RecS load_rec(const GroupRec* recs, int g) {
@@ -54,6 +55,7 @@ __device__ __forceinline__ RecS load_rec(const GroupRec* recs, int g) {
   const int4 w0 = p[0], w1 = p[1];
   RecS r;
   r.slot_off = ((uint64_t)(uint32_t)uni(w0.y) << 32) | (uint32_t)uni(w0.x);
+  r.p0 = uni(w0.z);
   r.mcount = uni(w0.w);
   r.fmt = (uint32_t)uni(w1.x);
   const int* wi = reinterpret_cast<const int*>(recs + g);

@@ -1,5 +1,5 @@
 // Decode-path FC1 (gate/up, SiLU*up fused) and FC2 (down, routing weight fused) on the
-// matrix cores, for token groups of MT <= 4 tokens of one expert.
+// matrix cores, for token groups of up to MF_MT = 16 tokens of one expert.
 //
 // Sources: the routed experts are 2-bit vector codes with a sign-symmetric codebook,
 // decoded on the fly (Tandem-vLLM 0.2.0 announcement, "How it works"; vLLM-Moet README,
@@ -8,26 +8,31 @@
 // vLLM", row "MoE at decode"); silu*up fused into the expert product (vLLM-Moet README,
 // "Qwen3.8-Flash-Next-FP8 on 4x RTX PRO 6000").
 //
-// The product of a group of at most 4 tokens with one expert matrix is a GEMV-like
-// problem bound by the code stream.  It runs on v_mfma_f32_16x16x32_f16 anyway,
-// because there the contraction over k happens inside the matrix core.  That removes
-// the per-row cross-lane sums, and only the lanes that carry a real token read
-// activations from LDS.  The 12 or 15 padding token rows cost matrix-core cycles only,
-// and those are idle in this kernel.
+// The product of a group of at most 16 tokens with one expert matrix is a GEMV-like
+// problem bound by the code stream.  It runs on v_mfma_f32_16x16x32_f16: the 16 rows of
+// the A operand are the group's tokens, so each expert is read once per 16 tokens (the
+// Zipf-skewed batches give some experts many tokens), and the contraction over k
+// happens inside the matrix core, with no per-row cross-lane sums.
 //
-// B operand: a lane's 8 code bytes of one 128-wide scale group are 8 table lookups of
-// signed codebook vectors, which are exact fp16 values.  The group scale multiplies the
-// group's partial product afterwards in fp32, so no weight is rounded.  The contraction
-// index is permuted identically in A and B: within a group, lanes 16q..16q+15 hold
-// k = 32q + 8s + (0..7) at MFMA step s.
+// A operand: held in registers for the whole token group, never in LDS, so that the
+// only LDS traffic of the inner loop is the codebook lookups.  FC1 takes the staged
+// fp16 x (one power-of-two factor per token and 1024 columns, exact for bf16 x); FC2
+// converts the fp32 h of each pair to fp16 with one power-of-two factor per 128-column
+// scale group.  The factor multiplies the group's product in fp32.
 //
-// A operand: the staged activations, fp16 with one power-of-two factor per (token, 1024
-// columns) (exact for bf16 x); the factor also multiplies the group's product.
+// B operand: a lane's code bytes of one 128-wide scale group are table lookups of signed
+// codebook vectors, which are exact fp16 values.  The group scale multiplies the group's
+// partial product afterwards in fp32, so no weight is rounded.  Codes arrive as 16-byte
+// loads that cover two scale groups (16 rows x 64 bytes per instruction); one
+// v_permlane32_swap per dword pair regroups them so that every lane holds 8 code bytes
+// of each group.  The contraction index is permuted identically in A and B: within a
+// group, lanes 16q..16q+15 hold k = 32 p(q) + 8s + (0..7) at MFMA step s, with
+// p = (0, 2, 1, 3).
 //
-// Work: a tile is (token group, 16 * NB rows); the eight waves of a workgroup take the
-// eight parts of K, and their partial sums meet in LDS at the end of the tile.  Each
-// wave keeps its whole part of the next tile's codes in flight: the register ring
-// slot of a (group, matrix, row block) is reloaded with the next tile's codes right
+// Work: a tile is (token group, 16 * NB rows); the W waves of a workgroup take the W
+// parts of K, and their partial sums meet in LDS at the end of the tile.  Each
+// wave keeps its whole part of the next tile's codes in flight: the register ring slot
+// of a (group pair, matrix, row block) is reloaded with the next tile's codes right
 // after this tile has consumed it.
 #include <type_traits>
 
@@ -38,33 +43,55 @@ namespace mvq {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int MF_WAVES = 8;                 // waves per workgroup; each takes 1/8 of K
-constexpr int MF_THREADS = 64 * MF_WAVES;
+// Waves per workgroup; each takes 1/W of K and holds its part of the A fragments in
+// registers.  K = 2048 and 1024: one wave per SIMD (W = 4), with the 512 registers a
+// wave has when it is alone on its SIMD.  K = 7168 (FC1): W = 8, two waves per SIMD
+// with 256 registers each, of which the A fragments of 7 groups take 112.
+template <int CPL, bool FC1>
+constexpr int mf_waves() { return CPL == 7 ? 8 : 4; }
 
 template <int CPL, bool FC1>
 struct MfGeom {
+  static constexpr int W = mf_waves<CPL, FC1>();
+  static constexpr int THREADS = 64 * W;
   static constexpr int K = 1024 * CPL;
   static constexpr int NM = FC1 ? 2 : 1;
-  static constexpr int NGQ = CPL;      // 128-wide scale groups in a wave's eighth of K
-  // 16-row blocks per tile: enough (group, matrix, block) ring slots per wave to keep
-  // 14-16 loads of 512 bytes in flight
-  static constexpr int NB = CPL >= 4 ? (FC1 ? 1 : 2) : (FC1 ? 8 / CPL : 16 / CPL);
+  static constexpr int NGQ = 8 * CPL / W;  // 128-wide scale groups in a wave's part of K
+  static constexpr int NPAIR = NGQ / 2;  // groups read two at a time (16-byte loads)
+  static constexpr bool ODD = (NGQ & 1) != 0;  // the last group is read alone (8 bytes)
+  // 16-row blocks per tile: enough ring slots per wave to keep about 7 KB of codes in
+  // flight, and at most 8 (matrix, block) pairs so the partial sums fit in LDS
+  static constexpr int NB_RULE = CPL >= 4 ? (FC1 ? 1 : 2) : (FC1 ? 8 / CPL : 16 / CPL);
+  static constexpr int NB = NB_RULE < 8 / NM ? NB_RULE : 8 / NM;
   static constexpr int ROWS = 16 * NB;
-  static constexpr int KS = CPL;       // activation slices of 1024 columns
-  // MXFP4 tiles load MXG groups per pass: the largest divisor of NGQ whose codes fit in
-  // about 80 registers next to the (live) VQ2 ring
+  static constexpr int KS = CPL;       // activation slices of 1024 columns (FC1 factors)
+  static constexpr int NSLW = (NGQ + 6) / 8 + 1;  // slices a wave's groups can touch
+  static constexpr int QS = ROWS + 1;  // LDS stride of one token's partial sums
+  static constexpr int RED = W * NM * MF_MT * QS;  // floats per reduction buffer
+  static constexpr int NBUF = (size_t)TAB_BYTES + 2 * (size_t)RED * 4 <= (size_t)150 * 1024 ? 2 : 1;
+  // MXFP4 tiles load up to MXG groups per pass: as many as fit in about 80 registers
+  // (30 with two waves per SIMD, where the A fragments take 112 of 256)
   static constexpr int mxg() {
+    const int budget = W == 4 ? 80 : 30;
     int best = 1;
     for (int d = 1; d <= NGQ; ++d)
-      if (NGQ % d == 0 && d * NM * NB * 5 <= 80) best = d;
+      if (d * NM * NB * 5 <= budget) best = d;
     return best;
   }
   static constexpr int MXG = mxg();
+  static constexpr int MXP = (NGQ + MXG - 1) / MXG;  // passes
 };
 
-// VQ2 codes one lane holds for one (group, matrix, row block): 8 code bytes and the
-// group's fp16 scale bits.
-struct MfCode {
+// VQ2 codes one lane holds for one (group pair, matrix, row block): 16 code bytes (8 of
+// each group once swapped) and the two groups' fp16 scale bits.  Pairs start at an even
+// group, so the two scales are one aligned dword.
+struct MfPair {
+  uint4 q;
+  uint32_t s;  // scale bits: low half the first group, high half the second
+};
+
+// The same for a group read alone.
+struct MfOne {
   uint2 q;
   uint32_t s;
 };
@@ -75,110 +102,139 @@ struct MfMx {
   uint32_t e;
 };
 
-size_t mf_lds_bytes(int MT, int K, bool fc1) {
-  const int cpl = K / 1024;
-  const int nm = fc1 ? 2 : 1;
-  const int nb = cpl >= 4 ? (fc1 ? 1 : 2) : (fc1 ? 8 / cpl : 16 / cpl);
-  const size_t b = (size_t)TAB_BYTES + (size_t)MT * K * 2 + (size_t)MT * cpl * 4 +
-                   (size_t)2 * MF_WAVES * nm * nb * 16 * MT * 4 + (size_t)MF_WAVES * MT * cpl * 4;
-  return (b + 511) & ~(size_t)511;
-}
-
-template <int CPL, int MT, bool FC1>
-__global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
+template <int CPL, bool FC1>
+__global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel(FcArgs a) {
   using G = MfGeom<CPL, FC1>;
+  constexpr int MF_WAVES = G::W, MF_THREADS = G::THREADS;
   constexpr int K = G::K, NM = G::NM, NB = G::NB, ROWS = G::ROWS, NGQ = G::NGQ, KS = G::KS;
+  constexpr int NPAIR = G::NPAIR, QS = G::QS, RED = G::RED, NBUF = G::NBUF, NSLW = G::NSLW;
+  constexpr bool ODD = G::ODD;
   __shared__ uint2 tab[256 * TAB_COPIES];
-  __shared__ __align__(16) _Float16 xs[MT * K];
-  __shared__ float xsc[MT * KS];
-  __shared__ float red[2][MF_WAVES][NM][NB][16][MT];
-  __shared__ float smax[MF_WAVES][MT * KS];
+  __shared__ float red[NBUF * RED];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, kq = lane >> 4;
+  const int pq = ((kq & 1) << 1) | (kq >> 1);  // k-part of the group held by this lane
   const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
   const int NROWS = FC1 ? a.I : a.H;
   const int RB = (NROWS + ROWS - 1) / ROWS;
-  const int g0 = uni(wave) * NGQ;  // first scale group of this wave's eighth of K
+  const int g0 = uni(wave) * NGQ;  // first scale group of this wave's part of K
+  const int sl0 = g0 >> 3;         // its first 1024-column slice (FC1 factors)
+  // Register slot gi of the wave's groups: slots 0 .. 2*NPAIR-1 are the pairs, starting
+  // at the first even group; slot NGQ-1 (odd NGQ) is the group read alone, the first
+  // group when g0 is odd, else the last.
+  const int gpair = g0 + (g0 & 1);
+  const int gone = (g0 & 1) ? g0 : g0 + NGQ - 1;
+  auto gid = [&](int gi) __attribute__((always_inline)) -> int { return (ODD && gi == NGQ - 1) ? gone : gpair + gi; };
 
   const uint2 cbv = reinterpret_cast<const uint2*>(a.codebook)[tid & 127];
-  if (!ws_ok(a, FC1, MT)) return;
+  if (!ws_ok(a, FC1, MF_MT)) return;
   const int n_tiles = (int)a.hdr[FC1 ? HDR_GROUPS1 : HDR_GROUPS2] * RB;
   const int t_begin = (int)(((long)blockIdx.x * n_tiles) / gridDim.x);
   const int t_end = (int)(((long)(blockIdx.x + 1) * n_tiles) / gridDim.x);
   if (t_begin >= t_end) return;
 
-  // Stage the activations of record r (FC1: fp16 x of its tokens; FC2: h of its pairs,
-  // scaled to fp16 with one power-of-two factor per 1024-column slice).
-  auto stage = [&](const RecS& r) __attribute__((always_inline)) {
-    const int t0 = opaque(threadIdx.x);
-    const int w0 = t0 >> 6, l0 = t0 & 63;
+  // ---- activations of the current token group, in registers
+  half8_t A[NGQ][4];                            // A fragments, group gi, step s
+  float fx1[FC1 ? NSLW : 1][4];                 // FC1: factor of D row r, slice sl0 + j
+  float fx2[FC1 ? 1 : NGQ][4];                  // FC2: factor of D row r, group gi
+  float4 A32[FC1 ? 1 : NGQ][8];                 // FC2: the next group's h, as loaded
+
+  // Per-lane token (FC1) or pair (FC2) of A row i16 and of the lane's four D rows
+  // (4 kq + r) for group record r; padding rows repeat the last real one.
+  struct Tok {
+    int arow;
+    int drow[4];
+  };
+  auto tok_load = [&](const RecS& r) __attribute__((always_inline)) -> Tok {
+    Tok t;
+    const int last = r.mcount - 1;
+    t.arow = a.pair_list[r.p0 + min(i16, last)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t.drow[q] = FC1 ? a.pair_list[r.p0 + min(4 * kq + q, last)] : 0;
+    return t;
+  };
+  // Issue the loads of a token group's activations (FC1: fp16 x and its factors; FC2:
+  // fp32 h, converted by convert_h when the group's first tile starts).
+  auto act_load = [&](const Tok& t, const RecS& r) __attribute__((always_inline)) {
     if (FC1) {
-      constexpr int XU = (K / 8 + MF_THREADS - 1) / MF_THREADS;
-      uint4 xv[MT][XU];
-      float scv[MT];
+      const int tokA = t.arow / a.k;
+      const uint16_t* xr = a.x_h + (size_t)tokA * K + 32 * pq;
 #pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        const bool live = j < r.mcount;
-        const size_t tok = live ? (size_t)(r.pair[j] / a.k) : 0;
-        const uint4* src = reinterpret_cast<const uint4*>(a.x_h + tok * K);
+      for (int gi = 0; gi < NGQ; ++gi)
 #pragma unroll
-        for (int i = 0; i < XU; ++i) {
-          const int o = t0 + i * MF_THREADS;
-          xv[j][i] = (live && o < K / 8) ? src[o] : make_uint4(0u, 0u, 0u, 0u);
+        for (int s = 0; s < 4; ++s) A[gi][s] = *reinterpret_cast<const half8_t*>(xr + gid(gi) * 128 + 8 * s);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tokD = t.drow[q] / a.k;
+        const bool live = 4 * kq + q < r.mcount;
+#pragma unroll
+        for (int j = 0; j < (FC1 ? NSLW : 1); ++j) {
+          const float v = a.x_sc[(size_t)tokD * KS + min(sl0 + j, KS - 1)];
+          fx1[j][q] = live ? v : 0.f;
         }
-        scv[j] = (live && t0 < KS) ? a.x_sc[tok * KS + t0] : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < MT; ++j) {
-#pragma unroll
-        for (int i = 0; i < XU; ++i) {
-          const int o = t0 + i * MF_THREADS;
-          if (o < K / 8) reinterpret_cast<uint4*>(xs + j * K)[o] = xv[j][i];
-        }
-        if (t0 < KS) xsc[j * KS + t0] = scv[j];
       }
     } else {
-      // one slice of 1024 columns is 512 threads x 2 values
-      float2 hv[MT * KS];
+      const float* hr = a.h_in + (size_t)t.arow * K + 32 * pq;
 #pragma unroll
-      for (int j = 0; j < MT; ++j)
+      for (int gi = 0; gi < NGQ; ++gi)
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          hv[j * KS + s] = j < r.mcount
-                               ? reinterpret_cast<const float2*>(a.h_in + (size_t)r.pair[j] * K)[s * 512 + t0]
-                               : make_float2(0.f, 0.f);
+        for (int i = 0; i < 8; ++i) A32[FC1 ? 0 : gi][i] = *reinterpret_cast<const float4*>(hr + gid(gi) * 128 + 4 * i);
+    }
+  };
+  // FC2: fp32 h -> fp16 A fragments with one power-of-two factor per (pair, group); the
+  // factor of D row r (pair 4 kq + r) comes from the lanes holding that A row.
+  auto convert_h = [&](const RecS& r) __attribute__((always_inline)) {
+    if (!FC1) {
 #pragma unroll
-      for (int js = 0; js < MT * KS; ++js) {
-        const float2 v = hv[js];
-        float m = fmaxf(fabsf(v.x), fabsf(v.y));
-        m = wave_max(m);
-        if (l0 == 0) smax[w0][js] = m;
-      }
-      __syncthreads();
+      for (int gi = 0; gi < NGQ; ++gi) {
+        const int gk = FC1 ? 0 : gi;
+        float m = 0.f;
 #pragma unroll
-      for (int js = 0; js < MT * KS; ++js) {
-        float m = smax[0][js];
-#pragma unroll
-        for (int w = 1; w < MF_WAVES; ++w) m = fmaxf(m, smax[w][js]);
+        for (int i = 0; i < 8; ++i)
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(A32[gk][i].x), fabsf(A32[gk][i].y)),
+                             fmaxf(fabsf(A32[gk][i].z), fabsf(A32[gk][i].w))));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
         int ex = 0;
-        if (m > 0.f && m == m) ex = frexp_exponent(m) - 15;
-        const float2 v = hv[js];
-        const int j = js / KS, s = js % KS;
-        reinterpret_cast<uint32_t*>(xs + j * K + s * SLICE)[t0] = pack_half2(ldexp2(v.x, -ex), ldexp2(v.y, -ex));
-        if (t0 == 0) xsc[js] = j < r.mcount ? ldexp2(1.0f, ex) : 0.f;
+        if (m > 0.f && m < INFINITY) ex = frexp_exponent(m) - 15;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float4 u = A32[gk][2 * s], v = A32[gk][2 * s + 1];
+          A[gi][s] = half8_t{(_Float16)ldexp2(u.x, -ex), (_Float16)ldexp2(u.y, -ex), (_Float16)ldexp2(u.z, -ex),
+                             (_Float16)ldexp2(u.w, -ex), (_Float16)ldexp2(v.x, -ex), (_Float16)ldexp2(v.y, -ex),
+                             (_Float16)ldexp2(v.z, -ex), (_Float16)ldexp2(v.w, -ex)};
+        }
+        const float f = ldexp2(1.0f, ex);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v = __shfl(f, 4 * kq + q);
+          fx2[gk][q] = 4 * kq + q < r.mcount ? v : 0.f;
+        }
       }
     }
   };
+  // factor of D row q for group gi of the wave's part
+  auto factor = [&](int gi, int q) __attribute__((always_inline)) -> float {
+    if (FC1) {
+      const int j = (gid(gi) >> 3) - sl0;  // uniform; picks among the wave's slices
+      float f = fx1[0][q];
+#pragma unroll
+      for (int i = 1; i < (FC1 ? NSLW : 1); ++i) f = j == i ? fx1[i][q] : f;
+      return f;
+    }
+    return fx2[FC1 ? 0 : gi][q];
+  };
 
-  // Addresses of one tile's VQ2 codes: uniform matrix bases, one 32-bit offset per lane
-  // and row block (row, first group of the wave's part of K, lane's 8 bytes); the group
-  // offset gi*32 (gi*2 for the scales) is the load instruction's immediate.
+  // Addresses of one tile's VQ2 codes: uniform matrix bases, 32-bit per-lane offsets per
+  // row block; the pair offset pi*64 (scales: group offset * 2) is an immediate.
   struct MfAddr {
     const uint8_t* qb[NM];
     const uint8_t* sb[NM];
     uint32_t qo[NB], so[NB];
   };
+  const uint32_t lane_pair = (uint32_t)(gpair * 32 + kq * 16);  // 16 bytes of a group pair
+  const uint32_t lane_one = (uint32_t)(gone * 32 + pq * 8);      // 8 bytes of the lone group
   auto vq_addr = [&](const RecS& r, int rb) __attribute__((always_inline)) -> MfAddr {
     MfAddr d;
     const uint8_t* slot = a.pool + r.slot_off;
@@ -189,36 +245,22 @@ __global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
     for (int nb = 0; nb < NB; ++nb) {
       // rows past the end (ragged shapes only) re-read the last row; the epilogue drops them
       const uint32_t n = (uint32_t)min(rb * ROWS + nb * 16 + i16, NROWS - 1);
-      d.qo[nb] = n * (uint32_t)(K / 4) + (uint32_t)(g0 * 32 + kq * 8);
-      d.so[nb] = (n * (uint32_t)(K / 128) + (uint32_t)g0) * 2u;
+      d.qo[nb] = n * (uint32_t)(K / 4);
+      d.so[nb] = n * (uint32_t)(K / 128) * 2u;
     }
     return d;
   };
-  auto vq_load = [&](const MfAddr& d, int gi, int m, int nb) __attribute__((always_inline)) -> MfCode {
-    MfCode c;
-    c.q = *reinterpret_cast<const uint2*>(d.qb[m] + d.qo[nb] + gi * 32);
-    c.s = *reinterpret_cast<const uint16_t*>(d.sb[m] + d.so[nb] + gi * 2);
+  auto load_pair = [&](const MfAddr& d, int pi, int m, int nb) __attribute__((always_inline)) -> MfPair {
+    MfPair c;
+    c.q = *reinterpret_cast<const uint4*>(d.qb[m] + d.qo[nb] + lane_pair + pi * 64);
+    c.s = *reinterpret_cast<const uint32_t*>(d.sb[m] + d.so[nb] + gpair * 2 + pi * 4);
     return c;
   };
-
-  // A fragments of group g.  Rows of the product are independent, so the lanes of the
-  // padding token rows (i16 >= MT) read a real row too: their results are never used
-  // (their factors are 0 and the epilogue writes rows < MT only), and the reads need no
-  // branch.
-  const _Float16* xrow = xs + (i16 % MT) * K + 32 * kq;
-  auto a_frags = [&](int g, half8_t (&af)[4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) af[s] = *reinterpret_cast<const half8_t*>(xrow + g * 128 + 8 * s);
-  };
-  // per-lane factor of D row r (token 4*kq + r) for activation slice sl; 0 for the
-  // padding rows
-  const bool real_rows = kq == 0;
-  auto x_factors = [&](int sl, float (&fx)[4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = xsc[(r < MT ? r : MT - 1) * KS + sl];
-      fx[r] = (real_rows && r < MT) ? v : 0.f;
-    }
+  auto load_one = [&](const MfAddr& d, int m, int nb) __attribute__((always_inline)) -> MfOne {
+    MfOne c;
+    c.q = *reinterpret_cast<const uint2*>(d.qb[m] + d.qo[nb] + lane_one);
+    c.s = *reinterpret_cast<const uint16_t*>(d.sb[m] + d.so[nb] + gone * 2);
+    return c;
   };
 
   f32x4_t acc[NM][NB];
@@ -229,53 +271,110 @@ __global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
       for (int nb = 0; nb < NB; ++nb) acc[m][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
 
-  // VQ2 tile: consume the ring, refilling each slot with the next tile's codes
-  MfCode ring[NGQ][NM][NB];
-  auto compute_vq = [&](bool refill, const RecS& rn, int rbn) __attribute__((always_inline)) {
-    const MfAddr dn = vq_addr(rn, rbn);
+  // 8 code bytes of one group (this lane's k-part) -> its 4 B fragments
+  auto b_frags = [&](uint32_t w0, uint32_t w1, half8_t (&bfr)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int gi = 0; gi < NGQ; ++gi) {
-      const int g = g0 + gi;
-      half8_t af[4];
-      a_frags(g, af);
-      float fx[4];
-      x_factors(g >> 3, fx);
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t wd = s < 2 ? w0 : w1;
+      const uint2 e0 = tab_lookup(tab, tab_addr_sel(wd, laneoff, (2 * s) & 3));
+      const uint2 e1 = tab_lookup(tab, tab_addr_sel(wd, laneoff, (2 * s + 1) & 3));
+      bfr[s] = __builtin_bit_cast(half8_t, make_uint4(e0.x, e0.y, e1.x, e1.y));
+    }
+  };
+  auto group_mma = [&](int gi, const half8_t (&bfr)[4], float sc, f32x4_t& ac) __attribute__((always_inline)) {
+    f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+    for (int s = 0; s < 4; ++s) tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[gi][s], bfr[s], tmp, 0, 0, 0);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          // the slot is consumed (lookups, scale) before its refill is issued, so the
-          // refill can land in the same registers: no copies of in-flight loads at
-          // the loop edge (a copy would wait for the load)
-          const MfCode c = ring[gi][m][nb];
-          half8_t bfr[4];
+    for (int q = 0; q < 4; ++q) ac[q] = fmaf(sc * factor(gi, q), tmp[q], ac[q]);
+  };
+
+  // VQ2 tile: consume the ring, refilling each slot with the next tile's codes.  Slot j
+  // is (pair, matrix, row block) for j < NPS, then (matrix, row block) of the lone
+  // group; unit u is one scale group of a slot (two per pair slot).  Software pipeline:
+  // the lookups of unit u + 1 are issued before the matrix ops of unit u, so the LDS
+  // latency hides behind them.  The refill is issued for every slot; without a next
+  // VQ2 tile it re-reads this tile's codes (cache hits), which keeps the loop free of
+  // branches.
+  MfPair ringP[NPAIR > 0 ? NPAIR : 1][NM][NB];
+  MfOne ringS[ODD ? NM : 1][ODD ? NB : 1];
+  constexpr int NPS = NPAIR * NM * NB;                // pair slots
+  constexpr int NU = 2 * NPS + (ODD ? NM * NB : 0);   // units
+  struct UDec {
+    half8_t b[4];
+    float sc;
+  };
+  uint32_t pw2, pw3, ps;  // second group of the pair slot being consumed (words, scale bits)
+  auto decode = [&](int u, const MfAddr& dn) __attribute__((always_inline)) -> UDec {
+    UDec d;
+    if (u < 2 * NPS) {
+      const int j = u >> 1;
+      const int pi = j / (NM * NB), m = (j / NB) % NM, nb = j % NB;
+      if ((u & 1) == 0) {
+        // the slot is consumed (swap, scales) before its refill is issued, so the refill
+        // can land in the same registers
+        const MfPair c = ringP[pi][m][nb];
+        const auto lo = __builtin_amdgcn_permlane32_swap(c.q.x, c.q.z, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(c.q.y, c.q.w, false, false);
+        pw2 = lo[1];
+        pw3 = hi[1];
+        ps = c.s >> 16;
+        d.sc = f16_bits_to_f32(c.s & 0xFFFFu);
+        ringP[pi][m][nb] = load_pair(dn, pi, m, nb);
+        b_frags(lo[0], hi[0], d.b);
+      } else {
+        d.sc = f16_bits_to_f32(ps);
+        b_frags(pw2, pw3, d.b);
+      }
+    } else {
+      const int m = ((u - 2 * NPS) / NB) % NM, nb = (u - 2 * NPS) % NB;
+      const MfOne c = ringS[ODD ? m : 0][ODD ? nb : 0];
+      d.sc = f16_bits_to_f32(c.s);
+      ringS[ODD ? m : 0][ODD ? nb : 0] = load_one(dn, m, nb);
+      b_frags(c.q.x, c.q.y, d.b);
+    }
+    return d;
+  };
+  auto unit_mma = [&](int u, const UDec& d) __attribute__((always_inline)) {
+    if (u < 2 * NPS) {
+      const int j = u >> 1;
+      const int pi = j / (NM * NB), m = (j / NB) % NM, nb = j % NB;
+      group_mma(2 * pi + (u & 1), d.b, d.sc, acc[m][nb]);
+    } else {
+      const int m = ((u - 2 * NPS) / NB) % NM, nb = (u - 2 * NPS) % NB;
+      group_mma(NGQ - 1, d.b, d.sc, acc[m][nb]);
+    }
+  };
+  auto compute_vq = [&](bool refill, const RecS& rn, int rbn, const RecS& rcur, int rbc)
+                        __attribute__((always_inline)) {
+    const MfAddr dn = refill ? vq_addr(rn, rbn) : vq_addr(rcur, rbc);
+    if (MF_WAVES > 4) {
+      // two waves per SIMD interleave by themselves: no registers for a pipeline
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const uint32_t wd = s < 2 ? c.q.x : c.q.y;
-            const uint2 e0 = tab_lookup(tab, tab_addr_sel(wd, laneoff, (2 * s) & 3));
-            const uint2 e1 = tab_lookup(tab, tab_addr_sel(wd, laneoff, (2 * s + 1) & 3));
-            bfr[s] = __builtin_bit_cast(half8_t, make_uint4(e0.x, e0.y, e1.x, e1.y));
-          }
-          const float sc = f16_bits_to_f32(c.s);
-          if (refill) ring[gi][m][nb] = vq_load(dn, gi, m, nb);
-          f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < NU; ++u) unit_mma(u, decode(u, dn));
+    } else {
+      UDec cur = decode(0, dn);
 #pragma unroll
-          for (int s = 0; s < 4; ++s) tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], bfr[s], tmp, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[m][nb][r] = fmaf(sc * fx[r], tmp[r], acc[m][nb][r]);
-        }
+      for (int u = 0; u < NU; ++u) {
+        UDec nxt;
+        if (u + 1 < NU) nxt = decode(u + 1, dn);
+        unit_mma(u, cur);
+        if (u + 1 < NU) cur = nxt;
+      }
     }
   };
 
-  // MXFP4 tile (not pipelined): MXG groups of the wave's part of K per pass
+  // MXFP4 tile (not pipelined): up to MXG groups of the wave's part of K per pass; each
+  // lane reads the 32 weights of its k-part p(q) of the group
   auto compute_mx = [&](const RecS& r, int rb) __attribute__((always_inline)) {
     const uint8_t* slot = a.pool + r.slot_off;
 #pragma unroll
-    for (int h = 0; h < NGQ / G::MXG; ++h) {
+    for (int h = 0; h < G::MXP; ++h) {
       constexpr int NH = G::MXG;
       MfMx mx[NH][NM][NB];
 #pragma unroll
       for (int j = 0; j < NH; ++j)
+        if (h * NH + j < NGQ)
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -283,23 +382,20 @@ __global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
             const uint8_t* qb = slot + (m == 0 ? (FC1 ? a.mx4.q_gate : a.mx4.q_down) : a.mx4.q_up);
             const uint8_t* sb = slot + (m == 0 ? (FC1 ? a.mx4.s_gate : a.mx4.s_down) : a.mx4.s_up);
             const uint32_t n = (uint32_t)min(rb * ROWS + nb * 16 + i16, NROWS - 1);
-            const int g = g0 + h * NH + j;
-            mx[j][m][nb].q = *reinterpret_cast<const uint4*>(qb + n * (uint32_t)(K / 2) + (uint32_t)(g * 64 + kq * 16));
-            mx[j][m][nb].e = sb[n * (uint32_t)(K / 32) + (uint32_t)(g * 4 + kq)];
+            const int g = gid(h * NH + j);
+            mx[j][m][nb].q = *reinterpret_cast<const uint4*>(qb + n * (uint32_t)(K / 2) + (uint32_t)(g * 64 + pq * 16));
+            mx[j][m][nb].e = sb[n * (uint32_t)(K / 32) + (uint32_t)(g * 4 + pq)];
           }
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
-        const int g = g0 + h * NH + j;
-        half8_t af[4];
-        a_frags(g, af);
-        float fx[4];
-        x_factors(g >> 3, fx);
+        const int gi = h * NH + j;
+        if (gi >= NGQ) break;
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const float es = e8m0_to_f32(mx[j][m][nb].e);
-            f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
+            half8_t bfr[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
               const uint32_t wd = s == 0 ? mx[j][m][nb].q.x : s == 1 ? mx[j][m][nb].q.y
@@ -308,102 +404,123 @@ __global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
               const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 1);
               const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 2);
               const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 3);
-              const half8_t b = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-              tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], b, tmp, 0, 0, 0);
+              bfr[s] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[m][nb][q] = fmaf(fx[q], tmp[q], acc[m][nb][q]);
+            group_mma(gi, bfr, 1.0f, acc[m][nb]);
           }
       }
     }
   };
 
-  // End of a tile: the eight waves' partial sums meet in LDS, then the outputs.
+  // End of a tile: the waves' partial sums meet in LDS, then the outputs.  LDS
+  // layout [wave][matrix][token][row] with a padded token stride.
   auto finish = [&](const RecS& r, int rb, int buf) __attribute__((always_inline)) {
-    if (kq == 0) {
+    float* R = red + (NBUF > 1 ? buf * RED : 0);
+    if (NBUF == 1) __syncthreads();  // the previous tile's sums have been read
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int q = 0; q < MT; ++q) red[buf][wave][m][nb][i16][q] = acc[m][nb][q];
-    }
+        for (int q = 0; q < 4; ++q)
+          if (4 * kq + q < r.mcount) R[((wave * NM + m) * MF_MT + 4 * kq + q) * QS + nb * 16 + i16] = acc[m][nb][q];
     __syncthreads();
-    if (tid < NB * 16) {
-      const int nb = tid >> 4, i = tid & 15;
-      const int n = rb * ROWS + nb * 16 + i;
+    const int nout = ROWS * r.mcount;
+    for (int o = tid; o < nout; o += MF_THREADS) {
+      const int q = o / ROWS, ri = o % ROWS;
+      const int n = rb * ROWS + ri;
+      if (n < NROWS) {
+        float v[NM];
 #pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        if (q < r.mcount && n < NROWS) {
-          float v[NM];
+        for (int m = 0; m < NM; ++m) {
+          float sum = R[(m * MF_MT + q) * QS + ri];
 #pragma unroll
-          for (int m = 0; m < NM; ++m)
-          {
-            float sum = red[buf][0][m][nb][i][q];
-#pragma unroll
-            for (int w = 1; w < MF_WAVES; ++w) sum += red[buf][w][m][nb][i][q];
-            v[m] = sum;
-          }
-          const int p = r.pair[q];
-          if (FC1) a.out[(size_t)p * a.I + n] = silu_fast(v[0]) * v[NM - 1];
-          else a.out[(size_t)p * a.H + n] = a.pair_w[p] * v[0];
+          for (int w = 1; w < MF_WAVES; ++w) sum += R[((w * NM + m) * MF_MT + q) * QS + ri];
+          v[m] = sum;
         }
+        const int p = a.pair_list[r.p0 + q];
+        if (FC1) a.out[(size_t)p * a.I + n] = silu_fast(v[0]) * v[NM - 1];
+        else a.out[(size_t)p * a.H + n] = a.pair_w[p] * v[0];
       }
     }
   };
 
-  // Loads of a whole ring for tile (r, rb), in the order the refills use (group,
-  // matrix, row block); the scheduling barriers keep that order, so that the count of
-  // loads in flight after each slot is the same whichever way the loop is entered.
+  // Loads of a whole ring for tile (r, rb), in the order the refills use; the
+  // scheduling barriers keep that order, so that the count of loads in flight after
+  // each slot is the same whichever way the loop is entered.
   auto ring_load = [&](const RecS& r, int rb) __attribute__((always_inline)) {
     const MfAddr d = vq_addr(r, rb);
 #pragma unroll
-    for (int gi = 0; gi < NGQ; ++gi)
+    for (int pi = 0; pi < NPAIR; ++pi)
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          ring[gi][m][nb] = vq_load(d, gi, m, nb);
+          ringP[pi][m][nb] = load_pair(d, pi, m, nb);
           __builtin_amdgcn_sched_barrier(0);
         }
+    if (ODD) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          ringS[ODD ? m : 0][ODD ? nb : 0] = load_one(d, m, nb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  };
+
+  auto ring_clear = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int pi = 0; pi < (NPAIR > 0 ? NPAIR : 1); ++pi)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) ringP[pi][m][nb] = MfPair{make_uint4(0u, 0u, 0u, 0u), 0u};
+#pragma unroll
+    for (int m = 0; m < (ODD ? NM : 1); ++m)
+#pragma unroll
+      for (int nb = 0; nb < (ODD ? NB : 1); ++nb) ringS[m][nb] = MfOne{make_uint2(0u, 0u), 0u};
   };
 
   // ---- prologue.  Records are read one tile ahead of their use (rn is needed for the
-  // refill addresses while this tile decodes; reading it later would wait for loads
-  // issued after it).
+  // refill addresses while this tile decodes).
   int t = t_begin;
   RecS rc = load_rec(a.rec, t / RB);
   RecS rn = (t + 1 < t_end) ? load_rec(a.rec, (t + 1) / RB) : rc;
-  stage(rc);  // staging loads are issued before the code loads
+  act_load(tok_load(rc), rc);
   if (rc.fmt == MOE_VQ_FMT_VQ2) ring_load(rc, t % RB);
-  if (tid < 256) write_table_entry(tab, cbv, tid);
+  if (tid < 256) write_table_entry(tab, cbv, tid);  // (every block has >= 256 threads)
   __syncthreads();
 
+  bool fresh = true;  // the tile is the first of its token group (FC2 converts h)
   int buf = 0;
   for (;;) {
     const int tn = t + 1;
     const bool more = tn < t_end;
     const RecS rnn = (tn + 1 < t_end) ? load_rec(a.rec, (tn + 1) / RB) : rn;
     const bool next_vq = more && rn.fmt == MOE_VQ_FMT_VQ2;
+    const bool next_group = more && tn / RB != t / RB;
+    Tok tk{};
+    if (next_group) tk = tok_load(rn);
+    if (fresh) convert_h(rc);
     zero_acc();
     if (rc.fmt == MOE_VQ_FMT_VQ2) {
-      compute_vq(next_vq, rn, tn % RB);  // refills the ring with tile tn's codes
+      compute_vq(next_vq, rn, tn % RB, rc, t % RB);  // refills the ring with tile tn's codes
     } else {
       if (rc.fmt == MOE_VQ_FMT_MXFP4) compute_mx(rc, t % RB);
       // (an absent expert keeps zeros; the worklist has recorded MOE_VQ_ENOTRESIDENT)
       if (next_vq) ring_load(rn, tn % RB);
+      else ring_clear();  // the ring is then dead here, not kept alive across compute_mx
     }
+    if (next_group) act_load(tk, rn);  // this tile was the last use of the activations
     finish(rc, t % RB, buf);
     if (!more) break;
-    if (!same_inputs<MT, FC1>(rn, rc, a.k)) {
-      __syncthreads();  // every wave is done with the staged activations
-      stage(rn);
-      __syncthreads();
-    }
+    fresh = next_group;
     rc = rn;
     rn = rnn;
     t = tn;
-    buf ^= 1;
+    buf ^= NBUF - 1;
   }
 }
 
@@ -414,27 +531,25 @@ __global__ __launch_bounds__(MF_THREADS, 1) void fc_mfma_kernel(FcArgs a) {
 template <bool FC1>
 hipError_t launch_mfma(const FcArgs& a, int K, int MT, int max_groups, int n_cu, hipStream_t st, bool* done) {
   *done = false;
-  // token groups of 4; single tokens take the vector-ALU stream kernel
-  if (K % 1024 != 0 || MT != 4) return hipSuccess;
+  if (MT != MF_MT || !mf_supported(K, FC1)) return hipSuccess;
   const int cpl = K / 1024;
   const int nrows = FC1 ? a.I : a.H;
-  const size_t lds = mf_lds_bytes(MT, K, FC1);
-  if (lds > (size_t)LDS_LIMIT) return hipSuccess;
-  const int per_cu = 1;  // 8 waves of up to 256 registers fill a CU
-#define MVQ_MFMA_CASE(C, M)                                                                  \
-  if (cpl == C && MT == M) {                                                                 \
+  const int per_cu = 1;  // a workgroup fills the CU's registers
+#define MVQ_MFMA_CASE(C)                                                                     \
+  if (cpl == C) {                                                                            \
     constexpr int ROWS = MfGeom<C, FC1>::ROWS;                                               \
     const long tiles = (long)max_groups * ((nrows + ROWS - 1) / ROWS);                      \
     long grid = (long)n_cu * per_cu;                                                         \
     if (tiles < grid) grid = tiles;                                                          \
     *done = true;                                                                            \
     if (grid <= 0) return hipSuccess;                                                        \
-    fc_mfma_kernel<C, M, FC1><<<(unsigned)grid, MF_THREADS, 0, st>>>(a);                     \
+    fc_mfma_kernel<C, FC1><<<(unsigned)grid, MfGeom<C, FC1>::THREADS, 0, st>>>(a);           \
     return hipGetLastError();                                                                \
   }
-  MVQ_MFMA_CASE(1, 4) MVQ_MFMA_CASE(2, 4) MVQ_MFMA_CASE(7, 4)
+  MVQ_MFMA_CASE(1) MVQ_MFMA_CASE(2)
+  if constexpr (FC1) { MVQ_MFMA_CASE(7) }
 #undef MVQ_MFMA_CASE
-  return hipSuccess;
+  return hipErrorInvalidValue;
 }
 
 template hipError_t launch_mfma<true>(const FcArgs&, int, int, int, int, hipStream_t, bool*);

@@ -84,7 +84,14 @@ __host__ __device__ inline SlotLayout slot_layout(int fmt, int H, int I) {
 
 __host__ __device__ inline int n_slices(int n) { return (n + SLICE - 1) / SLICE; }
 
-constexpr int MAX_MT = 4;  // largest token group of the decode-path FC kernels
+constexpr int MAX_MT = 4;  // largest token group of the vector-ALU FC kernels
+constexpr int MF_MT = 16;  // token group of the matrix-core FC kernel (its A operand rows)
+
+// K of the matrix-core FC kernel it is built for (FC2 holds its fp32 activations for a
+// whole quarter of K in registers, which caps K at 2048 there).
+__host__ __device__ inline bool mf_supported(int K, bool fc1) {
+  return K == 1024 || K == 2048 || (fc1 && K == 7168);
+}
 
 // One token group of one expert, as the FC kernels consume it: a tile is (group, block
 // of rows), so a tile reads one record to know where its codes and tokens are.
@@ -94,7 +101,7 @@ struct __align__(16) GroupRec {
   int32_t mcount;         // tokens in the group (1..MT)
   uint32_t fmt;           // slot format (MOE_VQ_FMT_ABSENT when not resident)
   int32_t expert;
-  int32_t pair[MAX_MT];   // the group's pair indices p = t*k + i (repeats the last when short)
+  int32_t pair[MAX_MT];   // its first pair indices p = t*k + i (repeats the last when short)
   int32_t pad[4];
 };
 
@@ -117,8 +124,11 @@ __host__ __device__ inline size_t fc_lds_bytes(int MT, int K) {
   return (b + 511) & ~(size_t)511;
 }
 
-// Tokens of one expert that share one pass over its codes.
-__host__ __device__ inline int fc_group_tokens(int n_tokens, int K) {
+// Tokens of one expert that share one pass over its codes: one token alone (the
+// vector-ALU stream kernel), else up to 16 on the matrix-core kernel where it is built
+// for K, else up to 4 on the vector-ALU kernels.
+__host__ __device__ inline int fc_group_tokens(int n_tokens, int K, bool fc1) {
+  if (n_tokens > 1 && mf_supported(K, fc1)) return MF_MT;
   int mt = n_tokens <= 1 ? 1 : 4;
   while (mt > 1 && fc_lds_bytes(mt, K) > (size_t)LDS_LIMIT) mt >>= 1;
   return mt;
@@ -168,8 +178,8 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int T) {
   L.act_fmt = take((size_t)E * 4);
   L.grp1 = take((size_t)(E + 1) * 4);
   L.grp2 = take((size_t)(E + 1) * 4);
-  L.MT1 = fc_group_tokens(T, H);
-  L.MT2 = fc_group_tokens(T, I);
+  L.MT1 = fc_group_tokens(T, H, true);
+  L.MT2 = fc_group_tokens(T, I, false);
   L.G1 = fc_max_groups(T, k, E, L.MT1);
   L.G2 = fc_max_groups(T, k, E, L.MT2);
   L.rec1 = take((size_t)L.G1 * sizeof(GroupRec));

@@ -256,6 +256,34 @@ def test_mini_fp32_activations(mini):
 
 
 # ---------------------------------------------------------------------------------
+# Full-width experts with few of them: every expert takes more than one 16-token group
+# ---------------------------------------------------------------------------------
+
+WIDE = synth.Config("wide", 40, 7168, 2048, 4, 2, "bf16", "normal", seed=4343)
+
+
+def test_wide_experts_split_into_token_groups():
+    syn = synth.SynthLayer(WIDE, cache=False)
+    dev = DeviceLayer.from_synth(syn)
+    for T in (40, 17):
+        x = syn.x(n=T, stream=60 + T)
+        say(f"wide step T={T}")
+        g = run(dev, x, "bf16")
+        assert g["status"] == _lib.OK
+        counts = np.bincount(g["ids"].ravel(), minlength=WIDE.n_experts)
+        if T == 40:
+            assert counts.max() > 16  # 80 pairs over 4 experts: some group is full and split
+        compare(syn, x, "bf16", g, WIDE.top_k)
+    # the same with two experts in MXFP4: the format changes between token groups
+    v, dev = tiny_variant(syn, formats=[synth.FMT_MXFP4, synth.FMT_VQ2, synth.FMT_MXFP4, synth.FMT_VQ2])
+    x = syn.x(n=40, stream=99)
+    say("wide step T=40, mixed formats")
+    g = run(dev, x, "bf16")
+    assert g["status"] == _lib.OK
+    compare(v, x, "bf16", g, WIDE.top_k)
+
+
+# ---------------------------------------------------------------------------------
 # Full-size layers (H=7168, I=2048, E=256, k=8), sampled tokens
 # ---------------------------------------------------------------------------------
 
