@@ -27,7 +27,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_vq.so")
-SOURCES = ["api.hip", "route.hip", "fc.hip", "fc_mfma.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "route.hip", "fc.hip", "fc_mfma.hip", "fc2_single.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

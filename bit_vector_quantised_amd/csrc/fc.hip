@@ -35,52 +35,6 @@ constexpr int LB_VQ = 14;   // 16-byte code loads in flight per lane (VQ2 tiles)
 constexpr int LB_MX = 14;   // same budget for MXFP4 tiles (twice the bytes per weight)
 
 // -------------------------------------------------------------------------------------
-// Shared pieces
-// -------------------------------------------------------------------------------------
-
-// Four VQ2 words (one dword of codes) against their 16 fp16 activations (8 dwords),
-// added to p in order.  A 16-byte chunk is four such steps.
-__device__ __forceinline__ float vq2_dword_dot(const uint2* tab, uint32_t wd, uint32_t laneoff,
-                                               const uint32_t* xw, float p) {
-  uint2 e0 = tab_lookup(tab, tab_addr<0>(wd, laneoff));
-  uint2 e1 = tab_lookup(tab, tab_addr<1>(wd, laneoff));
-  uint2 e2 = tab_lookup(tab, tab_addr<2>(wd, laneoff));
-  uint2 e3 = tab_lookup(tab, tab_addr<3>(wd, laneoff));
-  p = dot2(e0.x, xw[0], p); p = dot2(e0.y, xw[1], p);
-  p = dot2(e1.x, xw[2], p); p = dot2(e1.y, xw[3], p);
-  p = dot2(e2.x, xw[4], p); p = dot2(e2.y, xw[5], p);
-  p = dot2(e3.x, xw[6], p); p = dot2(e3.y, xw[7], p);
-  return p;
-}
-
-__device__ __forceinline__ uint32_t dword_of(const uint4& q, int i) {
-  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
-}
-
-// 16 VQ2 words of one 16-byte chunk against 64 fp16 activations (32 dwords).
-__device__ __forceinline__ float vq2_chunk_dot(const uint2* tab, const uint4& q, uint32_t laneoff,
-                                               const uint32_t* xw) {
-  float p = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p = vq2_dword_dot(tab, dword_of(q, i), laneoff, xw + 8 * i, p);
-  return p;
-}
-
-// 32 E2M1 elements of one 16-byte chunk against 32 fp16 activations (16 dwords).
-__device__ __forceinline__ float mx4_chunk_dot(const uint4& q, const uint32_t* xw) {
-  float p = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t wd = i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
-    p = dot2h(fp4x2_to_half2<0>(wd), xw[4 * i + 0], p);
-    p = dot2h(fp4x2_to_half2<1>(wd), xw[4 * i + 1], p);
-    p = dot2h(fp4x2_to_half2<2>(wd), xw[4 * i + 2], p);
-    p = dot2h(fp4x2_to_half2<3>(wd), xw[4 * i + 3], p);
-  }
-  return p;
-}
-
-// -------------------------------------------------------------------------------------
 // fc_stream_kernel: K = 1024 * CPL, LPR = 16, persistent and software-pipelined
 // -------------------------------------------------------------------------------------
 
@@ -718,7 +672,9 @@ hipError_t launch_fc1(const FcArgs& a, int MT, int max_groups, int n_cu, hipStre
 hipError_t launch_fc2(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st) {
   (void)hipGetLastError();  // start from a clean error state: report only our own launches
   bool done = false;
-  hipError_t e = launch_mfma<false>(a, a.I, MT, max_groups, n_cu, st, &done);
+  hipError_t e = launch_fc2_single(a, MT, st, &done);  // one token: writes y itself
+  if (e != hipSuccess || done) return e;
+  e = launch_mfma<false>(a, a.I, MT, max_groups, n_cu, st, &done);
   if (e == hipSuccess && !done) e = launch_stream<false>(a, a.I, MT, max_groups, n_cu, st, &done);
   if (e == hipSuccess && !done) e = launch_generic<false>(a, a.I, MT, max_groups, n_cu, st);
   if (e != hipSuccess) return e;

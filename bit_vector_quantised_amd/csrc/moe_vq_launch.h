@@ -9,10 +9,13 @@ hipError_t launch_route(const RouteArgs& ra, int x_dtype, const WorklistArgs& wa
 
 // FC1 / FC2 (+ combine) of the decode path; MT = token-group size, max_groups = the
 // worst-case number of token groups for this n_tokens, n_cu = compute units.
-// Matrix-core decode kernel for token groups of 1 or 4 and K a multiple of 1024 (up to
-// 7168); *done says whether it took the call.
+// Matrix-core decode kernel for token groups of 16 (K = 1024, 2048; FC1 also 7168);
+// *done says whether it took the call.
 template <bool FC1>
 hipError_t launch_mfma(const FcArgs& a, int K, int MT, int max_groups, int n_cu, hipStream_t st, bool* done);
+
+// FC2 and the combine at once for a one-token step (K = 1024 or 2048, k <= 8).
+hipError_t launch_fc2_single(const FcArgs& a, int MT, hipStream_t st, bool* done);
 
 hipError_t launch_fc1(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st);
 hipError_t launch_fc2(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st);
