@@ -44,11 +44,11 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Waves per workgroup; each takes 1/W of K and holds its part of the A fragments in
-// registers.  K = 2048 and 1024: one wave per SIMD (W = 4), with the 512 registers a
-// wave has when it is alone on its SIMD.  K = 7168 (FC1): W = 8, two waves per SIMD
-// with 256 registers each, of which the A fragments of 7 groups take 112.
+// registers.  W = 8: two waves per SIMD with 256 registers each (at K = 7168 the A
+// fragments of 7 groups take 112).  One wave per SIMD (W = 4, 512 registers) measured
+// slower: two waves per SIMD hide each other's LDS and load latency.
 template <int CPL, bool FC1>
-constexpr int mf_waves() { return CPL == 7 ? 8 : 4; }
+constexpr int mf_waves() { return 8; }
 
 template <int CPL, bool FC1>
 struct MfGeom {
@@ -59,10 +59,12 @@ struct MfGeom {
   static constexpr int NGQ = 8 * CPL / W;  // 128-wide scale groups in a wave's part of K
   static constexpr int NPAIR = NGQ / 2;  // groups read two at a time (16-byte loads)
   static constexpr bool ODD = (NGQ & 1) != 0;  // the last group is read alone (8 bytes)
-  // 16-row blocks per tile: enough ring slots per wave to keep about 7 KB of codes in
-  // flight, and at most 8 (matrix, block) pairs so the partial sums fit in LDS
+  // 16-row blocks per tile: ring slots per wave for several KB of codes in flight, at
+  // most 4 blocks with eight waves (registers), at most 8 (matrix, block) pairs so the
+  // partial sums fit in LDS
   static constexpr int NB_RULE = CPL >= 4 ? (FC1 ? 1 : 2) : (FC1 ? 8 / CPL : 16 / CPL);
-  static constexpr int NB = NB_RULE < 8 / NM ? NB_RULE : 8 / NM;
+  static constexpr int NB_CAP = W == 8 ? 4 : 8 / NM;
+  static constexpr int NB = NB_RULE < NB_CAP ? NB_RULE : NB_CAP;
   static constexpr int ROWS = 16 * NB;
   static constexpr int KS = CPL;       // activation slices of 1024 columns (FC1 factors)
   static constexpr int NSLW = (NGQ + 6) / 8 + 1;  // slices a wave's groups can touch
