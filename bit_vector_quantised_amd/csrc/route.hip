@@ -44,85 +44,114 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
   }
   const bool stage = (blockIdx.x == 0);
 
-  for (int t = t0; t < t1; ++t) {
-    float d[2] = {0.f, 0.f};
-    float xf[16];
-    if (col_ok) {
+  // Tokens in batches of TB: every x load of a batch is issued before any is used, so a
+  // batch waits for one memory latency, not one per token.
+  constexpr int TB = XF32 ? 4 : 8;
+  for (int tb = t0; tb < t1; tb += TB) {
+    uint4 xv[TB][XF32 ? 4 : 2];  // a lane's 16 columns: bf16 (2 units) or fp32 (4 units)
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int t = tb + u;
+#pragma unroll
+      for (int q = 0; q < (XF32 ? 4 : 2); ++q) xv[u][q] = make_uint4(0, 0, 0, 0);
+      if (col_ok && t < t1) {
+        const uint4* px = XF32 ? reinterpret_cast<const uint4*>(static_cast<const float*>(a.x) + (size_t)t * a.H + c0)
+                               : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * a.H + c0);
+#pragma unroll
+        for (int q = 0; q < (XF32 ? 4 : 2); ++q) xv[u][q] = px[q];
+      }
+    }
+    // a lane's 16 x values of token u as fp32
+    auto xval = [&](int u, float (&xf)[16]) __attribute__((always_inline)) {
       if (XF32) {
-        const float4* px = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)t * a.H + c0);
+        const float* f = reinterpret_cast<const float*>(&xv[u][0]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float4 v = px[q];
-          xf[4 * q + 0] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t* wj = reinterpret_cast<const uint32_t*>(&w[j][0]);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            d[j] = fmaf(bf16_bits_to_f32(wj[q] & 0xFFFFu), xf[2 * q], d[j]);
-            d[j] = fmaf(bf16_bits_to_f32(wj[q] >> 16), xf[2 * q + 1], d[j]);
-          }
-        }
+        for (int q = 0; q < 16; ++q) xf[q] = f[q];
       } else {
-        const uint4* px = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * a.H + c0);
-        uint4 xv[2] = {px[0], px[1]};
-        const uint32_t* xw = reinterpret_cast<const uint32_t*>(xv);
+        const uint32_t* xw = reinterpret_cast<const uint32_t*>(&xv[u][0]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           xf[2 * q] = bf16_bits_to_f32(xw[q] & 0xFFFFu);
           xf[2 * q + 1] = bf16_bits_to_f32(xw[q] >> 16);
         }
+      }
+    };
+    float d[TB][2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t* wj = reinterpret_cast<const uint32_t*>(&w[j][0]);
+    for (int u = 0; u < TB; ++u) {
+      d[u][0] = d[u][1] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t* wj = reinterpret_cast<const uint32_t*>(&w[j][0]);
+        if (XF32) {
+          float xf[16];
+          xval(u, xf);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            d[u][j] = fmaf(bf16_bits_to_f32(wj[q] & 0xFFFFu), xf[2 * q], d[u][j]);
+            d[u][j] = fmaf(bf16_bits_to_f32(wj[q] >> 16), xf[2 * q + 1], d[u][j]);
+          }
+        } else {
+          const uint32_t* xw = reinterpret_cast<const uint32_t*>(&xv[u][0]);
 #pragma unroll
           for (int q = 0; q < 8; ++q)
-            d[j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wj[q]),
-                                                   __builtin_bit_cast(bf16x2_t, xw[q]), d[j], false);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) xf[q] = 0.f;
-    }
-    const float s0 = wave_sum(d[0]);
-    const float s1 = wave_sum(d[1]);
-    if (lane == 0) {
-      float* dst = a.logits + (size_t)t * a.E * KSP;
-      if (e0 < a.E) dst[(size_t)e0 * KSP + s] = s0;
-      if (e0 + 1 < a.E) dst[(size_t)(e0 + 1) * KSP + s] = s1;
-      if (s == a.KS - 1) {  // zero the padding slices once
-        for (int z = a.KS; z < KSP; ++z) {
-          if (e0 < a.E) dst[(size_t)e0 * KSP + z] = 0.f;
-          if (e0 + 1 < a.E) dst[(size_t)(e0 + 1) * KSP + z] = 0.f;
+            d[u][j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wj[q]),
+                                                      __builtin_bit_cast(bf16x2_t, xw[q]), d[u][j], false);
         }
       }
     }
-    if (stage && wave == (t & 3)) {
-      float m = 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(xf[q]));
-      m = wave_max(m);
-      int ex = 0;
-      if (m > 0.f && m == m) {
-        int e2;
-        frexpf(m, &e2);  // m < 2^e2
-        ex = e2 - 15;    // |x| * 2^-ex < 2^15
-      }
-      if (col_ok) {
-        uint32_t packed[8];
+    for (int u = 0; u < TB; ++u) {
+      d[u][0] = wave_sum(d[u][0]);
+      d[u][1] = wave_sum(d[u][1]);
+    }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const _Float16 lo = (_Float16)ldexpf(xf[2 * q], -ex);
-          const _Float16 hi = (_Float16)ldexpf(xf[2 * q + 1], -ex);
-          packed[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    for (int u = 0; u < TB; ++u) {
+      const int t = tb + u;
+      if (lane == 0 && t < t1) {
+        float* dst = a.logits + (size_t)t * a.E * KSP;
+        if (e0 < a.E) dst[(size_t)e0 * KSP + s] = d[u][0];
+        if (e0 + 1 < a.E) dst[(size_t)(e0 + 1) * KSP + s] = d[u][1];
+        if (s == a.KS - 1) {  // zero the padding slices once
+          for (int z = a.KS; z < KSP; ++z) {
+            if (e0 < a.E) dst[(size_t)e0 * KSP + z] = 0.f;
+            if (e0 + 1 < a.E) dst[(size_t)(e0 + 1) * KSP + z] = 0.f;
+          }
         }
-        uint4* dst = reinterpret_cast<uint4*>(a.x_h + (size_t)t * a.H + c0);
-        dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
       }
-      if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = ldexpf(1.0f, ex);
+    }
+    if (stage) {
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int t = tb + u;
+        if (t < t1 && wave == (t & 3)) {
+          float xf[16];
+          xval(u, xf);
+          float m = 0.f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(xf[q]));
+          m = wave_max(m);
+          int ex = 0;
+          if (m > 0.f && m == m) {
+            int e2;
+            frexpf(m, &e2);  // m < 2^e2
+            ex = e2 - 15;    // |x| * 2^-ex < 2^15
+          }
+          if (col_ok) {
+            uint32_t packed[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const _Float16 lo = (_Float16)ldexpf(xf[2 * q], -ex);
+              const _Float16 hi = (_Float16)ldexpf(xf[2 * q + 1], -ex);
+              packed[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+            uint4* dst = reinterpret_cast<uint4*>(a.x_h + (size_t)t * a.H + c0);
+            dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+            dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+          }
+          if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = ldexpf(1.0f, ex);
+        }
+      }
     }
   }
 }
