@@ -213,7 +213,7 @@ int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n
   a.x16_e = at<int32_t>(ws, W.x16_e);
   a.mt_pre = at<int32_t>(ws, W.mt_pre);
   a.hmax = at<uint32_t>(ws, W.hmax);
-  a.h = at<float>(ws, W.h_pre);
+  a.h = at<uint16_t>(ws, W.h_pre);
   a.o_buf = at<float>(ws, W.o_buf);
   a.y = y;
   a.T = T; a.H = H; a.I = I; a.k = k; a.E = E;

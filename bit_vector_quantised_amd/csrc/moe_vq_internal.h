@@ -193,7 +193,7 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int T) {
   L.x16_e = take((size_t)T * 4);
   L.mt_pre = take((size_t)(E + 1) * 4);
   L.hmax = take(P * 4);
-  L.h_pre = take(P * I * 4);
+  L.h_pre = take(P * I * 2);
   L.total = off;
   return L;
 }
@@ -268,7 +268,7 @@ struct PrefillArgs {
   int32_t* x16_e;            // [T] x = x16 * 2^e
   int32_t* mt_pre;           // [E + 1] token-tile prefix over active experts
   uint32_t* hmax;            // [P] bits of max |h| per pair
-  float* h;                  // [P][I]
+  uint16_t* h;               // [P][I] bf16 (FC1 output, FC2 input)
   float* o_buf;              // [P][H]
   float* y;                  // [T][H]
   int T, H, I, k, E;

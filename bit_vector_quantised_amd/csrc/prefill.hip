@@ -209,72 +209,70 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
   for (int nb = 0; nb < NB; ++nb)  // rows past the end re-read the last row; the epilogue drops them
     rows[nb] = min(tl.nt * BN + wave * NB * 16 + nb * 16 + i16, NROWS - 1);
 
-  // staging: thread tid stages 32 consecutive k of token row tid/4
+  // staging: thread tid stages 32 consecutive k of token row tid/4 (FC1: fp16 x; FC2:
+  // the bf16 h that FC1 wrote, scaled by the pair's power-of-two factor into fp16)
   const int srow = tid >> 2, skq = (tid & 3) * 32;
   const int sp = s_pair[srow];  // -1 past the tile's tokens
-  constexpr int AV = FC1 ? 4 : 8;  // 16-byte loads per thread per group
+  constexpr int AV = 4;         // 16-byte loads per thread per group
   auto a_load = [&](int g, uint4 (&v)[AV]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) v[i] = make_uint4(0u, 0u, 0u, 0u);
     if (sp >= 0) {
-      if (FC1) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.x16 + (size_t)(sp / a.k) * K + g * PF_KG + skq);
+      const uint4* src = FC1 ? reinterpret_cast<const uint4*>(a.x16 + (size_t)(sp / a.k) * K + g * PF_KG + skq)
+                             : reinterpret_cast<const uint4*>(a.h + (size_t)sp * K + g * PF_KG + skq);
 #pragma unroll
-        for (int i = 0; i < AV; ++i) v[i] = src[i];
-      } else {
-        const uint4* src = reinterpret_cast<const uint4*>(a.h + (size_t)sp * K + g * PF_KG + skq);
-#pragma unroll
-        for (int i = 0; i < AV; ++i) v[i] = src[i];
-      }
+      for (int i = 0; i < AV; ++i) v[i] = src[i];
     }
   };
   auto a_store = [&](int buf, const uint4 (&v)[AV]) __attribute__((always_inline)) {
     uint4* dst = reinterpret_cast<uint4*>(&As[buf][srow * PF_AROW + skq]);
     if (FC1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = v[i];
+      for (int i = 0; i < AV; ++i) dst[i] = v[i];
     } else {
-      // fp32 h -> fp16 with the pair's power-of-two factor
+      // bf16 h -> fp16 with the pair's power-of-two factor
       const float f = s_fac[srow];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 u0 = __builtin_bit_cast(float4, v[2 * i]), u1 = __builtin_bit_cast(float4, v[2 * i + 1]);
-        const float w8[8] = {u0.x * f, u0.y * f, u0.z * f, u0.w * f, u1.x * f, u1.y * f, u1.z * f, u1.w * f};
-        uint4 o;
-        uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
+      for (int i = 0; i < AV; ++i) {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&v[i]);
+        uint32_t ow[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ow[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w8[2 * q]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w8[2 * q + 1]) << 16);
-        dst[i] = o;
+        for (int q = 0; q < 4; ++q) {
+          const float x0 = bf16_bits_to_f32(w[q] & 0xFFFFu) * f, x1 = bf16_bits_to_f32(w[q] >> 16) * f;
+          ow[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x0) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x1) << 16);
+        }
+        dst[i] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
       }
     }
   };
 
-  PfCodes cur[NM][NB], nxt[NM][NB];
+  // Codes and activations are loaded two groups ahead of their use: register set
+  // g % 3 holds group g.  The loop is unrolled by three so the sets rotate by name and
+  // no register holding an in-flight load is ever copied (a copy would wait for it).
+  PfCodes cs0[NM][NB], cs1[NM][NB], cs2[NM][NB];
+  uint4 as0[AV], as1[AV], as2[AV];
+  auto codes_load = [&](int g, PfCodes (&c)[NM][NB]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) cur[m][nb] = pf_load_codes<FMT>(qb[m], sb[m], rows[nb], K, 0, kq);
-  {
-    uint4 v[AV];
-    a_load(0, v);
-    a_store(0, v);
-  }
+      for (int nb = 0; nb < NB; ++nb) c[m][nb] = pf_load_codes<FMT>(qb[m], sb[m], rows[nb], K, g, kq);
+  };
+  codes_load(0, cs0);
+  if (NG > 1) codes_load(1, cs1);
+  a_load(0, as0);
+  if (NG > 1) a_load(1, as1);
+  a_store(0, as0);
   __syncthreads();
 
-  for (int g = 0; g < NG; ++g) {
-    const int buf = g & 1;
-    const bool more = g + 1 < NG;
-    uint4 av[AV];
-    if (more) {
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) nxt[m][nb] = pf_load_codes<FMT>(qb[m], sb[m], rows[nb], K, g + 1, kq);
-      a_load(g + 1, av);
+  // group g: issue group g + 2, multiply group g, stage group g + 1's activations
+  auto body = [&](int g, const PfCodes (&cur)[NM][NB], PfCodes (&c_ahead)[NM][NB], const uint4 (&a_next)[AV],
+                  uint4 (&a_ahead)[AV]) __attribute__((always_inline)) {
+    if (g + 2 < NG) {
+      codes_load(g + 2, c_ahead);
+      a_load(g + 2, a_ahead);
     }
-    const _Float16* Ab = As[buf];
+    const _Float16* Ab = As[g & 1];
     auto step = [&](auto S_) __attribute__((always_inline)) {
       constexpr int S = decltype(S_)::value;
       half8_t af[4];
@@ -295,14 +293,13 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
     step(std::integral_constant<int, 1>{});
     step(std::integral_constant<int, 2>{});
     step(std::integral_constant<int, 3>{});
-    if (more) {
-      a_store(buf ^ 1, av);
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) cur[m][nb] = nxt[m][nb];
-    }
+    if (g + 1 < NG) a_store((g + 1) & 1, a_next);
     __syncthreads();
+  };
+  for (int g = 0; g < NG; g += 3) {
+    body(g, cs0, cs2, as1, as2);
+    if (g + 1 < NG) body(g + 1, cs1, cs0, as2, as0);
+    if (g + 2 < NG) body(g + 2, cs2, cs1, as0, as1);
   }
 }
 
@@ -320,8 +317,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a
   const int NROWS = FC1 ? a.I : a.H;
   const int NT = (NROWS + BN - 1) / BN;
   const int n_act = (int)a.hdr[HDR_N_ACTIVE];
-  const int mt = blockIdx.x / NT;
-  if (mt >= a.mt_pre[n_act]) return;
+  // XCD-aware order: workgroups go to the 8 XCDs round-robin (block b to XCD b % 8),
+  // each with its own L2.  XCD x takes the x-th eighth of the logical tiles (token tile
+  // major, row tile minor, experts in order), so the row tiles that share one token
+  // tile's activations, and the token tiles that share one expert's codes, run together
+  // on one XCD and read those bytes into one L2 instead of eight.
+  const int n_valid = a.mt_pre[n_act] * NT;
+  const int per = (n_valid + 7) / 8;
+  const int jx = blockIdx.x >> 3;
+  if (jx >= per) return;
+  const int L = (blockIdx.x & 7) * per + jx;
+  if (L >= n_valid) return;
+  const int mt = L / NT;
   // active expert of this token tile: the last rank whose tile prefix is <= mt
   int lo = 0, hi = n_act - 1;
   while (lo < hi) {
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a
     if (a.mt_pre[mid] <= mt) lo = mid; else hi = mid - 1;
   }
   PfTile<FC1> tl;
-  tl.nt = blockIdx.x % NT;
+  tl.nt = L % NT;
   tl.p_lo = a.act_start[lo] + (mt - a.mt_pre[lo]) * PF_BM;
   tl.mcnt = min(PF_BM, a.act_start[lo + 1] - tl.p_lo);
   tl.fmt = a.act_fmt[lo];
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a
             const float gv = acc[0][nb][mb][r] * f, uv = acc[1][nb][mb][r] * f;
             const float h = silu_fast(gv) * uv;
             if (n < NROWS) {
-              a.h[(size_t)p * a.I + n] = h;
+              a.h[(size_t)p * a.I + n] = f32_to_bf16_rne(h);
               hm = fmaxf(hm, fabsf(h));
             }
           }
@@ -419,8 +426,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int x_dtype, hipStream_t st) {
   else prefill_stage_kernel<false><<<a.T, PF_THREADS, 0, st>>>(a);
   prefill_setup_kernel<<<1, 1024, 0, st>>>(a);
   const long mt_max = pf_max_mtiles(a.T, a.k, a.E);
-  const long g1 = mt_max * ((a.I + pf_rows_per_tile(true) - 1) / pf_rows_per_tile(true));
-  const long g2 = mt_max * ((a.H + pf_rows_per_tile(false) - 1) / pf_rows_per_tile(false));
+  // (rounded up to whole rounds of the 8 XCDs: the kernel maps block b to XCD b % 8)
+  const long g1 = (mt_max * ((a.I + pf_rows_per_tile(true) - 1) / pf_rows_per_tile(true)) + 7) & ~7L;
+  const long g2 = (mt_max * ((a.H + pf_rows_per_tile(false) - 1) / pf_rows_per_tile(false)) + 7) & ~7L;
   if (g1 > 0x7FFFFFFF || g2 > 0x7FFFFFFF) return hipErrorInvalidValue;
   prefill_fc_kernel<true><<<(unsigned)g1, PF_THREADS, 0, st>>>(a);
   prefill_fc_kernel<false><<<(unsigned)g2, PF_THREADS, 0, st>>>(a);
