@@ -496,9 +496,73 @@ __global__ __launch_bounds__(64) void stage_x_kernel(RouteArgs a) {
   if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = ldexp2(1.0f, ex);
 }
 
+// One-token step (k <= 64, one token group per routed pair): one wave does the top-k,
+// orders the k experts by id, checks their slots and writes the same worklist as
+// worklist_kernel (experts ascending, one pair and one group of each list per expert),
+// with a few memory round trips instead of a 1024-thread workgroup's phases.
+template <int NPL>
+__global__ __launch_bounds__(64) void worklist_one_kernel(RouteArgs ra, WorklistArgs a) {
+  const int lane = threadIdx.x;
+  const int k = a.k;
+  int id = 0;
+  topk_token<NPL>(ra, 0, lane, &id);  // lane i < k: expert of pair i (pair index p = i)
+  // rank of this lane's expert among the k (distinct) experts
+  int rank = 0;
+  for (int j = 0; j < k; ++j) rank += __shfl(id, j) < id ? 1 : 0;
+  moe_vq_slot sl{};
+  if (lane < k) sl = a.slots[id];
+  uint32_t fmt = sl.format;
+  const uint64_t off = sl.byte_offset;
+  uint64_t need = 0;
+  if (fmt == MOE_VQ_FMT_VQ2 || fmt == MOE_VQ_FMT_MXFP4) need = slot_layout((int)fmt, a.H, a.I).total;
+  const bool ok = need != 0 && (off & 255) == 0 && off <= a.pool_bytes && need <= a.pool_bytes - off;
+  if (!ok) fmt = MOE_VQ_FMT_ABSENT;
+  int bad = (lane < k && !ok) ? id : 0x7FFFFFFF;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) bad = min(bad, __shfl_xor(bad, d));
+  if (lane < k) {
+    a.pair_list[rank] = lane;
+    a.act_expert[rank] = id;
+    a.act_start[rank] = rank;
+    a.act_off[rank] = off;
+    a.act_fmt[rank] = fmt;
+    a.grp1[rank] = rank;
+    a.grp2[rank] = rank;
+    GroupRec r;
+    r.slot_off = off;
+    r.p0 = rank;
+    r.mcount = 1;
+    r.fmt = fmt;
+    r.expert = id;
+#pragma unroll
+    for (int j = 0; j < MAX_MT; ++j) r.pair[j] = lane;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.pad[j] = 0;
+    a.rec1[rank] = r;
+    a.rec2[rank] = r;
+  }
+  if (lane == 0) {
+    a.act_start[k] = k;
+    a.grp1[k] = k;
+    a.grp2[k] = k;
+    a.hdr[HDR_STATUS] = bad != 0x7FFFFFFF ? MOE_VQ_ENOTRESIDENT : MOE_VQ_OK;
+    a.hdr[HDR_INFO] = (uint32_t)(bad != 0x7FFFFFFF ? bad : -1);
+    a.hdr[HDR_N_ACTIVE] = k;
+    a.hdr[HDR_N_PAIRS] = k;
+    a.hdr[HDR_N_TOKENS] = 1;
+    a.hdr[HDR_GROUPS1] = k;
+    a.hdr[HDR_GROUPS2] = k;
+    a.hdr[HDR_MT1] = a.MT1;
+    a.hdr[HDR_MT2] = a.MT2;
+    a.hdr[HDR_KEY] = a.key;
+  }
+}
+
 template <int NPL>
 static void launch_topk_worklist(const RouteArgs& ra, const WorklistArgs& wa, hipStream_t st) {
-  if (ra.T <= FUSED_TOPK_MAX_T) {
+  if (ra.T == 1 && ra.k <= 64 && wa.MT1 == 1 && wa.MT2 == 1 && wa.G1 >= ra.k && wa.G2 >= ra.k) {
+    worklist_one_kernel<NPL><<<1, 64, 0, st>>>(ra, wa);
+  } else if (ra.T <= FUSED_TOPK_MAX_T) {
     worklist_kernel<true, NPL><<<1, 1024, 0, st>>>(ra, wa);
   } else {
     topk_kernel<NPL><<<(ra.T + 3) / 4, 256, 0, st>>>(ra);

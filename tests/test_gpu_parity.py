@@ -197,6 +197,33 @@ def test_absent_expert_is_reported_and_left_out(tiny):
     assert err.max() <= 1e-2
 
 
+def test_one_token_absent_experts_reported(tiny):
+    """One-token steps take their own worklist kernel: two selected experts absent, the
+    lowest one reported, both left out of y."""
+    syn, _ = tiny
+    x = syn.x()[:1]
+    x64 = oracle.x_value(x, "f32")
+    ids = oracle.topk(oracle.router_logits(syn.router_w, x64), syn.cfg.top_k)[0]
+    fm = list(syn.formats)
+    for e in ids:
+        fm[int(e)] = synth.FMT_ABSENT
+    v, dev = tiny_variant(syn, formats=fm)
+    g = run(dev, x, "f32")
+    assert g["status"] == _lib.ENOTRESIDENT and g["info"] == int(min(ids))
+    assert np.array_equal(g["ids"][0], ids)
+    assert np.all(g["y"] == 0.0)  # every routed expert absent: nothing is added
+    # one of the two absent: y is the other expert's weighted output
+    fm = list(syn.formats)
+    fm[int(ids[1])] = synth.FMT_ABSENT
+    v, dev = tiny_variant(syn, formats=fm)
+    g = run(dev, x, "f32")
+    assert g["status"] == _lib.ENOTRESIDENT and g["info"] == int(ids[1])
+    r = oracle.forward(syn, x64, syn.cfg.top_k, forced_selection=g["ids"])
+    y_ref = r["w"][0, 0] * r["o"][0, 0]
+    err = np.abs(g["y"][0] - y_ref).max() / np.abs(y_ref).max()
+    assert err <= 1e-2
+
+
 def test_slot_outside_pool_is_reported(tiny):
     syn, _ = tiny
     v, dev = tiny_variant(syn)
