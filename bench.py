@@ -12,10 +12,12 @@ bits/weight, all resident in one HBM slot pool).  Tokens are cycled from a pool 
 256 distinct pre-drawn tokens so consecutive steps touch different experts (the
 256 MB Infinity Cache holds about two steps' experts, not the pool).
 
-Prints one JSON line.  `value` is tokens/s of the whole step timed on the host
-between two device synchronisations; `roofline` rates the dominant kernel (FC1)
-by its algorithmic code+scale bytes per launch over its mean duration measured
-with HIP events on the launch stream inside the timed region.
+Prints one JSON line.  `value` is tokens/s of K steps timed on the host between two
+device synchronisations, with nothing else on the stream.  The same K steps then run
+again with HIP events recorded on the launch stream around FC1 and FC2 (each event
+costs the device a few microseconds, so they stay out of the throughput region);
+`roofline` rates the dominant kernel (FC1) by its algorithmic code+scale bytes per
+launch over the mean duration those events measure.
 
 `roofline.traffic` is the FC1 kernel's HBM traffic per launch as the hardware
 counters saw it: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc
@@ -244,14 +246,21 @@ def main():
         step_bytes.append(expert_stream_bytes(dev, inf["experts"]))
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # throughput: K steps, nothing but the step on the stream
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_step(args.warmup + i, events[i])
+        run_step(args.warmup + i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    # kernel durations: the same K steps with HIP events around FC1 and FC2
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] kernel timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        run_step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
     fc1_ms = [events[i][0].elapsed_time(events[i][1]) for i in range(args.steps)]
     fc2_ms = [events[i][1].elapsed_time(events[i][2]) for i in range(args.steps)]
     bidx = [(args.warmup + i) % n_batches for i in range(args.steps)]
