@@ -148,6 +148,14 @@ def test_fc_and_prefill_and_decode_reject_bad_arguments():
     assert raw.moe_vq_decode_expert(P(L), 0, 0, _lib.F32, None, None, None) == _lib.EINVAL
     assert raw.moe_vq_check(None, None, None) == _lib.EINVAL
     assert raw.moe_vq_step_info(None, 4, WS, None, None, None) == _lib.EINVAL
+    # no tokens: every step call is a no-op; more than 65536 tokens: rejected
+    assert raw.moe_vq_fc2_combine(P(L), H_, 0, WS, ws_ok, Y, None) == _lib.OK
+    assert raw.moe_vq_prefill_gemm(P(L), 0x40000, _lib.BF16, 0, WS, ws_ok, Y, None) == _lib.OK
+    for T in (-1, 65537):
+        assert raw.moe_vq_route_topk(P(L), 0x40000, _lib.F32, T, 0x50000, 0x60000, WS, ws_ok, None) == _lib.EINVAL
+        assert raw.moe_vq_fc1_silu(P(L), T, WS, ws_ok, H_, None) == _lib.EINVAL
+        assert raw.moe_vq_fc2_combine(P(L), H_, T, WS, ws_ok, Y, None) == _lib.EINVAL
+        assert raw.moe_vq_prefill_gemm(P(L), 0x40000, _lib.BF16, T, WS, ws_ok, Y, None) == _lib.EINVAL
 
 
 def test_strerror():

@@ -154,6 +154,29 @@ def test_sign_flip_of_down_codes_negates_y(tiny):
     assert np.all(np.abs(b["y"] + a["y"]) <= 2.0 ** -20 * scale)
 
 
+@pytest.mark.parametrize("T", [1, 5])
+def test_top1_routing(tiny, T):
+    """k = 1: every routing weight is 1 and y is the selected expert's output."""
+    syn, _ = tiny
+    v, dev = tiny_variant(syn, top_k=1)
+    x = syn.x(n=T, stream=70 + T)
+    g = run(dev, x, "f32")
+    assert g["status"] == _lib.OK
+    assert np.all(g["w"] == 1.0)
+    compare(syn, x, "f32", g, 1)
+
+
+def test_top1_routing_tiled_kernels(mini):
+    """k = 1 on shapes that take the one-token FC2 and the matrix-core kernels."""
+    syn, _ = mini
+    v, dev = tiny_variant(syn, top_k=1)
+    for T in (1, 40):
+        x = syn.x(n=T, stream=80 + T)
+        g = run(dev, x, "bf16")
+        assert g["status"] == _lib.OK
+        compare(syn, x, "bf16", g, 1)
+
+
 def test_k_equals_E_gives_full_softmax(tiny):
     syn, _ = tiny
     E = syn.cfg.n_experts
