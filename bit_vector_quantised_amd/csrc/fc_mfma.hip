@@ -59,11 +59,12 @@ struct MfGeom {
   static constexpr int NGQ = 8 * CPL / W;  // 128-wide scale groups in a wave's part of K
   static constexpr int NPAIR = NGQ / 2;  // groups read two at a time (16-byte loads)
   static constexpr bool ODD = (NGQ & 1) != 0;  // the last group is read alone (8 bytes)
-  // 16-row blocks per tile: ring slots per wave for several KB of codes in flight, at
-  // most 4 blocks with eight waves (registers), at most 8 (matrix, block) pairs so the
+  // 16-row blocks per tile: ring slots per wave for several KB of codes in flight (a
+  // tile's time is mostly load latency, so more bytes per tile is more throughput); FC1
+  // at most 4 blocks with eight waves (registers), at most 8 (matrix, block) pairs so the
   // partial sums fit in LDS
   static constexpr int NB_RULE = CPL >= 4 ? (FC1 ? 1 : 2) : (FC1 ? 8 / CPL : 16 / CPL);
-  static constexpr int NB_CAP = W == 8 ? 4 : 8 / NM;
+  static constexpr int NB_CAP = W == 8 ? (FC1 ? 4 : 8) : 8 / NM;
   static constexpr int NB = NB_RULE < NB_CAP ? NB_RULE : NB_CAP;
   static constexpr int ROWS = 16 * NB;
   static constexpr int KS = CPL;       // activation slices of 1024 columns (FC1 factors)
@@ -496,6 +497,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   __syncthreads();
 
   bool fresh = true;  // the tile is the first of its token group (FC2 converts h)
+  if (!FC1) { convert_h(rc); fresh = false; }
   int buf = 0;
   for (;;) {
     const int tn = t + 1;
@@ -515,10 +517,13 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
       if (next_vq) ring_load(rn, tn % RB);
       else ring_clear();  // the ring is then dead here, not kept alive across compute_mx
     }
-    if (next_group) act_load(tk, rn);  // this tile was the last use of the activations
+    if (next_group) {
+      act_load(tk, rn);  // this tile was the last use of the activations
+      if (!FC1) convert_h(rn);  // (waits for the h loads here: fp32 h is not kept across tiles)
+    }
     finish(rc, t % RB, buf);
     if (!more) break;
-    fresh = next_group;
+    fresh = false;
     rc = rn;
     rn = rnn;
     t = tn;
