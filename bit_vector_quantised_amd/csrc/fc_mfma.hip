@@ -351,7 +351,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   auto compute_vq = [&](bool refill, const RecS& rn, int rbn, const RecS& rcur, int rbc)
                         __attribute__((always_inline)) {
     const MfAddr dn = refill ? vq_addr(rn, rbn) : vq_addr(rcur, rbc);
-    if (MF_WAVES > 4) {
+    if (FC1 && MF_WAVES > 4) {
       // two waves per SIMD interleave by themselves: no registers for a pipeline
 #pragma unroll
       for (int u = 0; u < NU; ++u) unit_mma(u, decode(u, dn));

@@ -405,6 +405,13 @@ def b8mx():
     torch.cuda.empty_cache()
 
 
+def test_b8mx_decode_sampled_rows_mxfp4(b8mx):
+    """Full-size MXFP4 expert (one of the 52 most popular): sampled rows bit for bit."""
+    syn, dev = b8mx
+    say("b8mx decode")
+    _check_decode(syn, dev, [int(np.nonzero(syn.formats == synth.FMT_MXFP4)[0][3])], rows=slice(0, 2048, 97))
+
+
 def test_b8mx_step(b8mx):
     syn, dev = b8mx
     x = syn.x()
