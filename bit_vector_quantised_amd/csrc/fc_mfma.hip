@@ -72,17 +72,17 @@ struct MfGeom {
   static constexpr int QS = ROWS + 1;  // LDS stride of one token's partial sums
   static constexpr int RED = W * NM * MF_MT * QS;  // floats per reduction buffer
   static constexpr int NBUF = (size_t)TAB_BYTES + 2 * (size_t)RED * 4 <= (size_t)150 * 1024 ? 2 : 1;
-  // MXFP4 tiles load up to MXG groups per pass: as many as fit in about 80 registers
+  // MXFP4 groups beyond the ring's load in passes of up to MXG groups: as many as fit in
+  // about 40 registers (80 with one wave per SIMD)
   // (30 with two waves per SIMD, where the A fragments take 112 of 256)
   static constexpr int mxg() {
-    const int budget = W == 4 ? 80 : 30;
+    const int budget = W == 4 ? 80 : 40;
     int best = 1;
     for (int d = 1; d <= NGQ; ++d)
       if (d * NM * NB * 5 <= budget) best = d;
     return best;
   }
   static constexpr int MXG = mxg();
-  static constexpr int MXP = (NGQ + MXG - 1) / MXG;  // passes
 };
 
 // VQ2 codes one lane holds for one (group pair, matrix, row block): 16 code bytes (8 of
@@ -229,40 +229,68 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     return fx2[FC1 ? 0 : gi][q];
   };
 
-  // Addresses of one tile's VQ2 codes: uniform matrix bases, 32-bit per-lane offsets per
-  // row block; the pair offset pi*64 (scales: group offset * 2) is an immediate.
+  // Addresses of one tile's codes in the ring's shape: uniform matrix bases, 32-bit
+  // per-lane row offsets per row block, and per-slot immediates.  Both formats put slot
+  // pi's 16 bytes per lane 64 bytes further along the row and its scale dword 4 bytes
+  // further: VQ2 pair slot pi is groups gpair + 2pi, gpair + 2pi + 1 (16 bytes at the
+  // lane's quarter of the pair's 64); an MXFP4 slot pi is group gpair + pi (16 bytes of
+  // the lane's k-part p(q), and the dword of the group's four E8M0 bytes).
   struct MfAddr {
     const uint8_t* qb[NM];
     const uint8_t* sb[NM];
-    uint32_t qo[NB], so[NB];
+    uint32_t qo[NB], so[NB];  // per row block: slot 0's code and scale offsets
+    uint32_t dq0, ds0;        // subtracted: back to the row start (lane part of the codes)
+    uint32_t dq1, ds1;        // added for the lone group (wrapping 32-bit deltas)
   };
-  const uint32_t lane_pair = (uint32_t)(gpair * 32 + kq * 16);  // 16 bytes of a group pair
-  const uint32_t lane_one = (uint32_t)(gone * 32 + pq * 8);      // 8 bytes of the lone group
+  // VQ2 lone group, relative to slot 0's offsets: (gone*32 + pq*8) - (gpair*32 + kq*16)
+  const uint32_t lone_dq = (uint32_t)(gone * 32 + pq * 8) - (uint32_t)(gpair * 32 + kq * 16);
+  const uint32_t lone_ds = (uint32_t)(gone * 2) - (uint32_t)(gpair * 2);
   auto vq_addr = [&](const RecS& r, int rb) __attribute__((always_inline)) -> MfAddr {
     MfAddr d;
+    const bool mx = r.fmt == MOE_VQ_FMT_MXFP4;
+    const SlotLayout& L = mx ? a.mx4 : a.vq2;
     const uint8_t* slot = a.pool + r.slot_off;
-    d.qb[0] = slot + (FC1 ? a.vq2.q_gate : a.vq2.q_down);
-    d.sb[0] = slot + (FC1 ? a.vq2.s_gate : a.vq2.s_down);
-    if (NM > 1) { d.qb[NM - 1] = slot + a.vq2.q_up; d.sb[NM - 1] = slot + a.vq2.s_up; }
+    d.qb[0] = slot + (FC1 ? L.q_gate : L.q_down);
+    d.sb[0] = slot + (FC1 ? L.s_gate : L.s_down);
+    if (NM > 1) { d.qb[NM - 1] = slot + L.q_up; d.sb[NM - 1] = slot + L.s_up; }
+    const uint32_t qrow = mx ? (uint32_t)(K / 2) : (uint32_t)(K / 4);
+    const uint32_t srow = mx ? (uint32_t)(K / 32) : (uint32_t)(K / 64);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       // rows past the end (ragged shapes only) re-read the last row; the epilogue drops them
       const uint32_t n = (uint32_t)min(rb * ROWS + nb * 16 + i16, NROWS - 1);
-      d.qo[nb] = n * (uint32_t)(K / 4);
-      d.so[nb] = n * (uint32_t)(K / 128) * 2u;
+      d.qo[nb] = n * qrow;
+      d.so[nb] = n * srow;
     }
+    const uint32_t lq = mx ? (uint32_t)(pq * 16) : (uint32_t)(kq * 16);   // per lane
+    const uint32_t uq0 = mx ? (uint32_t)(gpair * 64) : (uint32_t)(gpair * 32);
+    const uint32_t us0 = mx ? (uint32_t)(gpair * 4) : (uint32_t)(gpair * 2);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      d.qo[nb] += lq + uq0;
+      d.so[nb] += us0;
+    }
+    d.dq0 = uq0;  // (MXFP4: the row start plus the lane's k-part offset is qo - dq0)
+    d.ds0 = us0;
+    // The lone delta is relative to the VQ2 lane part (kq*16), which an MXFP4 d does not
+    // hold (pq*16): there it could reach below the row start and wrap.  An MXFP4 tile
+    // never reads its lone slot, so that load goes to the lane's row start instead.
+    d.dq1 = mx ? 0u - uq0 : lone_dq;
+    d.ds1 = mx ? 0u - us0 : lone_ds;
     return d;
   };
   auto load_pair = [&](const MfAddr& d, int pi, int m, int nb) __attribute__((always_inline)) -> MfPair {
     MfPair c;
-    c.q = *reinterpret_cast<const uint4*>(d.qb[m] + d.qo[nb] + lane_pair + pi * 64);
-    c.s = *reinterpret_cast<const uint32_t*>(d.sb[m] + d.so[nb] + gpair * 2 + pi * 4);
+    c.q = *reinterpret_cast<const uint4*>(d.qb[m] + d.qo[nb] + pi * 64);
+    c.s = *reinterpret_cast<const uint32_t*>(d.sb[m] + d.so[nb] + pi * 4);
     return c;
   };
   auto load_one = [&](const MfAddr& d, int m, int nb) __attribute__((always_inline)) -> MfOne {
     MfOne c;
-    c.q = *reinterpret_cast<const uint2*>(d.qb[m] + d.qo[nb] + lane_one);
-    c.s = *reinterpret_cast<const uint16_t*>(d.sb[m] + d.so[nb] + gone * 2);
+    // (the sums wrap in 32 bits: the lone group can lie before slot 0; the true sum is
+    // never negative)
+    c.q = *reinterpret_cast<const uint2*>(d.qb[m] + (uint32_t)(d.qo[nb] + d.dq1));
+    c.s = *reinterpret_cast<const uint16_t*>(d.sb[m] + (uint32_t)(d.so[nb] + d.ds1));
     return c;
   };
 
@@ -367,50 +395,66 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     }
   };
 
-  // MXFP4 tile (not pipelined): up to MXG groups of the wave's part of K per pass; each
-  // lane reads the 32 weights of its k-part p(q) of the group
+  // MXFP4 tile: its first NPAIR groups arrived in the ring with the previous tile (one
+  // unit per ring pair slot); the remaining groups load here in passes of up to MXG
+  // groups, the first of them before the ring groups are multiplied.  Each lane reads the
+  // 32 weights of its k-part p(q) of a group.
+  auto mx_unit = [&](int gi, const uint4& q, uint32_t e, int m, int nb) __attribute__((always_inline)) {
+    const float es = e8m0_to_f32(e);
+    half8_t bfr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t wd = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
+      const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 0);
+      const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 1);
+      const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 2);
+      const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 3);
+      bfr[s] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+    group_mma(gi, bfr, 1.0f, acc[m][nb]);
+  };
   auto compute_mx = [&](const RecS& r, int rb) __attribute__((always_inline)) {
-    const uint8_t* slot = a.pool + r.slot_off;
-#pragma unroll
-    for (int h = 0; h < G::MXP; ++h) {
-      constexpr int NH = G::MXG;
-      MfMx mx[NH][NM][NB];
-#pragma unroll
-      for (int j = 0; j < NH; ++j)
-        if (h * NH + j < NGQ)
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const uint8_t* qb = slot + (m == 0 ? (FC1 ? a.mx4.q_gate : a.mx4.q_down) : a.mx4.q_up);
-            const uint8_t* sb = slot + (m == 0 ? (FC1 ? a.mx4.s_gate : a.mx4.s_down) : a.mx4.s_up);
-            const uint32_t n = (uint32_t)min(rb * ROWS + nb * 16 + i16, NROWS - 1);
-            const int g = gid(h * NH + j);
-            mx[j][m][nb].q = *reinterpret_cast<const uint4*>(qb + n * (uint32_t)(K / 2) + (uint32_t)(g * 64 + pq * 16));
-            mx[j][m][nb].e = sb[n * (uint32_t)(K / 32) + (uint32_t)(g * 4 + pq)];
-          }
+    const MfAddr d = vq_addr(r, rb);
+    constexpr int NH = G::MXG;
+    constexpr int REM = NGQ - NPAIR;             // groups not in the ring
+    constexpr int NPASS = (REM + NH - 1) / NH;
+    MfMx mx[NH][NM][NB];
+    auto mx_load = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
-        const int gi = h * NH + j;
+        const int gi = NPAIR + h * NH + j;
+        if (gi < NGQ)
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              const uint32_t g = (uint32_t)gid(gi);
+              mx[j][m][nb].q = *reinterpret_cast<const uint4*>(d.qb[m] + (uint32_t)(d.qo[nb] - d.dq0 + g * 64));
+              mx[j][m][nb].e = d.sb[m][(uint32_t)(d.so[nb] - d.ds0 + g * 4 + pq)];
+            }
+      }
+    };
+    if (NPASS > 0) mx_load(0);
+#pragma unroll
+    for (int pi = 0; pi < NPAIR; ++pi)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const MfPair c = ringP[pi][m][nb];
+          mx_unit(pi, c.q, (c.s >> (8 * pq)) & 0xFFu, m, nb);
+        }
+#pragma unroll
+    for (int h = 0; h < NPASS; ++h) {
+      if (h > 0) mx_load(h);
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const int gi = NPAIR + h * NH + j;
         if (gi >= NGQ) break;
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const float es = e8m0_to_f32(mx[j][m][nb].e);
-            half8_t bfr[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const uint32_t wd = s == 0 ? mx[j][m][nb].q.x : s == 1 ? mx[j][m][nb].q.y
-                                : s == 2 ? mx[j][m][nb].q.z : mx[j][m][nb].q.w;
-              const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 0);
-              const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 1);
-              const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 2);
-              const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 3);
-              bfr[s] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-            }
-            group_mma(gi, bfr, 1.0f, acc[m][nb]);
-          }
+          for (int nb = 0; nb < NB; ++nb) mx_unit(gi, mx[j][m][nb].q, mx[j][m][nb].e, m, nb);
       }
     }
   };
@@ -492,7 +536,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   RecS rc = load_rec(a.rec, t / RB);
   RecS rn = (t + 1 < t_end) ? load_rec(a.rec, (t + 1) / RB) : rc;
   act_load(tok_load(rc), rc);
-  if (rc.fmt == MOE_VQ_FMT_VQ2) ring_load(rc, t % RB);
+  if (rc.fmt == MOE_VQ_FMT_VQ2 || rc.fmt == MOE_VQ_FMT_MXFP4) ring_load(rc, t % RB);
   if (tid < 256) write_table_entry(tab, cbv, tid);  // (every block has >= 256 threads)
   __syncthreads();
 
@@ -503,7 +547,9 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     const int tn = t + 1;
     const bool more = tn < t_end;
     const RecS rnn = (tn + 1 < t_end) ? load_rec(a.rec, (tn + 1) / RB) : rn;
-    const bool next_vq = more && rn.fmt == MOE_VQ_FMT_VQ2;
+    // the ring takes the next tile's codes (VQ2: all but the lone group; MXFP4: the first
+    // NPAIR groups)
+    const bool next_vq = more && (rn.fmt == MOE_VQ_FMT_VQ2 || rn.fmt == MOE_VQ_FMT_MXFP4);
     const bool next_group = more && tn / RB != t / RB;
     Tok tk{};
     if (next_group) tk = tok_load(rn);
