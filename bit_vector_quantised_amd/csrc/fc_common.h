@@ -89,6 +89,18 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
+// v copied into a new register by an instruction the compiler cannot see through.  An
+// in-place cross-lane op (v_permlane32_swap) ties its operands to its results; handed a
+// ring register directly, the register coalescer gives the loop-carried ring value the
+// swap's registers, so the refill load lands elsewhere and the loop's back edge copies it
+// back, waiting for every refill in flight.  Copying at the point of use keeps the ring
+// in the registers its loads write.
+__device__ __forceinline__ uint32_t reg_copy(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
 static_assert(offsetof(GroupRec, p0) == 8 && offsetof(GroupRec, mcount) == 12 && offsetof(GroupRec, fmt) == 16 &&
               offsetof(GroupRec, pair) == 24, "GroupRec layout");
 

@@ -114,6 +114,10 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   constexpr bool ODD = G::ODD;
   __shared__ uint2 tab[256 * TAB_COPIES];
   __shared__ float red[NBUF * RED];
+  // pair of each token row of the current and the next token group: the outputs' rows,
+  // read here rather than from global memory at the end of every tile (a load there
+  // would wait for every older load, i.e. for the ring in flight)
+  __shared__ int s_pair[2][MF_MT];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, kq = lane >> 4;
@@ -159,6 +163,17 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   };
   // Issue the loads of a token group's activations (FC1: fp16 x and its factors; FC2:
   // fp32 h, converted by convert_h when the group's first tile starts).
+  // The token rows of the next group are loaded at the top of a tile and used after it:
+  // arithmetic on them next to their load would wait there for every older load, i.e.
+  // for the ring in flight.  This fence keeps their first use where it is written.
+  auto tok_fence = [&](const Tok& t_in) __attribute__((always_inline)) -> Tok {
+    Tok t;
+    t.arow = opaque(t_in.arow);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t.drow[q] = FC1 ? opaque(t_in.drow[q]) : 0;
+    return t;
+  };
+  float hw = 0.f;  // FC2: routing weight of the pair of A row i16 (folded into h)
   auto act_load = [&](const Tok& t, const RecS& r) __attribute__((always_inline)) {
     if (FC1) {
       const int tokA = t.arow / a.k;
@@ -178,6 +193,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
         }
       }
     } else {
+      hw = a.pair_w[t.arow];
       const float* hr = a.h_in + (size_t)t.arow * K + 32 * pq;
 #pragma unroll
       for (int gi = 0; gi < NGQ; ++gi)
@@ -185,14 +201,22 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
         for (int i = 0; i < 8; ++i) A32[FC1 ? 0 : gi][i] = *reinterpret_cast<const float4*>(hr + gid(gi) * 128 + 4 * i);
     }
   };
-  // FC2: fp32 h -> fp16 A fragments with one power-of-two factor per (pair, group); the
-  // factor of D row r (pair 4 kq + r) comes from the lanes holding that A row.
+  // FC2: fp32 h times the pair's routing weight -> fp16 A fragments with one power-of-two
+  // factor per (pair, group); the factor of D row r (pair 4 kq + r) comes from the lanes
+  // holding that A row.  (The weighted sum then needs no weight at the output.)
   auto convert_h = [&](const RecS& r) __attribute__((always_inline)) {
     if (!FC1) {
 #pragma unroll
       for (int gi = 0; gi < NGQ; ++gi) {
         const int gk = FC1 ? 0 : gi;
         float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          A32[gk][i].x *= hw;
+          A32[gk][i].y *= hw;
+          A32[gk][i].z *= hw;
+          A32[gk][i].w *= hw;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           m = fmaxf(m, fmaxf(fmaxf(fabsf(A32[gk][i].x), fabsf(A32[gk][i].y)),
@@ -345,12 +369,13 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
         // the slot is consumed (swap, scales) before its refill is issued, so the refill
         // can land in the same registers
         const MfPair c = ringP[pi][m][nb];
-        const auto lo = __builtin_amdgcn_permlane32_swap(c.q.x, c.q.z, false, false);
-        const auto hi = __builtin_amdgcn_permlane32_swap(c.q.y, c.q.w, false, false);
+        const auto lo = __builtin_amdgcn_permlane32_swap(reg_copy(c.q.x), reg_copy(c.q.z), false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(reg_copy(c.q.y), reg_copy(c.q.w), false, false);
         pw2 = lo[1];
         pw3 = hi[1];
-        ps = c.s >> 16;
-        d.sc = f16_bits_to_f32(c.s & 0xFFFFu);
+        const uint32_t cs = reg_copy(c.s);
+        ps = cs >> 16;
+        d.sc = f16_bits_to_f32(cs & 0xFFFFu);
         ringP[pi][m][nb] = load_pair(dn, pi, m, nb);
         b_frags(lo[0], hi[0], d.b);
       } else {
@@ -360,9 +385,10 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     } else {
       const int m = ((u - 2 * NPS) / NB) % NM, nb = (u - 2 * NPS) % NB;
       const MfOne c = ringS[ODD ? m : 0][ODD ? nb : 0];
-      d.sc = f16_bits_to_f32(c.s);
+      const uint32_t c0 = reg_copy(c.q.x), c1 = reg_copy(c.q.y);
+      d.sc = f16_bits_to_f32(reg_copy(c.s));
       ringS[ODD ? m : 0][ODD ? nb : 0] = load_one(dn, m, nb);
-      b_frags(c.q.x, c.q.y, d.b);
+      b_frags(c0, c1, d.b);
     }
     return d;
   };
@@ -395,10 +421,8 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     }
   };
 
-  // MXFP4 tile: its first NPAIR groups arrived in the ring with the previous tile (one
-  // unit per ring pair slot); the remaining groups load here in passes of up to MXG
-  // groups, the first of them before the ring groups are multiplied.  Each lane reads the
-  // 32 weights of its k-part p(q) of a group.
+  // MXFP4 tile (not in the ring): the groups of the wave's part of K load in passes of up
+  // to MXG groups.  Each lane reads the 32 weights of its k-part p(q) of a group.
   auto mx_unit = [&](int gi, const uint4& q, uint32_t e, int m, int nb) __attribute__((always_inline)) {
     const float es = e8m0_to_f32(e);
     half8_t bfr[4];
@@ -416,13 +440,12 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   auto compute_mx = [&](const RecS& r, int rb) __attribute__((always_inline)) {
     const MfAddr d = vq_addr(r, rb);
     constexpr int NH = G::MXG;
-    constexpr int REM = NGQ - NPAIR;             // groups not in the ring
-    constexpr int NPASS = (REM + NH - 1) / NH;
+    constexpr int NPASS = (NGQ + NH - 1) / NH;
     MfMx mx[NH][NM][NB];
     auto mx_load = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
-        const int gi = NPAIR + h * NH + j;
+        const int gi = h * NH + j;
         if (gi < NGQ)
 #pragma unroll
           for (int m = 0; m < NM; ++m)
@@ -434,22 +457,12 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
             }
       }
     };
-    if (NPASS > 0) mx_load(0);
-#pragma unroll
-    for (int pi = 0; pi < NPAIR; ++pi)
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const MfPair c = ringP[pi][m][nb];
-          mx_unit(pi, c.q, (c.s >> (8 * pq)) & 0xFFu, m, nb);
-        }
 #pragma unroll
     for (int h = 0; h < NPASS; ++h) {
-      if (h > 0) mx_load(h);
+      mx_load(h);
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
-        const int gi = NPAIR + h * NH + j;
+        const int gi = h * NH + j;
         if (gi >= NGQ) break;
 #pragma unroll
         for (int m = 0; m < NM; ++m)
@@ -461,7 +474,10 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 
   // End of a tile: the waves' partial sums meet in LDS, then the outputs.  LDS
   // layout [wave][matrix][token][row] with a padded token stride.
-  auto finish = [&](const RecS& r, int rb, int buf) __attribute__((always_inline)) {
+  // gb: the current group's half of s_pair; the next group's pairs (arow_next, lanes 0-15
+  // of wave 0) go to the other half after the barrier, when every wave is past the
+  // previous tile's reads of it.
+  auto finish = [&](const RecS& r, int rb, int buf, int gb, bool wr_next, int arow_next) __attribute__((always_inline)) {
     float* R = red + (NBUF > 1 ? buf * RED : 0);
     if (NBUF == 1) __syncthreads();  // the previous tile's sums have been read
 #pragma unroll
@@ -472,6 +488,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
         for (int q = 0; q < 4; ++q)
           if (4 * kq + q < r.mcount) R[((wave * NM + m) * MF_MT + 4 * kq + q) * QS + nb * 16 + i16] = acc[m][nb][q];
     __syncthreads();
+    if (wr_next && wave == 0 && kq == 0) s_pair[gb ^ 1][i16] = arow_next;
     const int nout = ROWS * r.mcount;
     for (int o = tid; o < nout; o += MF_THREADS) {
       const int q = o / ROWS, ri = o % ROWS;
@@ -485,9 +502,9 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
           for (int w = 1; w < MF_WAVES; ++w) sum += R[((w * NM + m) * MF_MT + q) * QS + ri];
           v[m] = sum;
         }
-        const int p = a.pair_list[r.p0 + q];
+        const int p = s_pair[gb][q];
         if (FC1) a.out[(size_t)p * a.I + n] = silu_fast(v[0]) * v[NM - 1];
-        else a.out[(size_t)p * a.H + n] = a.pair_w[p] * v[0];
+        else a.out[(size_t)p * a.H + n] = v[0];  // (h carries the routing weight)
       }
     }
   };
@@ -530,45 +547,73 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
       for (int nb = 0; nb < (ODD ? NB : 1); ++nb) ringS[m][nb] = MfOne{make_uint2(0u, 0u), 0u};
   };
 
-  // ---- prologue.  Records are read one tile ahead of their use (rn is needed for the
-  // refill addresses while this tile decodes).
+  // Records are read one tile ahead of their use (rn is needed for the refill addresses
+  // while this tile decodes).  They are read-only for the whole launch, so they are read
+  // through the constant address space, i.e. with scalar loads: a vector load's value
+  // waits for every older vector load (they complete in order), here the whole ring in
+  // flight.
+  typedef const int __attribute__((address_space(4))) cint_t;
+  auto load_rec_c = [&](int g) __attribute__((always_inline)) -> RecS {
+    cint_t* w = reinterpret_cast<cint_t*>(reinterpret_cast<uintptr_t>(a.rec + g));
+    RecS r{};
+    r.slot_off = ((uint64_t)(uint32_t)w[1] << 32) | (uint32_t)w[0];
+    r.p0 = w[2];
+    r.mcount = w[3];
+    r.fmt = (uint32_t)w[4];
+    return r;
+  };
+
+  // ---- prologue
   int t = t_begin;
   RecS rc = load_rec(a.rec, t / RB);
   RecS rn = (t + 1 < t_end) ? load_rec(a.rec, (t + 1) / RB) : rc;
-  act_load(tok_load(rc), rc);
-  if (rc.fmt == MOE_VQ_FMT_VQ2 || rc.fmt == MOE_VQ_FMT_MXFP4) ring_load(rc, t % RB);
+  {
+    const Tok t0 = tok_load(rc);
+    act_load(t0, rc);
+    if (wave == 0 && kq == 0) s_pair[0][i16] = t0.arow;
+  }
+  if (rc.fmt == MOE_VQ_FMT_VQ2) ring_load(rc, t % RB);
+  bool ring_ok = rc.fmt == MOE_VQ_FMT_VQ2;  // the ring holds this tile's codes
   if (tid < 256) write_table_entry(tab, cbv, tid);  // (every block has >= 256 threads)
   __syncthreads();
 
   bool fresh = true;  // the tile is the first of its token group (FC2 converts h)
   if (!FC1) { convert_h(rc); fresh = false; }
-  int buf = 0;
+  int buf = 0, gb = 0;
   for (;;) {
     const int tn = t + 1;
     const bool more = tn < t_end;
-    const RecS rnn = (tn + 1 < t_end) ? load_rec(a.rec, (tn + 1) / RB) : rn;
-    // the ring takes the next tile's codes (VQ2: all but the lone group; MXFP4: the first
-    // NPAIR groups)
-    const bool next_vq = more && (rn.fmt == MOE_VQ_FMT_VQ2 || rn.fmt == MOE_VQ_FMT_MXFP4);
+    const RecS rnn = load_rec_c((tn + 1 < t_end ? tn + 1 : tn) / RB);  // (a valid record either way)
+    const bool next_vq = more && rn.fmt == MOE_VQ_FMT_VQ2;  // the ring takes the next tile's codes
     const bool next_group = more && tn / RB != t / RB;
-    Tok tk{};
+    Tok tk;  // (no initial value: writing one would wait for the last group's row loads)
     if (next_group) tk = tok_load(rn);
     if (fresh) convert_h(rc);
     zero_acc();
+    // The ring is defined in this branch only (a second definition elsewhere in the loop
+    // makes the compiler keep it in other registers and copy it back at the loop's back
+    // edge, waiting for every load in flight).  After a tile of another format it is
+    // stale, and the VQ2 tile loads its own codes first.
     if (rc.fmt == MOE_VQ_FMT_VQ2) {
+      if (!ring_ok) ring_load(rc, t % RB);
       compute_vq(next_vq, rn, tn % RB, rc, t % RB);  // refills the ring with tile tn's codes
-    } else {
-      if (rc.fmt == MOE_VQ_FMT_MXFP4) compute_mx(rc, t % RB);
-      // (an absent expert keeps zeros; the worklist has recorded MOE_VQ_ENOTRESIDENT)
-      if (next_vq) ring_load(rn, tn % RB);
-      else ring_clear();  // the ring is then dead here, not kept alive across compute_mx
+    } else if (rc.fmt == MOE_VQ_FMT_MXFP4) {
+      compute_mx(rc, t % RB);
     }
+    // (an absent expert keeps zeros; the worklist has recorded MOE_VQ_ENOTRESIDENT)
+    ring_ok = rc.fmt == MOE_VQ_FMT_VQ2 && next_vq;
     if (next_group) {
+      tk = tok_fence(tk);
       act_load(tk, rn);  // this tile was the last use of the activations
       if (!FC1) convert_h(rn);  // (waits for the h loads here: fp32 h is not kept across tiles)
+      // The activations are complete before the next tile, on this path: otherwise the
+      // tile body would carry a wait for them that, on every other tile, waits for the
+      // ring in flight too.  (s_waitcnt vmcnt(0); expcnt and lgkmcnt left alone.)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     }
-    finish(rc, t % RB, buf);
+    finish(rc, t % RB, buf, gb, next_group, tk.arow);
     if (!more) break;
+    if (next_group) gb ^= 1;
     fresh = false;
     rc = rn;
     rn = rnn;
