@@ -450,8 +450,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouteArgs a) {
 // decode-path FC kernels (exact for bf16 x): one wave per (token, slice), 16 columns
 // per lane.
 template <bool XF32>
-__global__ __launch_bounds__(64) void stage_x_kernel(RouteArgs a) {
-  const int lane = threadIdx.x, t = blockIdx.x, s = blockIdx.y;
+__device__ __forceinline__ void stage_x_row(const RouteArgs& a, int t, int s, int lane) {
   const int c0 = s * SLICE + lane * 16;
   const bool col_ok = c0 < a.H;
   float xf[16];
@@ -494,6 +493,74 @@ __global__ __launch_bounds__(64) void stage_x_kernel(RouteArgs a) {
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
   }
   if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = ldexp2(1.0f, ex);
+}
+
+template <bool XF32>
+__global__ __launch_bounds__(64) void stage_x_kernel(RouteArgs a) {
+  stage_x_row<XF32>(a, blockIdx.x, blockIdx.y, threadIdx.x);
+}
+
+// Fewer tokens than the matrix-core router takes (bf16 x): the product split over K as the
+// GEMV router splits it, on the matrix cores.  Workgroup (expert block of 16, slice of
+// 1024 columns); wave w takes 256 columns of the slice for every token block of 16.  Its
+// loads (weights and x) are all issued before the first matrix op, so a workgroup waits
+// for one memory latency.  The four waves' sums meet in LDS in a fixed order, and the
+// slice's partial logit goes where the GEMV router puts it ([T][E][ksp]).  Workgroups of
+// expert block 0 also stage x as fp16 for the FC kernels.
+constexpr int RS_EXPERTS = 16;
+constexpr int RS_MAX_T = 64;  // token blocks of 16, at most four
+
+__global__ __launch_bounds__(256) void router_mfma_small_kernel(RouteArgs a) {
+  __shared__ float red[4][RS_MAX_T / 16][16][17];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i16 = lane & 15, kq = lane >> 4;
+  const int e0 = blockIdx.x * RS_EXPERTS, s = blockIdx.y;
+  const int T = a.T, H = a.H, MB = (T + 15) / 16;
+  const int c0 = s * SLICE + wave * 256 + 8 * kq;  // + 32 j: 8 columns, all in or all out (H % 128 == 0)
+  const uint16_t* xb = static_cast<const uint16_t*>(a.x);
+  const uint16_t* wr = a.router_w + (size_t)min(e0 + i16, a.E - 1) * H;
+  const bf16x8_t zero = bf16x8_t{};
+  bf16x8_t bfr[8], afr[RS_MAX_T / 16][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = c0 + 32 * j;
+    bfr[j] = c < H ? *reinterpret_cast<const bf16x8_t*>(wr + c) : zero;
+  }
+#pragma unroll
+  for (int mb = 0; mb < RS_MAX_T / 16; ++mb) {
+    const uint16_t* xr = xb + (size_t)min(mb * 16 + i16, T - 1) * H;  // rows past T re-read the last
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = c0 + 32 * j;
+      afr[mb][j] = (mb < MB && c < H) ? *reinterpret_cast<const bf16x8_t*>(xr + c) : zero;
+    }
+  }
+  // D: lane holds expert column i16 and token rows 4 kq + 0..3 of each token block
+#pragma unroll
+  for (int mb = 0; mb < RS_MAX_T / 16; ++mb) {
+    if (mb < MB) {
+      rf32x4_t acc = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mb][j], bfr[j], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][mb][4 * kq + r][i16] = acc[r];
+    }
+  }
+  __syncthreads();
+  const int KSP = a.ksp;
+  for (int o = tid; o < MB * 256; o += 256) {
+    const int mb = o >> 8, row = (o >> 4) & 15, col = o & 15;
+    const int t = mb * 16 + row, e = e0 + col;
+    if (t < T && e < a.E) {
+      const float v = ((red[0][mb][row][col] + red[1][mb][row][col]) + red[2][mb][row][col]) + red[3][mb][row][col];
+      float* dst = a.logits + ((size_t)t * a.E + e) * KSP;
+      dst[s] = v;
+      if (s == a.KS - 1)
+        for (int z = a.KS; z < KSP; ++z) dst[z] = 0.f;  // the padding slices
+    }
+  }
+  if (blockIdx.x == 0)
+    for (int t = wave; t < T; t += 4) stage_x_row<false>(a, t, s, lane);
 }
 
 // One-token step (k <= 64, one token group per routed pair): one wave does the top-k,
@@ -586,7 +653,9 @@ hipError_t launch_route(const RouteArgs& ra, int x_dtype, const WorklistArgs& wa
     return hipGetLastError();
   }
   dim3 g1((ra.E + RT_EXPERTS - 1) / RT_EXPERTS, ra.KS, (ra.T + RT_TOKENS - 1) / RT_TOKENS);
-  if (x_dtype == MOE_VQ_F32)
+  if (x_dtype == MOE_VQ_BF16 && ra.T >= 1 && ra.T <= RS_MAX_T)
+    router_mfma_small_kernel<<<dim3((ra.E + RS_EXPERTS - 1) / RS_EXPERTS, ra.KS), 256, 0, st>>>(ra);
+  else if (x_dtype == MOE_VQ_F32)
     router_gemv_kernel<true><<<g1, 256, 0, st>>>(ra);
   else
     router_gemv_kernel<false><<<g1, 256, 0, st>>>(ra);
