@@ -112,12 +112,16 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   constexpr int K = G::K, NM = G::NM, NB = G::NB, ROWS = G::ROWS, NGQ = G::NGQ, KS = G::KS;
   constexpr int NPAIR = G::NPAIR, QS = G::QS, RED = G::RED, NBUF = G::NBUF, NSLW = G::NSLW;
   constexpr bool ODD = G::ODD;
-  __shared__ uint2 tab[256 * TAB_COPIES];
-  __shared__ float red[NBUF * RED];
-  // pair of each token row of the current and the next token group: the outputs' rows,
-  // read here rather than from global memory at the end of every tile (a load there
-  // would wait for every older load, i.e. for the ring in flight)
-  __shared__ int s_pair[2][MF_MT];
+  // LDS, in one array so that the decode table starts at address 0: a lookup's address
+  // is then the v_perm result itself (past 64 KB it would need an add per lookup, the
+  // immediate offset of a ds_read being 16 bits).  Then the per-wave partial sums, and
+  // the pair of each token row of the current and the next token group: the outputs'
+  // rows, read from LDS rather than from global memory at the end of every tile (a load
+  // there would wait for every older load, i.e. for the ring in flight).
+  __shared__ __attribute__((aligned(16))) uint8_t lds[TAB_BYTES + NBUF * RED * 4 + 2 * MF_MT * 4];
+  uint2* const tab = reinterpret_cast<uint2*>(lds);
+  float* const red = reinterpret_cast<float*>(lds + TAB_BYTES);
+  int (*const s_pair)[MF_MT] = reinterpret_cast<int (*)[MF_MT]>(lds + TAB_BYTES + NBUF * RED * 4);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, kq = lane >> 4;
