@@ -571,13 +571,33 @@ template <int NPL>
 __global__ __launch_bounds__(64) void worklist_one_kernel(RouteArgs ra, WorklistArgs a) {
   const int lane = threadIdx.x;
   const int k = a.k;
+  // every expert's slot is read before the top-k (expert lane + 64 i in lane's entry i),
+  // so that looking the chosen ones up costs shuffles, not a memory round trip after it
+  moe_vq_slot pre[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    pre[i] = e < a.E ? a.slots[e] : moe_vq_slot{};
+  }
   int id = 0;
   topk_token<NPL>(ra, 0, lane, &id);  // lane i < k: expert of pair i (pair index p = i)
   // rank of this lane's expert among the k (distinct) experts
   int rank = 0;
   for (int j = 0; j < k; ++j) rank += __shfl(id, j) < id ? 1 : 0;
   moe_vq_slot sl{};
-  if (lane < k) sl = a.slots[id];
+  {
+    const int src = id & 63, hi = id >> 6;  // (every lane takes part in the shuffles)
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const uint32_t lo32 = (uint32_t)__shfl((int)(uint32_t)pre[i].byte_offset, src);
+      const uint32_t hi32 = (uint32_t)__shfl((int)(uint32_t)(pre[i].byte_offset >> 32), src);
+      const uint32_t fm = (uint32_t)__shfl((int)pre[i].format, src);
+      if (lane < k && hi == i) {
+        sl.byte_offset = ((uint64_t)hi32 << 32) | lo32;
+        sl.format = fm;
+      }
+    }
+  }
   uint32_t fmt = sl.format;
   const uint64_t off = sl.byte_offset;
   uint64_t need = 0;
