@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   topk_token<NPL>(a, t, lane, &id);
 }
 
-constexpr int FUSED_TOPK_MAX_T = 64;
+constexpr int FUSED_TOPK_MAX_T = 16;
 constexpr int PL_LDS = 2048;  // pair lists up to this length are also kept in LDS
 
 // Single workgroup: (optionally the top-k of every token, one wave per token), then
