@@ -505,8 +505,8 @@ __global__ __launch_bounds__(64) void stage_x_kernel(RouteArgs a) {
 // 1024 columns); wave w takes 256 columns of the slice for every token block of 16.  Its
 // loads (weights and x) are all issued before the first matrix op, so a workgroup waits
 // for one memory latency.  The four waves' sums meet in LDS in a fixed order, and the
-// slice's partial logit goes where the GEMV router puts it ([T][E][ksp]).  Workgroups of
-// expert block 0 also stage x as fp16 for the FC kernels.
+// slice's partial logit goes where the GEMV router puts it ([T][E][ksp]).  The workgroups
+// of a slice also stage its x as fp16 for the FC kernels.
 constexpr int RS_EXPERTS = 16;
 constexpr int RS_MAX_T = 64;  // token blocks of 16, at most four
 
@@ -559,8 +559,9 @@ __global__ __launch_bounds__(256) void router_mfma_small_kernel(RouteArgs a) {
         for (int z = a.KS; z < KSP; ++z) dst[z] = 0.f;  // the padding slices
     }
   }
-  if (blockIdx.x == 0)
-    for (int t = wave; t < T; t += 4) stage_x_row<false>(a, t, s, lane);
+  // the slice's staging, spread over the workgroups of the slice: at most one token per
+  // wave up to 4 * E / 16 tokens (each token is a memory round trip)
+  for (int t = blockIdx.x * 4 + wave; t < T; t += gridDim.x * 4) stage_x_row<false>(a, t, s, lane);
 }
 
 // One-token step (k <= 64, one token group per routed pair): one wave does the top-k,
