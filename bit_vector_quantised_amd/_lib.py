@@ -20,7 +20,8 @@ MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 
 EXPORTS = ("moe_vq_expert_bytes", "moe_vq_slot_layout", "moe_vq_workspace_bytes", "moe_vq_route_topk",
            "moe_vq_fc1_silu", "moe_vq_fc2_combine", "moe_vq_prefill_gemm", "moe_vq_decode_expert",
-           "moe_vq_check", "moe_vq_step_info", "moe_vq_last_hip_error", "moe_vq_strerror")
+           "moe_vq_check", "moe_vq_step_info", "moe_vq_tier_init", "moe_vq_tier_plan", "moe_vq_tier_resolve",
+           "moe_vq_last_hip_error", "moe_vq_strerror")
 
 
 class MoeVqError(RuntimeError):
@@ -38,6 +39,14 @@ class Layer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
                 ("pool", ctypes.c_void_p), ("pool_bytes", ctypes.c_uint64), ("slots", ctypes.c_void_p)]
+
+
+class Tier(ctypes.Structure):
+    _fields_ = [("host_pool", ctypes.c_void_p), ("host_slots", ctypes.POINTER(Slot)), ("n_dev_slots", ctypes.c_int32),
+                ("dev_slot_offsets", ctypes.POINTER(ctypes.c_uint64)),
+                ("dev_slot_expert", ctypes.POINTER(ctypes.c_int32)),
+                ("dev_slot_stamp", ctypes.POINTER(ctypes.c_uint64)), ("slot_mirror", ctypes.POINTER(Slot)),
+                ("step", ctypes.c_uint64)]
 
 
 def _load():
@@ -65,6 +74,11 @@ def _load():
         "moe_vq_decode_expert": (i32, [LP, i32, i32, i32, vp, vp, vp]),
         "moe_vq_check": (i32, [vp, vp, ctypes.POINTER(ctypes.c_int32)]),
         "moe_vq_step_info": (i32, [LP, i32, vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), vp]),
+        "moe_vq_tier_init": (i32, [LP, ctypes.POINTER(Tier), vp, vp]),
+        "moe_vq_tier_plan": (i32, [ctypes.POINTER(Tier), i32, ctypes.POINTER(ctypes.c_int32), i32,
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int)]),
+        "moe_vq_tier_resolve": (i32, [LP, ctypes.POINTER(Tier), vp, vp, i32, vp, vp, ctypes.POINTER(ctypes.c_int32)]),
         "moe_vq_last_hip_error": (ctypes.c_char_p, []),
         "moe_vq_strerror": (ctypes.c_char_p, [i32]),
     }
@@ -148,6 +162,61 @@ def step_info(layer: Layer, n_tokens: int, ws: int, stream: int = 0):
     n = int(summ[2])
     return {"status": int(summ[0]), "info": int(summ[1]), "n_active": n, "n_pairs": int(summ[3]),
             "experts": [int(v) for v in ex[:n]]}
+
+
+class ExpertTier:
+    """Caller-owned state of a host-RAM expert tier (struct moe_vq_tier): keeps the
+    host arrays the C structure points to alive.  host_pool: address of a pinned host
+    buffer holding every expert's slot; host_slots: [(byte_offset, format)] per expert;
+    dev_slot_offsets: offsets in the device pool of the slots the tier manages."""
+
+    def __init__(self, n_experts: int, host_pool: int, host_slots, dev_slot_offsets):
+        self.n_experts = n_experts
+        self._host_slots = (Slot * n_experts)(*[Slot(int(o), int(f), 0) for o, f in host_slots])
+        ns = len(dev_slot_offsets)
+        self._offs = (ctypes.c_uint64 * ns)(*[int(o) for o in dev_slot_offsets])
+        self._held = (ctypes.c_int32 * ns)(*([-1] * ns))
+        self._stamp = (ctypes.c_uint64 * ns)()
+        self._mirror = (Slot * n_experts)()
+        self.c = Tier(host_pool, self._host_slots, ns, self._offs, self._held, self._stamp, self._mirror, 0)
+
+    def held(self):
+        """Expert held by each device slot (-1 = free)."""
+        return [int(v) for v in self._held]
+
+    def stamps(self):
+        return [int(v) for v in self._stamp]
+
+    def set_state(self, held, stamps):
+        """Overwrite the slot state (for exercising the plan on the host)."""
+        for i, (h, t) in enumerate(zip(held, stamps)):
+            self._held[i] = int(h)
+            self._stamp[i] = int(t)
+
+
+def tier_init(layer: Layer, tier: ExpertTier, slots: int, stream: int = 0) -> None:
+    _ok(_lib.moe_vq_tier_init(ctypes.byref(layer), ctypes.byref(tier.c), slots, stream), "tier_init")
+
+
+def tier_plan(tier: ExpertTier, active):
+    """[(expert, device slot, evicted expert or -1)] for a step selecting `active`."""
+    n = len(active)
+    act = (ctypes.c_int32 * max(1, n))(*active)
+    ie, isl, ev = ((ctypes.c_int32 * max(1, n))() for _ in range(3))
+    cnt = ctypes.c_int(0)
+    _ok(_lib.moe_vq_tier_plan(ctypes.byref(tier.c), tier.n_experts, act, n, ie, isl, ev, ctypes.byref(cnt)),
+        "tier_plan")
+    return [(int(ie[i]), int(isl[i]), int(ev[i])) for i in range(cnt.value)]
+
+
+def tier_resolve(layer: Layer, tier: ExpertTier, pool: int, slots: int, n_tokens: int, ws: int,
+                 stream: int = 0) -> int:
+    """Copy the missing experts of the step last routed on ws; returns how many (route
+    again before FC1 if not 0).  Synchronises stream."""
+    n = ctypes.c_int32(0)
+    _ok(_lib.moe_vq_tier_resolve(ctypes.byref(layer), ctypes.byref(tier.c), pool, slots, n_tokens, ws, stream,
+                                 ctypes.byref(n)), "tier_resolve")
+    return int(n.value)
 
 
 def raw():

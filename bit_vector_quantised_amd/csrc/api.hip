@@ -271,6 +271,127 @@ int moe_vq_step_info(const moe_vq_layer* L, int n_tokens, const void* ws, int32_
   return MOE_VQ_OK;
 }
 
+// ---- Host-RAM expert tier (see moe_vq.h) ----------------------------------------------
+
+int moe_vq_tier_plan(const moe_vq_tier* tier, int n_experts, const int32_t* active, int n_active,
+                     int32_t* install_expert, int32_t* install_slot, int32_t* evict_expert, int* n_install) {
+  if (!tier || !n_install || n_experts < 1 || n_experts > MAX_E || n_active < 0 || n_active > n_experts)
+    return MOE_VQ_EINVAL;
+  if (n_active > 0 && (!active || !install_expert || !install_slot || !evict_expert)) return MOE_VQ_EINVAL;
+  const int ns = tier->n_dev_slots;
+  if (ns < 1 || ns > 4096 || !tier->host_slots || !tier->dev_slot_expert || !tier->dev_slot_stamp)
+    return MOE_VQ_EINVAL;
+  *n_install = 0;
+  // slots held by an active expert are not candidates; an expert is resident if a slot
+  // holds it
+  bool is_active[MAX_E] = {};
+  for (int i = 0; i < n_active; ++i) {
+    if (active[i] < 0 || active[i] >= n_experts) return MOE_VQ_EINVAL;
+    is_active[active[i]] = true;
+  }
+  int slot_of[MAX_E];
+  for (int e = 0; e < n_experts; ++e) slot_of[e] = -1;
+  for (int s = 0; s < ns; ++s) {
+    const int e = tier->dev_slot_expert[s];
+    if (e >= n_experts) return MOE_VQ_EINVAL;
+    if (e >= 0) slot_of[e] = s;
+  }
+  bool taken[4096] = {};  // slots assigned by this plan
+  int n = 0;
+  for (int i = 0; i < n_active; ++i) {
+    const int e = active[i];
+    if (slot_of[e] >= 0) continue;
+    const uint32_t f = tier->host_slots[e].format;
+    if (f != MOE_VQ_FMT_VQ2 && f != MOE_VQ_FMT_MXFP4) continue;  // not in the host pool either
+    int best = -1;
+    for (int s = 0; s < ns && best < 0; ++s)
+      if (!taken[s] && tier->dev_slot_expert[s] < 0) best = s;
+    if (best < 0) {
+      for (int s = 0; s < ns; ++s) {
+        const int h = tier->dev_slot_expert[s];
+        if (taken[s] || h < 0 || is_active[h]) continue;
+        if (best < 0 || tier->dev_slot_stamp[s] < tier->dev_slot_stamp[best]) best = s;
+      }
+    }
+    if (best < 0) { *n_install = 0; return MOE_VQ_ENOSPACE; }
+    taken[best] = true;
+    install_expert[n] = e;
+    install_slot[n] = best;
+    evict_expert[n] = tier->dev_slot_expert[best];
+    ++n;
+  }
+  *n_install = n;
+  return MOE_VQ_OK;
+}
+
+int moe_vq_tier_init(const moe_vq_layer* L, moe_vq_tier* tier, moe_vq_slot* slots, void* stream) {
+  if (!L || !dims_ok(L->hidden, L->inter, L->n_experts, L->top_k) || !tier || !slots) return MOE_VQ_EINVAL;
+  const int ns = tier->n_dev_slots, E = L->n_experts;
+  if (ns < 1 || ns > 4096 || !tier->host_pool || !tier->host_slots || !tier->dev_slot_offsets ||
+      !tier->dev_slot_expert || !tier->dev_slot_stamp || !tier->slot_mirror)
+    return MOE_VQ_EINVAL;
+  const size_t need = moe_vq_expert_bytes(MOE_VQ_FMT_MXFP4, L->hidden, L->inter) >
+                              moe_vq_expert_bytes(MOE_VQ_FMT_VQ2, L->hidden, L->inter)
+                          ? moe_vq_expert_bytes(MOE_VQ_FMT_MXFP4, L->hidden, L->inter)
+                          : moe_vq_expert_bytes(MOE_VQ_FMT_VQ2, L->hidden, L->inter);
+  for (int s = 0; s < ns; ++s) {
+    const uint64_t o = tier->dev_slot_offsets[s];
+    if ((o & 255) || o > L->pool_bytes || need > L->pool_bytes - o) return MOE_VQ_EINVAL;
+  }
+  for (int s = 0; s < ns; ++s) { tier->dev_slot_expert[s] = -1; tier->dev_slot_stamp[s] = 0; }
+  for (int e = 0; e < E; ++e) tier->slot_mirror[e] = moe_vq_slot{0, MOE_VQ_FMT_ABSENT, 0};
+  tier->step = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int r = hip_status(hipMemcpyAsync(slots, tier->slot_mirror, (size_t)E * sizeof(moe_vq_slot),
+                                    hipMemcpyHostToDevice, st));
+  if (r) return r;
+  return hip_status(hipStreamSynchronize(st));
+}
+
+int moe_vq_tier_resolve(const moe_vq_layer* L, moe_vq_tier* tier, uint8_t* pool, moe_vq_slot* slots,
+                        int n_tokens, const void* ws, void* stream, int32_t* n_installed) {
+  if (n_installed) *n_installed = 0;
+  if (!L || !dims_ok(L->hidden, L->inter, L->n_experts, L->top_k) || !tier || !pool || !slots || !ws)
+    return MOE_VQ_EINVAL;
+  if (n_tokens < 0 || n_tokens > MAX_T || !tier->slot_mirror || !tier->dev_slot_offsets || !tier->host_pool)
+    return MOE_VQ_EINVAL;
+  const int E = L->n_experts;
+  int32_t summary[4];
+  int32_t active[MAX_E];
+  int r = moe_vq_step_info(L, n_tokens, ws, summary, active, stream);  // (synchronises stream)
+  if (r) return r;
+  const int n_active = summary[2] < 0 ? 0 : (summary[2] > E ? E : summary[2]);
+  tier->step += 1;
+  for (int s = 0; s < tier->n_dev_slots; ++s) {
+    const int e = tier->dev_slot_expert[s];
+    if (e < 0) continue;
+    for (int i = 0; i < n_active; ++i)
+      if (active[i] == e) { tier->dev_slot_stamp[s] = tier->step; break; }
+  }
+  int32_t ie[MAX_E], is[MAX_E], ev[MAX_E];
+  int n = 0;
+  if ((r = moe_vq_tier_plan(tier, E, active, n_active, ie, is, ev, &n))) return r;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < n; ++i) {
+    const int e = ie[i], sl = is[i];
+    const moe_vq_slot hs = tier->host_slots[e];
+    const size_t bytes = moe_vq_expert_bytes((int)hs.format, L->hidden, L->inter);
+    const uint64_t dst = tier->dev_slot_offsets[sl];
+    if ((r = hip_status(hipMemcpyAsync(pool + dst, tier->host_pool + hs.byte_offset, bytes,
+                                       hipMemcpyHostToDevice, st))))
+      return r;
+    if (ev[i] >= 0) tier->slot_mirror[ev[i]] = moe_vq_slot{0, MOE_VQ_FMT_ABSENT, 0};
+    tier->slot_mirror[e] = moe_vq_slot{dst, hs.format, 0};
+    tier->dev_slot_expert[sl] = e;
+    tier->dev_slot_stamp[sl] = tier->step;
+    if (n_installed) *n_installed = i + 1;
+  }
+  if (n > 0 && (r = hip_status(hipMemcpyAsync(slots, tier->slot_mirror, (size_t)E * sizeof(moe_vq_slot),
+                                               hipMemcpyHostToDevice, st))))
+    return r;
+  return hip_status(hipStreamSynchronize(st));
+}
+
 const char* moe_vq_last_hip_error(void) {
   return g_last_hip_error == hipSuccess ? "" : hipGetErrorString(g_last_hip_error);
 }

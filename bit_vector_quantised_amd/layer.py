@@ -85,6 +85,64 @@ class DeviceLayer:
         self.slots.copy_(torch.from_numpy(slots.view(np.uint8).copy()))
 
 
+class TieredLayer:
+    """A layer whose experts live in a pinned host pool, with n_dev_slots device slots
+    managed by the library's expert tier (moe_vq_tier_*): the device slot table starts
+    all-absent and tiered_forward() copies the experts a step selects into device slots
+    (least recently used out).  Same interface as DeviceLayer for Step."""
+
+    def __init__(self, hidden: int, inter: int, n_experts: int, top_k: int, codebook: np.ndarray,
+                 router_w_bits: np.ndarray, experts: Callable[[int], Dict[str, np.ndarray]],
+                 formats: Sequence[int], n_dev_slots: int, device: str = "cuda"):
+        self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
+        self.device = torch.device(device)
+        host_slots, total = [], 0
+        for e in range(n_experts):
+            f = int(formats[e])
+            host_slots.append((total, f))
+            if f != _lib.FMT_ABSENT:
+                total += _lib.expert_bytes(f, hidden, inter)
+        self.host_pool = torch.empty(max(total, 256), dtype=torch.uint8, pin_memory=True)
+        for e in range(n_experts):
+            o, f = host_slots[e]
+            if f != _lib.FMT_ABSENT:
+                buf = pack_slot(experts(e), hidden, inter)
+                self.host_pool[o:o + buf.size].copy_(torch.from_numpy(buf))
+        slot_bytes = max(_lib.expert_bytes(_lib.FMT_VQ2, hidden, inter), _lib.expert_bytes(_lib.FMT_MXFP4, hidden, inter))
+        slot_bytes = (slot_bytes + 255) // 256 * 256
+        self.pool_bytes = slot_bytes * n_dev_slots
+        self.pool = torch.empty(self.pool_bytes, dtype=torch.uint8, device=self.device)
+        self.slots = torch.zeros(n_experts * 16, dtype=torch.uint8, device=self.device)
+        self.router_w = torch.from_numpy(np.ascontiguousarray(router_w_bits).view(np.int16)).to(self.device)
+        self.codebook = torch.from_numpy(np.ascontiguousarray(codebook).view(np.int16)).to(self.device)
+        self.c = _lib.Layer(hidden, inter, n_experts, top_k, self.router_w.data_ptr(), self.codebook.data_ptr(),
+                            self.pool.data_ptr(), self.pool_bytes, self.slots.data_ptr())
+        self.tier = _lib.ExpertTier(n_experts, self.host_pool.data_ptr(), host_slots,
+                                    [s * slot_bytes for s in range(n_dev_slots)])
+        _lib.tier_init(self.c, self.tier, self.slots.data_ptr(), torch.cuda.current_stream(self.device).cuda_stream)
+
+    @classmethod
+    def from_synth(cls, syn, n_dev_slots: int, device: str = "cuda", formats: Optional[Sequence[int]] = None):
+        cfg = syn.cfg
+        fm = syn.formats if formats is None else formats
+        return cls(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, syn.codebook, syn.router_w,
+                   syn.expert, fm, n_dev_slots, device)
+
+
+def tiered_forward(step: "Step", layer: TieredLayer, x: torch.Tensor):
+    """route -> copy the missing experts -> (route again) -> FC1 -> FC2.  Returns
+    (y view [T, H], number of experts copied)."""
+    T = x.shape[0]
+    step.route(x)
+    n = _lib.tier_resolve(layer.c, layer.tier, layer.pool.data_ptr(), layer.slots.data_ptr(), T,
+                          step.ws.data_ptr(), step.stream())
+    if n:
+        step.route(x)
+    step.fc1(T)
+    step.fc2(T)
+    return step.y[:T], n
+
+
 def x_dtype_code(x: torch.Tensor) -> int:
     if x.dtype == torch.bfloat16:
         return _lib.BF16

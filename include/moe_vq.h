@@ -166,6 +166,57 @@ int moe_vq_check(const void *ws, void *stream, int32_t *info);
 int moe_vq_step_info(const moe_vq_layer *layer, int n_tokens, const void *ws, int32_t summary[4],
                      int32_t *experts, void *stream);
 
+/* ---- Host-RAM expert tier.  Experts can live in a pinned host pool, with the device
+ * pool holding only some of them: a GPU cache of the experts in use in front of the rest
+ * (Tandem-vLLM 0.2.0 announcement, "How it works").  When a step selects an expert that
+ * is not resident, its slot is copied into a device slot (evicting the least recently
+ * used expert that the step does not select) and the step is run again; the result is
+ * bit-identical to a run with every expert resident, since the kernels read the same
+ * bytes.  All tier state is caller-owned host memory; the library allocates nothing. */
+typedef struct moe_vq_tier {
+  const uint8_t *host_pool;          /* [host] every expert's slot, pinned (hipHostMalloc) for
+                                        asynchronous copies; the slot layout of the device pool */
+  const moe_vq_slot *host_slots;     /* [host] [E] expert -> offset in host_pool and format
+                                        (MOE_VQ_FMT_ABSENT: not available, never installed)     */
+  int32_t n_dev_slots;               /* device slots the tier manages, 1..4096                  */
+  const uint64_t *dev_slot_offsets;  /* [host] [n_dev_slots] offsets in the device pool,
+                                        multiples of 256, each with room for the largest expert */
+  int32_t *dev_slot_expert;          /* [host] [n_dev_slots] state: expert held, -1 = free      */
+  uint64_t *dev_slot_stamp;          /* [host] [n_dev_slots] state: last step that used it       */
+  moe_vq_slot *slot_mirror;          /* [host] [E] state: the device slot table's contents      */
+  uint64_t step;                     /* state: steps resolved so far                            */
+} moe_vq_tier;
+
+/* [host] Start a tier: every device slot free, every expert absent.  Writes the device
+ * slot table slots[E] (the array layer->slots points to) to all-absent and synchronises
+ * stream.  Errors: MOE_VQ_EINVAL for a null pointer, a bad size or a device slot offset
+ * that is not a multiple of 256 or leaves no room for the largest expert in the pool. */
+int moe_vq_tier_init(const moe_vq_layer *layer, moe_vq_tier *tier, moe_vq_slot *slots, void *stream);
+
+/* [host] The tier's decision for one step, without side effects.  active[0..n_active) are
+ * the step's distinct experts.  Each active expert that is not resident and is available
+ * in the host pool gets a device slot: a free slot first (lowest index), else the slot
+ * of the least recently used expert that is not active (oldest stamp, then lowest
+ * index).  On return install_expert[i], install_slot[i] and evict_expert[i] (-1 if the
+ * slot was free), i < *n_install, list the copies in that order.  Arrays have room for
+ * n_active entries.  Returns MOE_VQ_ENOSPACE (nothing listed) if the step selects more
+ * experts than the tier has device slots for, MOE_VQ_EINVAL for bad arguments. */
+int moe_vq_tier_plan(const moe_vq_tier *tier, int n_experts, const int32_t *active, int n_active,
+                     int32_t *install_expert, int32_t *install_slot, int32_t *evict_expert,
+                     int *n_install);
+
+/* [host] Resolve the misses of the step last routed on ws: synchronise stream, read the
+ * step's distinct experts from ws, mark the resident ones as used, then copy every
+ * planned expert slot from tier->host_pool into the device pool (asynchronous on
+ * stream) and update slots[E] and the tier state.  Synchronises stream before it
+ * returns.  *n_installed (may be NULL) receives the number of experts copied; if it is
+ * not 0 the step must be routed again (moe_vq_route_topk) before FC1.  pool and slots
+ * are the writable device buffers behind layer->pool and layer->slots.  Errors: as
+ * moe_vq_tier_plan, and MOE_VQ_EHIP if a copy fails (the tier state is then updated
+ * only for the copies issued before it). */
+int moe_vq_tier_resolve(const moe_vq_layer *layer, moe_vq_tier *tier, uint8_t *pool, moe_vq_slot *slots,
+                        int n_tokens, const void *ws, void *stream, int32_t *n_installed);
+
 /* [host] Text of the last HIP runtime error seen by a call of this library on the
  * calling thread (the reason behind MOE_VQ_EHIP), or "" if none. */
 const char *moe_vq_last_hip_error(void);
