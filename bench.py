@@ -166,6 +166,54 @@ def cpu_baseline(syn, x_pool_np, top_k, budget_s=15.0, tokens_per_call=None):
                       f"host has {len(os.sched_getaffinity(0))} usable cores"}
 
 
+def bench_tier(args, cfg, syn, x_pool, n_batches):
+    """Decode steps with every expert in a pinned host pool and args.tier_slots device
+    slots: route, copy the missing experts over PCIe (least recently used out), route
+    again, FC1, FC2.  Prints one JSON line; the copies are inside the timed region."""
+    import torch
+    from bit_vector_quantised_amd import _lib
+    from bit_vector_quantised_amd.layer import Step, TieredLayer, tiered_forward
+
+    T = cfg.n_tokens
+    print(f"[bench] tier: {args.tier_slots} device slots of {cfg.n_experts} experts", file=sys.stderr, flush=True)
+    tl = TieredLayer.from_synth(syn, n_dev_slots=args.tier_slots)
+    st = Step(tl, T)
+    fmts = [int(f) for f in syn.formats]
+
+    def one(i):
+        xb = x_pool[(i % n_batches) * T:(i % n_batches + 1) * T]
+        before = set(tl.tier.held())
+        _, n = tiered_forward(st, tl, xb)
+        new = set(tl.tier.held()) - before
+        return n, sum(_lib.expert_bytes(fmts[e], cfg.hidden, cfg.inter) for e in new if e >= 0)
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    copied = nbytes = 0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        n, b = one(args.warmup + i)
+        copied += n
+        nbytes += b
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    status, info = st.check()
+    if status != _lib.OK:
+        raise RuntimeError(f"tier step status {status} ({_lib.strerror(status)}), expert {info}")
+    ms = dt / args.steps * 1e3
+    print(json.dumps({
+        "metric": "MoE-VQ layer tokens/s, experts in host RAM behind a device-slot tier (PCIe-inclusive)",
+        "value": T * args.steps / dt, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16/fp32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} with a host-RAM tier", "tokens_per_step": T,
+                   "n_experts": cfg.n_experts, "device_slots": args.tier_slots},
+        "tier": {"experts_copied_per_step": copied / args.steps, "h2d_bytes_per_step": nbytes / args.steps,
+                 "h2d_GBps": nbytes / dt / 1e9},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +224,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--traffic-from", default=None)
+    ap.add_argument("--tier-slots", type=int, default=0,
+                    help="experts in pinned host RAM, this many device slots (host-RAM tier; "
+                         "PCIe-inclusive, not the headline)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.traffic_from, args.config)
@@ -209,6 +260,8 @@ def main():
     n_batches = n_pool // T
     step = Step(dev, T)
     stream = torch.cuda.current_stream()
+    if args.tier_slots:
+        return bench_tier(args, cfg, syn_dev, x_pool, n_batches)
 
     def run_step(i, ev=None):
         xb = x_pool[(i % n_batches) * T:(i % n_batches + 1) * T]
