@@ -19,8 +19,12 @@ PAYLOAD_KEYS = {
 }
 
 
-def pack_slot(expert: Dict[str, np.ndarray], hidden: int, inter: int) -> np.ndarray:
-    """The bytes of one expert slot (layout of include/moe_vq.h, offsets from the library)."""
+def pack_slot(expert: Dict[str, np.ndarray], hidden: int, inter: int, fmt: Optional[int] = None) -> np.ndarray:
+    """The bytes of one expert slot (layout of include/moe_vq.h, offsets from the library).
+    fmt, when given, is the format the slot table will state; arrays of another format
+    are refused (they would fill only part of the slot)."""
+    if fmt is not None and int(fmt) != int(expert["format"]):
+        raise ValueError(f"expert arrays are format {int(expert['format'])}, slot format is {int(fmt)}")
     fmt = int(expert["format"])
     offs = _lib.slot_layout(fmt, hidden, inter)
     buf = np.zeros(offs[6], dtype=np.uint8)
@@ -56,7 +60,7 @@ class DeviceLayer:
             f = int(formats[e])
             if f == _lib.FMT_ABSENT:
                 continue
-            buf = pack_slot(experts(e), hidden, inter)
+            buf = pack_slot(experts(e), hidden, inter, f)
             o = int(offsets[e])
             self.pool[o:o + buf.size].copy_(torch.from_numpy(buf))
         slots = np.zeros(n_experts, dtype=[("byte_offset", "<u8"), ("format", "<u4"), ("reserved", "<u4")])
@@ -75,7 +79,7 @@ class DeviceLayer:
         cfg = syn.cfg
         fm = syn.formats if formats is None else formats
         return cls(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, syn.codebook, syn.router_w,
-                   syn.expert, fm, device)
+                   lambda e: syn.expert_as(e, fm[e]), fm, device)
 
     def set_slots(self, offsets: np.ndarray, formats: Sequence[int]) -> None:
         """Rewrite the slot table (e.g. to mark experts absent)."""
@@ -106,7 +110,7 @@ class TieredLayer:
         for e in range(n_experts):
             o, f = host_slots[e]
             if f != _lib.FMT_ABSENT:
-                buf = pack_slot(experts(e), hidden, inter)
+                buf = pack_slot(experts(e), hidden, inter, f)
                 self.host_pool[o:o + buf.size].copy_(torch.from_numpy(buf))
         slot_bytes = max(_lib.expert_bytes(_lib.FMT_VQ2, hidden, inter), _lib.expert_bytes(_lib.FMT_MXFP4, hidden, inter))
         slot_bytes = (slot_bytes + 255) // 256 * 256
@@ -126,7 +130,7 @@ class TieredLayer:
         cfg = syn.cfg
         fm = syn.formats if formats is None else formats
         return cls(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, syn.codebook, syn.router_w,
-                   syn.expert, fm, n_dev_slots, device)
+                   lambda e: syn.expert_as(e, fm[e]), fm, n_dev_slots, device)
 
 
 def tiered_forward(step: "Step", layer: TieredLayer, x: torch.Tensor):

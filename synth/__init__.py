@@ -207,6 +207,12 @@ class SynthLayer:
             self._cache[e] = a
         return a
 
+    def expert_as(self, e: int, fmt: int) -> Dict[str, np.ndarray]:
+        """Expert e stored in format fmt (its drawn format when fmt matches it)."""
+        if int(fmt) == int(self.formats[e]):
+            return self.expert(e)
+        return draw_expert(self.cfg, e, int(fmt), self.seed)
+
     def x(self, n: Optional[int] = None, stream: int = 0) -> np.ndarray:
         return draw_x(self.cfg, n, stream, self.router_w, self.seed)
 

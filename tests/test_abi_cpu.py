@@ -82,6 +82,21 @@ def test_packed_slot_reads_back(fmt):
         assert np.array_equal(back[key].view(np.uint8), np.asarray(val).view(np.uint8)), key
 
 
+def test_pack_slot_refuses_arrays_of_another_format():
+    # arrays of one format packed under another slot format would fill only part of
+    # the slot; the builder must refuse, and draw the expert in the slot's format instead
+    cfg = synth.PRESETS["tiny"]
+    ex = synth.draw_expert(cfg, 1, synth.FMT_VQ2)
+    with pytest.raises(ValueError):
+        pack_slot(ex, cfg.hidden, cfg.inter, synth.FMT_MXFP4)
+    syn = synth.SynthLayer(cfg)
+    for fmt in (synth.FMT_VQ2, synth.FMT_MXFP4):
+        e = 1
+        got = syn.expert_as(e, fmt)
+        assert int(got["format"]) == fmt
+        assert pack_slot(got, cfg.hidden, cfg.inter, fmt).size == _lib.expert_bytes(fmt, cfg.hidden, cfg.inter)
+
+
 def fake_layer(H=256, I=128, E=8, k=2, pool=1 << 20):
     # pointer values are never dereferenced by the paths exercised here
     return _lib.Layer(H, I, E, k, 0x10000, 0x20000, 0x100000, pool, 0x30000)
