@@ -29,6 +29,8 @@
 //    chunk ahead; used for the shapes the tile kernel does not cover.
 #include "fc_common.h"
 
+#include <type_traits>
+
 namespace mvq {
 
 constexpr int LB_VQ = 14;   // 16-byte code loads in flight per lane (VQ2 tiles)
@@ -57,6 +59,27 @@ struct VqBuf {
   uint4 q[TileGeom<CPL, MT, FC1>::RPL][TileGeom<CPL, MT, FC1>::NM][CPL];
   uint32_t s[TileGeom<CPL, MT, FC1>::RPL][TileGeom<CPL, MT, FC1>::NM][CPL];
 };
+
+// The loads of one (row, chunk) of a VQ2 tile: both matrices' 16 code bytes and scale.
+template <int CPL, int MT, bool FC1>
+__device__ __forceinline__ void issue_vq_chunk(VqBuf<CPL, MT, FC1>& b, const FcArgs& a, const RecS& r, int rb,
+                                               int NROWS, int wave, int rg, int sub, int rr, int j) {
+  using G = TileGeom<CPL, MT, FC1>;
+  constexpr int K = 1024 * CPL;
+  const uint8_t* slot = a.pool + r.slot_off;
+  const uint8_t* qb0 = slot + (FC1 ? a.vq2.q_gate : a.vq2.q_down);
+  const uint8_t* qb1 = slot + a.vq2.q_up;
+  const uint8_t* sb0 = slot + (FC1 ? a.vq2.s_gate : a.vq2.s_down);
+  const uint8_t* sb1 = slot + a.vq2.s_up;
+  const int n = min(rb * G::ROWS + rr * 16 + wave * 4 + rg, NROWS - 1);
+  const uint32_t qo = (uint32_t)n * (K / 4) + (uint32_t)sub * 16;
+  const uint32_t so = (uint32_t)n * (K / 64) + (uint32_t)(sub >> 1) * 2;
+#pragma unroll
+  for (int m = 0; m < G::NM; ++m) {
+    b.q[rr][m][j] = *reinterpret_cast<const uint4*>((m == 0 ? qb0 : qb1) + qo + j * 256);
+    b.s[rr][m][j] = *reinterpret_cast<const uint16_t*>((m == 0 ? sb0 : sb1) + so + j * 16);
+  }
+}
 
 template <int CPL, int MT, bool FC1>
 __device__ __forceinline__ void issue_vq(VqBuf<CPL, MT, FC1>& b, const FcArgs& a, const RecS& r, int rb,
@@ -217,8 +240,15 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
     }
   };
 
-  // VQ2 tile from a filled buffer.
-  auto compute_vq = [&](const VqBuf<CPL, MT, FC1>& b, const RecS& r, int rb) __attribute__((always_inline)) {
+  // VQ2 tile from a filled buffer.  With PF, the next tile's loads (record rn2, row
+  // block rbn, into nb) are issued one (row, chunk) at a time, each after the same
+  // (row, chunk) of this tile has been decoded: issuing a whole tile at once holds the
+  // wave until the memory pipeline has taken every load, which at one or two tiles per
+  // workgroup left the decode waiting until nearly all the data had arrived.  The two
+  // forms are separate code so that each keeps exact load counts in its waits.
+  auto compute_vq = [&](const VqBuf<CPL, MT, FC1>& b, const RecS& r, int rb, auto pf, VqBuf<CPL, MT, FC1>& nb,
+                        const RecS& rn2, int rbn) __attribute__((always_inline)) {
+    constexpr bool PF = decltype(pf)::value;
     // one base register plus immediate offsets for the factor reads (constant
     // addresses would each be held in a register across the tile loop)
     const float* xscb = xsc + opaque(0);
@@ -256,6 +286,7 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
               acc[m][rr][t] = fmaf(f16_bits_to_f32(b.s[rr][m][j]) * f, pr[m], acc[m][rr][t]);
           }
         }
+        if constexpr (PF) issue_vq_chunk(nb, a, rn2, rbn, NROWS, wave, rg, sub, rr, j);
       }
     finish(acc, r, rb);
   };
@@ -353,9 +384,9 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
     // prefetch only between VQ2 tiles of the same token group (an MXFP4 tile uses the
     // register budget of both buffers itself)
     const bool prefetch = more && same && rn.fmt == MOE_VQ_FMT_VQ2 && rc.fmt == MOE_VQ_FMT_VQ2;
-    if (prefetch) issue_vq(nxt, a, rn, tn % RB, NROWS, wave, rg, sub);
     const RecS rnn = (tn + 1 < t_end) ? load_rec(a.rec, (tn + 1) / RB) : rn;
-    if (rc.fmt == MOE_VQ_FMT_VQ2) compute_vq(cur, rc, t % RB);
+    if (prefetch) compute_vq(cur, rc, t % RB, std::true_type{}, nxt, rn, tn % RB);
+    else if (rc.fmt == MOE_VQ_FMT_VQ2) compute_vq(cur, rc, t % RB, std::false_type{}, nxt, rn, tn % RB);
     else compute_mx(rc, t % RB);
     if (!more) return false;
     if (!same) {

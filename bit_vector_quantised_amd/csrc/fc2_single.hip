@@ -6,158 +6,164 @@
 // (vLLM-Moet README, "What we changed against official vLLM", row "MoE at decode").
 //
 // With one token the k routed experts all write the same output rows.  A workgroup here
-// owns a block of output rows and walks every expert for them: it stages all k pairs' h
-// once (fp16, one power-of-two factor per pair and 1024 columns, as the other FC2
-// kernels do), issues every VQ2 code load of its rows up front, and adds w_i times each
-// expert's partial dot product in registers, in the worklist's expert order.  The 16
-// lanes of a row are reduced once, at the end, and y is written directly: no per-pair
-// outputs and no separate combine launch.  Seven waves of four rows give 28 rows per
-// workgroup, so H = 7168 is 256 workgroups, one per CU.
+// owns a block of 28 output rows and has one wave per routed expert.  Lane (c, r) of a
+// wave takes the 64-column chunk c of every r-th row of the block: it holds that chunk
+// of its pair's h in registers (fp16, with the power-of-two factor of its 1024-column
+// slice, as the other FC2 kernels scale h), issues the code loads of all its rows up
+// front, and decodes them against the same registers, so h is read once per lane and
+// never from LDS.  Each row's partial products are summed over the chunk lanes with
+// DPP and then over the experts, in the worklist's expert order, through a small LDS
+// array; y is written directly: no per-pair outputs and no separate combine launch.
+// H = 7168 is 256 workgroups, one per CU.
 #include "fc_common.h"
 
 namespace mvq {
 
-constexpr int F2S_WAVES = 7;
-constexpr int F2S_THREADS = 64 * F2S_WAVES;
-constexpr int F2S_ROWS = 4 * F2S_WAVES;  // 16 lanes per row, 4 rows per wave
-constexpr int F2S_KMAX = 8;              // routed experts per token this kernel takes
+constexpr int F2S_KMAX = 8;                 // routed experts per token this kernel takes
+constexpr int F2S_THREADS = 64 * F2S_KMAX;  // one wave per routed expert
+constexpr int F2S_ROWS = 28;                // output rows per workgroup
+constexpr int F2S_AHEAD = 4;                // rows of codes in flight ahead of the decode
 
 template <int CPL>
 __global__ __launch_bounds__(F2S_THREADS, 1) void fc2_single_kernel(FcArgs a) {
   constexpr int K = 1024 * CPL;
-  constexpr int KS = CPL;                      // activation slices of 1024 columns
-  constexpr int XT = (K / 64) * XCHUNK_UNITS;  // padded 16-byte units per pair
-  constexpr int NGS = F2S_KMAX * KS;           // (pair, slice) units to stage, at most
-  constexpr int GSW = (NGS + F2S_WAVES - 1) / F2S_WAVES;  // of them per wave, at most
+  constexpr int NCH = K / 64;           // 64-column chunks per row: lanes per row
+  constexpr int RGW = 64 / NCH;         // row groups per wave
+  constexpr int RPL = F2S_ROWS / RGW;   // rows per lane
+  constexpr int MXP = RPL > 7 ? 7 : RPL;  // MXFP4 rows loaded per pass
+  static_assert(F2S_ROWS % RGW == 0, "rows per workgroup");
   __shared__ uint2 tab[256 * TAB_COPIES];
-  __shared__ uint4 xs[F2S_KMAX * XT];
-  __shared__ float xsc[NGS];
+  __shared__ float red[F2S_KMAX][F2S_ROWS];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int rg = lane >> 4, sub = lane & 15;
+  const int tid = threadIdx.x, g = tid >> 6, lane = tid & 63;
+  const int c = lane % NCH, rgi = lane / NCH;
   const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
-  const int n_raw = blockIdx.x * F2S_ROWS + wave * 4 + rg;
-  const int n = min(n_raw, a.H - 1);  // rows past the end re-read the last row, written never
+  const int row0 = blockIdx.x * F2S_ROWS;
 
   const uint2 cbv = reinterpret_cast<const uint2*>(a.codebook)[tid & 127];
+  // this wave's record, read together with the header rather than after it (record
+  // min(g, max_groups - 1) lies in the record array whatever the header says); nothing
+  // read from it is used before the header check has passed
+  const int4* rp = reinterpret_cast<const int4*>(a.rec + (g < a.max_groups ? g : a.max_groups - 1));
+  const int4 w0 = rp[0], w1 = rp[1];
   if (!ws_ok(a, false, 1)) return;
   const int G = (int)a.hdr[HDR_GROUPS2];  // one group per routed pair
   if (G > F2S_KMAX) return;               // (the launcher takes this kernel only for k <= 8)
+  const bool live = g < G;
+  const uint64_t slot_off = ((uint64_t)(uint32_t)uni(w0.y) << 32) | (uint32_t)uni(w0.x);
+  const uint32_t fmt = live ? (uint32_t)uni(w1.x) : (uint32_t)MOE_VQ_FMT_ABSENT;
+  const int p = live ? uni(w1.z) : 0;  // the pair (only pair[0] of a one-token group)
+  const uint8_t* slot = a.pool + slot_off;
 
-  // the routed pairs, in the worklist's expert order
-  RecS rec[F2S_KMAX];
+  // ---- this lane's chunk of h, then every VQ2 code load of its rows
+  float4 hv[16];
+  if (live) {
+    const float4* src = reinterpret_cast<const float4*>(a.h_in + (size_t)p * K + c * 64);
 #pragma unroll
-  for (int g = 0; g < F2S_KMAX; ++g) rec[g] = load_rec(a.rec, g < G ? g : 0);
-
-  // ---- h of this wave's (pair, slice) units: issued before the code loads, which are
-  // the bulk of the traffic
-  float4 hv[GSW][4];
+    for (int i = 0; i < 16; ++i) hv[i] = src[i];
+  }
+  // Only the first F2S_AHEAD rows' codes are issued before the barrier: issuing them all
+  // would hold the wave until the memory pipeline had taken every load, so that the
+  // decode could start only once nearly all the data had arrived.  The other rows are
+  // issued in the decode loop, each F2S_AHEAD rows ahead of the row being decoded.
+  uint4 q[RPL];
+  uint32_t s[RPL];
+  const uint8_t* qb = slot + a.vq2.q_down + c * 16;
+  const uint8_t* sb = slot + a.vq2.s_down + (c >> 1) * 2;
+  auto load_row = [&](int i) __attribute__((always_inline)) {
+    // rows past the end re-read the last row; their sums are never written
+    const int n = min(row0 + rgi + RGW * i, a.H - 1);
+    q[i] = *reinterpret_cast<const uint4*>(qb + (size_t)n * (K / 4));
+    s[i] = *reinterpret_cast<const uint16_t*>(sb + (size_t)n * (K / 64));
+  };
+  if (fmt == MOE_VQ_FMT_VQ2) {
 #pragma unroll
-  for (int i = 0; i < GSW; ++i) {
-    const int gs = wave + i * F2S_WAVES;
-    if (gs < G * KS) {
-      const int g = gs / KS, sl = gs % KS;
-      int p = rec[0].pair[0];
-#pragma unroll
-      for (int gg = 1; gg < F2S_KMAX; ++gg) p = g == gg ? rec[gg].pair[0] : p;
-      const float4* row = reinterpret_cast<const float4*>(a.h_in + (size_t)p * K + sl * SLICE);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hv[i][r] = row[r * 64 + lane];
-    }
+    for (int i = 0; i < F2S_AHEAD && i < RPL; ++i) load_row(i);
   }
 
-  // ---- every VQ2 code load of this lane's row, for all experts
-  uint4 q[F2S_KMAX][CPL];
-  uint32_t s[F2S_KMAX][CPL];
+  // ---- h to fp16 with one power-of-two factor per 1024-column slice (16 chunk lanes)
+  uint32_t xw[32];
+  float xsc = 1.f;
+  if (live) {
+    float m = 0.f;
 #pragma unroll
-  for (int g = 0; g < F2S_KMAX; ++g) {
-    if (g < G && rec[g].fmt == MOE_VQ_FMT_VQ2) {
-      const uint8_t* slot = a.pool + rec[g].slot_off;
-      const uint8_t* qb = slot + a.vq2.q_down + (size_t)n * (K / 4) + sub * 16;
-      const uint8_t* sb = slot + a.vq2.s_down + (size_t)n * (K / 64) + (sub >> 1) * 2;
+    for (int i = 0; i < 16; ++i)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)), fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
+    m = fmaxf(m, dpp_f32<dpp::QUAD_XOR1>(m));
+    m = fmaxf(m, dpp_f32<dpp::QUAD_XOR2>(m));
+    m = fmaxf(m, dpp_f32<dpp::ROW_HALF_MIRROR>(m));
+    m = fmaxf(m, dpp_f32<dpp::ROW_MIRROR>(m));
+    int ex = 0;
+    if (m > 0.f && m < INFINITY) ex = frexp_exponent(m) - 15;
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        q[g][j] = *reinterpret_cast<const uint4*>(qb + j * 256);
-        s[g][j] = *reinterpret_cast<const uint16_t*>(sb + j * 16);
-      }
+    for (int i = 0; i < 16; ++i) {
+      xw[2 * i] = pack_half2(ldexp2(hv[i].x, -ex), ldexp2(hv[i].y, -ex));
+      xw[2 * i + 1] = pack_half2(ldexp2(hv[i].z, -ex), ldexp2(hv[i].w, -ex));
     }
-  }
-
-  // ---- stage h: fp16 with one power-of-two factor per (pair, slice); one wave per unit
-#pragma unroll
-  for (int i = 0; i < GSW; ++i) {
-    const int gs = wave + i * F2S_WAVES;
-    if (gs < G * KS) {
-      const int g = gs / KS, sl = gs % KS;
-      float m = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(hv[i][r].x), fabsf(hv[i][r].y)), fmaxf(fabsf(hv[i][r].z), fabsf(hv[i][r].w))));
-      m = wave_max(m);
-      int ex = 0;
-      if (m > 0.f && m < INFINITY) ex = frexp_exponent(m) - 15;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float4 v = hv[i][r];
-        const int f = r * 64 + lane;          // float4 index within the slice
-        const int u = sl * (SLICE / 8) + (f >> 1);  // 16-byte unit within the pair
-        reinterpret_cast<uint2*>(xs)[(g * XT + x_unit(u)) * 2 + (f & 1)] =
-            make_uint2(pack_half2(ldexp2(v.x, -ex), ldexp2(v.y, -ex)), pack_half2(ldexp2(v.z, -ex), ldexp2(v.w, -ex)));
-      }
-      if (lane == 0) xsc[gs] = ldexp2(1.0f, ex);
-    }
+    xsc = ldexp2(1.0f, ex);
   }
   if (tid < 256) write_table_entry(tab, cbv, tid);
   __syncthreads();
 
-  // ---- every expert's product for this row, weighted, summed in expert order
-  float acc = 0.f;
+  // ---- this lane's rows against its chunk
+  const float w = live ? a.pair_w[p] : 0.f;
+  float acc[RPL];
 #pragma unroll
-  for (int g = 0; g < F2S_KMAX; ++g) {
-    if (g < G) {
-      const RecS& r = rec[g];
-      const float w = a.pair_w[r.pair[0]];
-      if (r.fmt == MOE_VQ_FMT_VQ2) {
+  for (int i = 0; i < RPL; ++i) acc[i] = 0.f;
+  if (fmt == MOE_VQ_FMT_VQ2) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const uint4* xp = xs + g * XT + (sub + 16 * j) * XCHUNK_UNITS;
-          float pr = 0.f;
+    for (int i = 0; i < RPL; ++i) {
+      if (i + F2S_AHEAD < RPL) load_row(i + F2S_AHEAD);
+      float pr = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 xr[2] = {xp[2 * i], xp[2 * i + 1]};
-            pr = vq2_dword_dot(tab, dword_of(q[g][j], i), laneoff, reinterpret_cast<const uint32_t*>(xr), pr);
-          }
-          acc = fmaf(w * f16_bits_to_f32(s[g][j]) * xsc[g * KS + j], pr, acc);
-        }
-      } else if (r.fmt == MOE_VQ_FMT_MXFP4) {
-        // MXFP4 experts (not in flight ahead): 2 * CPL chunks of 32 weights per lane
-        const uint8_t* slot = a.pool + r.slot_off;
-        const uint8_t* qb = slot + a.mx4.q_down + (size_t)n * (K / 2);
-        const uint8_t* eb = slot + a.mx4.s_down + (size_t)n * (K / 32);
-        uint4 qm[2 * CPL];
-        uint32_t em[2 * CPL];
+      for (int d = 0; d < 4; ++d) pr = vq2_dword_dot(tab, dword_of(q[i], d), laneoff, xw + 8 * d, pr);
+      acc[i] = (w * f16_bits_to_f32(s[i]) * xsc) * pr;
+    }
+  } else if (fmt == MOE_VQ_FMT_MXFP4) {
+    // two 32-weight blocks per row and lane, MXP rows per pass
+    const uint8_t* qb = slot + a.mx4.q_down + c * 32;
+    const uint8_t* eb = slot + a.mx4.s_down + c * 2;
 #pragma unroll
-        for (int j = 0; j < 2 * CPL; ++j) {
-          const int c = sub + 16 * j;
-          qm[j] = *reinterpret_cast<const uint4*>(qb + c * 16);
-          em[j] = eb[c];
-        }
+    for (int i0 = 0; i0 < RPL; i0 += MXP) {
+      uint4 qm[MXP][2];
+      uint32_t em[MXP];
 #pragma unroll
-        for (int j = 0; j < 2 * CPL; ++j) {
-          const int c = sub + 16 * j;
-          const uint4* xp = xs + g * XT + (c >> 1) * XCHUNK_UNITS + (c & 1) * 4;
-          uint4 xr[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) xr[i] = xp[i];
-          const float pr = mx4_chunk_dot(qm[j], reinterpret_cast<const uint32_t*>(xr));
-          acc = fmaf(w * e8m0_to_f32(em[j]) * xsc[g * KS + (c >> 5)], pr, acc);
+      for (int ii = 0; ii < MXP; ++ii) {
+        const int n = min(row0 + rgi + RGW * (i0 + ii), a.H - 1);
+        if (i0 + ii < RPL) {
+          qm[ii][0] = *reinterpret_cast<const uint4*>(qb + (size_t)n * (K / 2));
+          qm[ii][1] = *reinterpret_cast<const uint4*>(qb + (size_t)n * (K / 2) + 16);
+          em[ii] = *reinterpret_cast<const uint16_t*>(eb + (size_t)n * (K / 32));
         }
       }
-      // (an absent expert adds nothing; the worklist has recorded MOE_VQ_ENOTRESIDENT)
+#pragma unroll
+      for (int ii = 0; ii < MXP; ++ii) {
+        if (i0 + ii < RPL) {
+          const float p0 = mx4_chunk_dot(qm[ii][0], xw);
+          const float p1 = mx4_chunk_dot(qm[ii][1], xw + 16);
+          float v = (w * e8m0_to_f32(em[ii] & 0xFF) * xsc) * p0;
+          acc[i0 + ii] = fmaf(w * e8m0_to_f32(em[ii] >> 8) * xsc, p1, v);
+        }
+      }
     }
   }
-  acc = group_sum<16>(acc);
-  if (sub == 0 && n_raw < a.H) a.y[n_raw] = acc;
+  // (an absent expert adds nothing; the worklist has recorded MOE_VQ_ENOTRESIDENT)
+
+  // ---- each row: sum over its chunk lanes, then over the experts in order
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    float v = group_sum<16>(acc[i]);
+    if (NCH == 32) v += __shfl_xor(v, 16);
+    if (c == 0) red[g][rgi + RGW * i] = v;
+  }
+  __syncthreads();
+  if (tid < F2S_ROWS && row0 + tid < a.H) {
+    float y = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < F2S_KMAX; ++gg)
+      if (gg < G) y += red[gg][tid];
+    a.y[row0 + tid] = y;
+  }
 }
 
 // y for a one-token step straight from the experts (K = 1024 or 2048, k <= 8); *done

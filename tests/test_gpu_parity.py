@@ -298,6 +298,26 @@ def test_mini_mixed_formats(mini):
         compare(v, x, "bf16", g, MINI.top_k)
 
 
+def test_mini_one_token_absent_expert(mini):
+    """One token at K = 1024 (the one-token FC2 kernel): a selected expert absent is
+    reported and its contribution left out, the other three added."""
+    syn, _ = mini
+    x = syn.x(n=1, stream=77)
+    x64 = oracle.x_value(x, "bf16")
+    ids = oracle.topk(oracle.router_logits(syn.router_w, x64), MINI.top_k)[0]
+    gone = int(ids[2])
+    fm = list(syn.formats)
+    fm[gone] = synth.FMT_ABSENT
+    v, dev = tiny_variant(syn, formats=fm)
+    g = run(dev, x, "bf16")
+    assert g["status"] == _lib.ENOTRESIDENT and g["info"] == gone
+    r = oracle.forward(syn, x64, MINI.top_k, forced_selection=g["ids"])
+    keep = (g["ids"] != gone)[:, :, None]
+    y_ref = (r["w"][:, :, None] * r["o"] * keep).sum(axis=1)
+    err = np.abs(g["y"] - y_ref).max(axis=1) / np.abs(y_ref).max(axis=1)
+    assert err.max() <= 1e-2
+
+
 def test_mini_fp32_activations(mini):
     syn, dev = mini
     x = oracle.x_value(syn.x(n=3, stream=50), "bf16").astype(np.float32) * np.float32(1.37)
@@ -331,6 +351,16 @@ def test_wide_experts_split_into_token_groups():
     g = run(dev, x, "bf16")
     assert g["status"] == _lib.OK
     compare(v, x, "bf16", g, WIDE.top_k)
+    # one-token steps (their own FC2 kernel, K = 2048, six of its eight expert waves idle)
+    chosen = set()
+    for st in range(100, 104):
+        x = syn.x(n=1, stream=st)
+        say(f"wide step T=1 stream {st}, mixed formats")
+        g = run(dev, x, "bf16")
+        assert g["status"] == _lib.OK
+        compare(v, x, "bf16", g, WIDE.top_k)
+        chosen |= set(int(e) for e in g["ids"].ravel())
+    assert chosen & {0, 2} and chosen & {1, 3}  # both formats went through it
 
 
 # ---------------------------------------------------------------------------------
