@@ -55,12 +55,16 @@ __global__ __launch_bounds__(F2S_THREADS, 1) void fc2_single_kernel(FcArgs a) {
   const int p = live ? uni(w1.z) : 0;  // the pair (only pair[0] of a one-token group)
   const uint8_t* slot = a.pool + slot_off;
 
-  // ---- this lane's chunk of h, then every VQ2 code load of its rows
-  float4 hv[16];
+  // ---- this lane's chunk of h, then the first rows' code loads.  At K = 2048 lanes c and
+  // c + 32 take the same chunk: each loads one half of it, and the halves are exchanged
+  // after the fp16 conversion (h is read once per workgroup, not twice).
+  constexpr int HV = NCH == 32 ? 8 : 16;  // float4 of h this lane loads
+  float4 hv[HV];
   if (live) {
-    const float4* src = reinterpret_cast<const float4*>(a.h_in + (size_t)p * K + c * 64);
+    const int half = NCH == 32 ? lane >> 5 : 0;
+    const float4* src = reinterpret_cast<const float4*>(a.h_in + (size_t)p * K + c * 64 + half * 32);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) hv[i] = src[i];
+    for (int i = 0; i < HV; ++i) hv[i] = src[i];
   }
   // Only the first F2S_AHEAD rows' codes are issued before the barrier: issuing them all
   // would hold the wave until the memory pipeline had taken every load, so that the
@@ -87,18 +91,37 @@ __global__ __launch_bounds__(F2S_THREADS, 1) void fc2_single_kernel(FcArgs a) {
   if (live) {
     float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < HV; ++i)
       m = fmaxf(m, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)), fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
     m = fmaxf(m, dpp_f32<dpp::QUAD_XOR1>(m));
     m = fmaxf(m, dpp_f32<dpp::QUAD_XOR2>(m));
     m = fmaxf(m, dpp_f32<dpp::ROW_HALF_MIRROR>(m));
     m = fmaxf(m, dpp_f32<dpp::ROW_MIRROR>(m));
+    if constexpr (NCH == 32) {
+      // v_permlane32_swap of a value with itself gives {lanes 0..31's value, lanes
+      // 32..63's value} in every lane pair (l, l + 32): here the two halves' maxima
+      const auto mm = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m),
+                                                       __builtin_bit_cast(uint32_t, m), false, false);
+      m = fmaxf(__builtin_bit_cast(float, (uint32_t)mm[0]), __builtin_bit_cast(float, (uint32_t)mm[1]));
+    }
     int ex = 0;
     if (m > 0.f && m < INFINITY) ex = frexp_exponent(m) - 15;
+    uint32_t own[2 * HV];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      xw[2 * i] = pack_half2(ldexp2(hv[i].x, -ex), ldexp2(hv[i].y, -ex));
-      xw[2 * i + 1] = pack_half2(ldexp2(hv[i].z, -ex), ldexp2(hv[i].w, -ex));
+    for (int i = 0; i < HV; ++i) {
+      own[2 * i] = pack_half2(ldexp2(hv[i].x, -ex), ldexp2(hv[i].y, -ex));
+      own[2 * i + 1] = pack_half2(ldexp2(hv[i].z, -ex), ldexp2(hv[i].w, -ex));
+    }
+    if constexpr (NCH == 32) {
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        const auto r = __builtin_amdgcn_permlane32_swap(own[d], own[d], false, false);
+        xw[d] = r[0];       // first half of the chunk (lane c's)
+        xw[16 + d] = r[1];  // second half (lane c + 32's)
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 32; ++d) xw[d] = own[d];
     }
     xsc = ldexp2(1.0f, ex);
   }
