@@ -360,7 +360,8 @@ def main():
                            "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
                            "kernel": "moe_vq_prefill_gemm (prefill_fc_kernel FC1 + FC2, grouped fp16 MFMA)",
                            "flops_per_launch": flops, "mean_launch_us": pf_s * 1e6}
-        out["prefill"] = {"ms": pf_s * 1e3, "code_bytes_per_step": step_b}
+        out["prefill"] = {"ms": pf_s * 1e3, "code_bytes_per_step": step_b,
+                          "ms_p10_p90": [float(np.percentile(fc1_ms, q)) for q in (10, 90)]}
     else:
         out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
@@ -368,7 +369,9 @@ def main():
                            + " FC1 (gate/up code decode + SiLU*up)",
                            "bytes_per_launch": fc1_b, "mean_launch_us": fc1_avg_s * 1e6}
         out["code_stream"] = {"GBps": code_stream, "frac": code_stream / HBM_PEAK_GBPS,
-                              "fc1_us": fc1_avg_s * 1e6, "fc2_us": fc2_avg_s * 1e6, "bytes_per_step": step_b}
+                              "fc1_us": fc1_avg_s * 1e6, "fc2_us": fc2_avg_s * 1e6, "bytes_per_step": step_b,
+                              "fc1_us_p10_p90": [float(np.percentile(fc1_ms, q)) * 1e3 for q in (10, 90)],
+                              "fc2_us_p10_p90": [float(np.percentile(fc2_ms, q)) * 1e3 for q in (10, 90)]}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         syn_or = synth.SynthLayer(cfg)
