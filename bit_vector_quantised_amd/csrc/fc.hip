@@ -364,8 +364,10 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
 
   // ---- prologue: first tile's record, its code loads, activations and the table
   int t = t_begin;
-  RecS rc = load_rec(a.rec, t / RB);
-  RecS rn = (t + 1 < t_end) ? load_rec(a.rec, (t + 1) / RB) : rc;
+  const RecRaw raw_c = load_rec_raw(a.rec, t / RB);
+  const RecRaw raw_n = load_rec_raw(a.rec, (t + 1 < t_end ? t + 1 : t) / RB);
+  RecS rc = rec_from_raw(raw_c);
+  RecS rn = rec_from_raw(raw_n);
   VqBuf<CPL, MT, FC1> A, B;
   {
     const StageRegs g = stage_load(rc);

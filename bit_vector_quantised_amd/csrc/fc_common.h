@@ -65,10 +65,11 @@ __device__ __forceinline__ float mx4_chunk_dot(const uint4& q, const uint32_t* x
   return p;
 }
 
+// All four header words are read before any is tested (one round trip, not four).
 __device__ __forceinline__ bool ws_ok(const FcArgs& a, bool fc1, int MT) {
-  return a.hdr[HDR_KEY] == a.key && a.hdr[HDR_N_ACTIVE] <= (uint32_t)a.E &&
-         a.hdr[fc1 ? HDR_GROUPS1 : HDR_GROUPS2] <= (uint32_t)a.max_groups &&
-         a.hdr[fc1 ? HDR_MT1 : HDR_MT2] == (uint32_t)MT;
+  const uint32_t key = a.hdr[HDR_KEY], n_active = a.hdr[HDR_N_ACTIVE];
+  const uint32_t groups = a.hdr[fc1 ? HDR_GROUPS1 : HDR_GROUPS2], mt = a.hdr[fc1 ? HDR_MT1 : HDR_MT2];
+  return (key == a.key) & (n_active <= (uint32_t)a.E) & (groups <= (uint32_t)a.max_groups) & (mt == (uint32_t)MT);
 }
 
 // The fields of a GroupRec a tile needs, held in scalar registers (uniform per workgroup).
@@ -103,6 +104,30 @@ __device__ __forceinline__ uint32_t reg_copy(uint32_t v) {
 
 static_assert(offsetof(GroupRec, p0) == 8 && offsetof(GroupRec, mcount) == 12 && offsetof(GroupRec, fmt) == 16 &&
               offsetof(GroupRec, pair) == 24, "GroupRec layout");
+
+// A record's two 16-byte words as loaded, and the fields taken from them; loading two
+// records before taking either lets their loads overlap.
+struct RecRaw {
+  int4 w0, w1, w2;
+};
+
+__device__ __forceinline__ RecRaw load_rec_raw(const GroupRec* recs, int g) {
+  const int4* p = reinterpret_cast<const int4*>(recs + g);
+  return RecRaw{p[0], p[1], p[2]};
+}
+
+__device__ __forceinline__ RecS rec_from_raw(const RecRaw& raw) {
+  RecS r;
+  r.slot_off = ((uint64_t)(uint32_t)uni(raw.w0.y) << 32) | (uint32_t)uni(raw.w0.x);
+  r.p0 = uni(raw.w0.z);
+  r.mcount = uni(raw.w0.w);
+  r.fmt = (uint32_t)uni(raw.w1.x);
+  static_assert(MAX_MT == 4, "pair indices span words 1 and 2");
+  const int pw[MAX_MT] = {raw.w1.z, raw.w1.w, raw.w2.x, raw.w2.y};
+#pragma unroll
+  for (int j = 0; j < MAX_MT; ++j) r.pair[j] = uni(pw[j]);
+  return r;
+}
 
 __device__ __forceinline__ RecS load_rec(const GroupRec* recs, int g) {
   const int4* p = reinterpret_cast<const int4*>(recs + g);

@@ -569,8 +569,10 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 
   // ---- prologue
   int t = t_begin;
-  RecS rc = load_rec(a.rec, t / RB);
-  RecS rn = (t + 1 < t_end) ? load_rec(a.rec, (t + 1) / RB) : rc;
+  const RecRaw raw_c = load_rec_raw(a.rec, t / RB);
+  const RecRaw raw_n = load_rec_raw(a.rec, (t + 1 < t_end ? t + 1 : t) / RB);
+  RecS rc = rec_from_raw(raw_c);
+  RecS rn = rec_from_raw(raw_n);
   {
     const Tok t0 = tok_load(rc);
     act_load(t0, rc);
