@@ -128,6 +128,10 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
   const int RB = (NROWS + ROWS - 1) / ROWS;
 
   const uint2 cbv = reinterpret_cast<const uint2*>(a.codebook)[tid & 127];
+  // The kernel arguments span five scalar-cache lines; the activation pointers' line and
+  // the grid size (a hidden argument) are read here, with the header, rather than first
+  // where they are used, behind a miss.
+  asm volatile("" ::"s"(FC1 ? a.x_h : (const uint16_t*)a.h_in), "s"(gridDim.x));
   if (!ws_ok(a, FC1, MT)) return;
   const int n_tiles = (int)a.hdr[FC1 ? HDR_GROUPS1 : HDR_GROUPS2] * RB;
   // a contiguous run of tiles per workgroup: consecutive tiles share the token group

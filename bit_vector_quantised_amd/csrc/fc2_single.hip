@@ -46,6 +46,10 @@ __global__ __launch_bounds__(F2S_THREADS, 1) void fc2_single_kernel(FcArgs a) {
   // read from it is used before the header check has passed
   const int4* rp = reinterpret_cast<const int4*>(a.rec + (g < a.max_groups ? g : a.max_groups - 1));
   const int4 w0 = rp[0], w1 = rp[1];
+  // The kernel arguments span five scalar-cache lines: the ones holding h, the routing
+  // weights and the down matrices' offsets are read here, with the header, rather than
+  // first where they are used, behind a miss.
+  asm volatile("" ::"s"(a.h_in), "s"(a.vq2.s_down));
   if (!ws_ok(a, false, 1)) return;
   const int G = (int)a.hdr[HDR_GROUPS2];  // one group per routed pair
   if (G > F2S_KMAX) return;               // (the launcher takes this kernel only for k <= 8)

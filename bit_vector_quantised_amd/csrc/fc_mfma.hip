@@ -139,6 +139,9 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   auto gid = [&](int gi) __attribute__((always_inline)) -> int { return (ODD && gi == NGQ - 1) ? gone : gpair + gi; };
 
   const uint2 cbv = reinterpret_cast<const uint2*>(a.codebook)[tid & 127];
+  // The kernel arguments span five scalar-cache lines: the activation and output
+  // pointers', the MXFP4 offsets' and the grid size's are read here with the header.
+  asm volatile("" ::"s"(FC1 ? a.x_h : (const uint16_t*)a.h_in), "s"(a.mx4.s_down), "s"(gridDim.x));
   if (!ws_ok(a, FC1, MF_MT)) return;
   const int n_tiles = (int)a.hdr[FC1 ? HDR_GROUPS1 : HDR_GROUPS2] * RB;
   const int t_begin = (int)(((long)blockIdx.x * n_tiles) / gridDim.x);

@@ -235,6 +235,7 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
 
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
+  asm volatile("" ::"s"(a.logits), "s"(a.pair_w));  // both argument lines at the start
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.T) return;
@@ -262,6 +263,8 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   __shared__ int r_start[MAX_E], r_tot[MAX_E], r_gs1[MAX_E], r_gs2[MAX_E], r_expert[MAX_E];
   __shared__ uint32_t r_fmt[MAX_E];
   __shared__ uint64_t r_off[MAX_E];
+  // all four scalar-cache lines of the arguments read at the start, together
+  asm volatile("" ::"s"(ra.logits), "s"(a.slots), "s"(a.hdr), "s"(a.rec1));
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int E = a.E, T = a.T, k = a.k;
   // the slot of expert tid is read first, so that its latency overlaps the top-k
@@ -512,6 +515,8 @@ constexpr int RS_MAX_T = 64;  // token blocks of 16, at most four
 
 __global__ __launch_bounds__(256) void router_mfma_small_kernel(RouteArgs a) {
   __shared__ float red[4][RS_MAX_T / 16][16][17];
+  // the argument lines and the grid size (a hidden argument) read at the start together
+  asm volatile("" ::"s"(a.x_h), "s"(a.pair_w), "s"(gridDim.x));
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, kq = lane >> 4;
   const int e0 = blockIdx.x * RS_EXPERTS, s = blockIdx.y;
@@ -570,6 +575,9 @@ __global__ __launch_bounds__(256) void router_mfma_small_kernel(RouteArgs a) {
 // with a few memory round trips instead of a 1024-thread workgroup's phases.
 template <int NPL>
 __global__ __launch_bounds__(64) void worklist_one_kernel(RouteArgs ra, WorklistArgs a) {
+  // The two argument structs span four scalar-cache lines; all are read here, at the
+  // start, rather than each first where it is used (after the top-k), behind a miss.
+  asm volatile("" ::"s"(ra.logits), "s"(a.slots), "s"(a.hdr), "s"(a.rec1));
   const int lane = threadIdx.x;
   const int k = a.k;
   // every expert's slot is read before the top-k (expert lane + 64 i in lane's entry i),
