@@ -22,7 +22,7 @@ namespace mvq {
 constexpr int F2S_KMAX = 8;                 // routed experts per token this kernel takes
 constexpr int F2S_THREADS = 64 * F2S_KMAX;  // one wave per routed expert
 constexpr int F2S_ROWS = 28;                // output rows per workgroup
-constexpr int F2S_AHEAD = 4;                // rows of codes in flight ahead of the decode
+constexpr int F2S_AHEAD = 3;                // rows of codes in flight ahead of the decode
 
 template <int CPL>
 __global__ __launch_bounds__(F2S_THREADS, 1) void fc2_single_kernel(FcArgs a) {
