@@ -446,10 +446,16 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   };
   auto compute_mx = [&](const RecS& r, int rb) __attribute__((always_inline)) {
     const MfAddr d = vq_addr(r, rb);
-    constexpr int NH = G::MXG;
+    // Groups load in passes of NH.  Where the register budget holds two or more groups,
+    // the passes are one group each in two buffers, and the loads of pass h + 1 are
+    // issued before pass h is decoded, so that they arrive while it decodes (buffers of
+    // two groups each spill at K = 7168).
+    constexpr bool DB = G::MXG >= 2;
+    constexpr int NH = DB ? 1 : G::MXG;
     constexpr int NPASS = (NGQ + NH - 1) / NH;
-    MfMx mx[NH][NM][NB];
+    MfMx mx[DB ? 2 : 1][NH][NM][NB];
     auto mx_load = [&](int h) __attribute__((always_inline)) {
+      const int b = DB ? (h & 1) : 0;
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
         const int gi = h * NH + j;
@@ -459,14 +465,17 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
               const uint32_t g = (uint32_t)gid(gi);
-              mx[j][m][nb].q = *reinterpret_cast<const uint4*>(d.qb[m] + (uint32_t)(d.qo[nb] - d.dq0 + g * 64));
-              mx[j][m][nb].e = d.sb[m][(uint32_t)(d.so[nb] - d.ds0 + g * 4 + pq)];
+              mx[b][j][m][nb].q = *reinterpret_cast<const uint4*>(d.qb[m] + (uint32_t)(d.qo[nb] - d.dq0 + g * 64));
+              mx[b][j][m][nb].e = d.sb[m][(uint32_t)(d.so[nb] - d.ds0 + g * 4 + pq)];
             }
       }
     };
+    if (DB) mx_load(0);
 #pragma unroll
     for (int h = 0; h < NPASS; ++h) {
-      mx_load(h);
+      if (!DB) mx_load(h);
+      else if (h + 1 < NPASS) mx_load(h + 1);
+      const int b = DB ? (h & 1) : 0;
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
         const int gi = h * NH + j;
@@ -474,7 +483,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) mx_unit(gi, mx[j][m][nb].q, mx[j][m][nb].e, m, nb);
+          for (int nb = 0; nb < NB; ++nb) mx_unit(gi, mx[b][j][m][nb].q, mx[b][j][m][nb].e, m, nb);
       }
     }
   };
