@@ -447,10 +447,10 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   auto compute_mx = [&](const RecS& r, int rb) __attribute__((always_inline)) {
     const MfAddr d = vq_addr(r, rb);
     // Groups load in passes of NH.  Where the register budget holds two or more groups,
-    // the passes are one group each in two buffers, and the loads of pass h + 1 are
-    // issued before pass h is decoded, so that they arrive while it decodes (buffers of
-    // two groups each spill at K = 7168).
-    constexpr bool DB = G::MXG >= 2;
+    // and in FC2, the passes are one group each in two buffers, and the loads of pass
+    // h + 1 are issued before pass h is decoded, so that they arrive while it decodes
+    // (buffers of two groups each spill at K = 7168).
+    constexpr bool DB = (G::MXG >= 2 || !FC1) && NGQ >= 2;
     constexpr int NH = DB ? 1 : G::MXG;
     constexpr int NPASS = (NGQ + NH - 1) / NH;
     MfMx mx[DB ? 2 : 1][NH][NM][NB];
