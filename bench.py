@@ -1,6 +1,7 @@
 """Benchmark of the MoE-VQ routed-expert step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b1|b32|b8mx] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b1|b32|b8mx|p4096]
+                    [--no-b32] [--no-cpu-baseline]
     python bench.py --copy-probe                 # plain device copy of known size (counter scale)
     python bench.py --traffic-from DIR [--config C]   # counter CSVs -> profiles/traffic_fc1_C.json
 
@@ -10,14 +11,19 @@ activations already sit in HBM.  The default workload is decode batch 1 of a
 DeepSeek-style layer (H=7168, I=2048, 256 experts, top-8, VQ2 experts at 2.125
 bits/weight, all resident in one HBM slot pool).  Tokens are cycled from a pool of
 256 distinct pre-drawn tokens so consecutive steps touch different experts (the
-256 MB Infinity Cache holds about two steps' experts, not the pool).
+256 MB Infinity Cache holds about two steps' experts, not the pool).  The metric
+names batch 1 and batch 32: the default run measures batch 32 (Zipf(1.1) expert
+popularity) the same way and reports it as the "b32" block of the same line.
 
 Prints one JSON line.  `value` is tokens/s of K steps timed on the host between two
 device synchronisations, with nothing else on the stream.  The same K steps then run
 again with HIP events recorded on the launch stream around FC1 and FC2 (each event
-costs the device a few microseconds, so they stay out of the throughput region);
+costs the device a few microseconds, so they stay out of the throughput region), each
+step preceded by a 512 MiB read that evicts the memory-side cache;
 `roofline` rates the dominant kernel (FC1) by its algorithmic code+scale bytes per
-launch over the mean duration those events measure.
+launch over the median duration those events measure (mean, p10 and p90 beside it).
+An event pair also counts the launch's dispatch, so the event duration exceeds the
+kernel's own run time in a rocprofv3 trace by about the dispatch latency.
 
 `roofline.traffic` is the FC1 kernel's HBM traffic per launch as the hardware
 counters saw it: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc
@@ -214,32 +220,13 @@ def bench_tier(args, cfg, syn, x_pool, n_batches):
     }))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="b1", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--traffic-from", default=None)
-    ap.add_argument("--tier-slots", type=int, default=0,
-                    help="experts in pinned host RAM, this many device slots (host-RAM tier; "
-                         "PCIe-inclusive, not the headline)")
-    args = ap.parse_args()
-    if args.traffic_from:
-        traffic_from(args.traffic_from, args.config)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the routed-expert step is measured on a single MI355X).", file=sys.stderr)
-        sys.exit(2)
+SCRUB_BYTES = 512 << 20
 
-    if args.copy_probe:
-        copy_probe()
-        return
 
+def measure(args, config, with_events=True):
+    """Build one configuration's layer, run warmup, the throughput region (K steps back
+    to back) and, with_events, the kernel-timing pass.  Returns the per-config block of
+    the JSON line (value, ms_per_step, roofline, code_stream or prefill)."""
     import numpy as np
     import torch
 
@@ -247,13 +234,12 @@ def main():
     from bit_vector_quantised_amd import _lib
     from bit_vector_quantised_amd.layer import DeviceLayer, Step
 
-    torch.cuda.set_device(0)
-    cfg = synth.PRESETS[args.config]
+    cfg = synth.PRESETS[config]
     T, k = cfg.n_tokens, cfg.top_k
-    print(f"[bench] building {args.config} layer ({cfg.n_experts} experts)", file=sys.stderr, flush=True)
+    print(f"[bench] building {config} layer ({cfg.n_experts} experts)", file=sys.stderr, flush=True)
     syn_dev = synth.SynthLayer(cfg, cache=False)
     dev = DeviceLayer.from_synth(syn_dev)
-    prefill = args.config in PREFILL
+    prefill = config in PREFILL
     n_pool = 256 if T == 1 else (max(8, 256 // T) * T if T <= 256 else 2 * T)
     x_pool_np = synth.SynthLayer(cfg, cache=False).x(n=n_pool, stream=7)
     x_pool = torch.from_numpy(x_pool_np.view(np.int16)).cuda().view(torch.bfloat16)
@@ -274,14 +260,14 @@ def main():
                 ev[1].record(stream)
                 ev[2].record(stream)
             return
-        step.fc1(T)
+        step.fc1(xb)
         if ev is not None:
             ev[1].record(stream)
         step.fc2(T)
         if ev is not None:
             ev[2].record(stream)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] {config}: warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         run_step(i)
     torch.cuda.synchronize()
@@ -300,85 +286,153 @@ def main():
     torch.cuda.synchronize()
 
     # throughput: K steps, nothing but the step on the stream
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {config}: timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         run_step(args.warmup + i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    # kernel durations: the same K steps with HIP events around FC1 and FC2
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    print(f"[bench] kernel timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        run_step(args.warmup + i, events[i])
-    torch.cuda.synchronize()
-    fc1_ms = [events[i][0].elapsed_time(events[i][1]) for i in range(args.steps)]
-    fc2_ms = [events[i][1].elapsed_time(events[i][2]) for i in range(args.steps)]
     bidx = [(args.warmup + i) % n_batches for i in range(args.steps)]
     fc1_b = float(np.mean([fc1_bytes[b] for b in bidx]))
     step_b = float(np.mean([step_bytes[b] for b in bidx]))
-    fc1_avg_s = float(np.mean(fc1_ms)) * 1e-3
-    fc2_avg_s = float(np.mean(fc2_ms)) * 1e-3
-    achieved = fc1_b / fc1_avg_s / 1e9
-    code_stream = step_b / (fc1_avg_s + fc2_avg_s) / 1e9
+    out = {"value": args.steps * T / dt, "unit": "tokens/s", "ms_per_step": dt * 1e3 / args.steps,
+           "workload": WORKLOADS[config], "tokens_per_step": T,
+           "unique_experts_per_step": float(np.mean([uniq[b] for b in bidx]))}
+    if not with_events:
+        return out, dev, syn_dev, x_pool_np
 
+    # kernel durations: the same K steps with HIP events around FC1 and FC2, on the
+    # launch stream, each step after a 512 MiB read that evicts the 256 MB memory-side
+    # cache (so the experts come from HBM: the cold case).  The scrub only reads: a
+    # read-modify-write would leave dirty lines whose write-back competes with FC1.
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] {config}: kernel timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        scrub.sum()
+        run_step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    del scrub
+    fc1_ms = np.array([events[i][0].elapsed_time(events[i][1]) for i in range(args.steps)])
+    fc2_ms = np.array([events[i][1].elapsed_time(events[i][2]) for i in range(args.steps)])
+    fc1_med = float(np.median(fc1_ms)) * 1e-3
+    fc2_med = float(np.median(fc2_ms)) * 1e-3
+
+    def spread(ms):
+        return {"median_us": float(np.median(ms)) * 1e3, "mean_us": float(np.mean(ms)) * 1e3,
+                "p10_us": float(np.percentile(ms, 10)) * 1e3, "p90_us": float(np.percentile(ms, 90)) * 1e3}
+
+    if prefill:
+        # FC1 + FC2 as grouped MFMA GEMMs: 2 * 3 * H * I flops per routed pair
+        flops = 2.0 * 3 * cfg.hidden * cfg.inter * T * k
+        tflops = flops / fc1_med / 1e12  # the events bracket the whole prefill call
+        out["dtype"] = "fp16 MFMA (decoded weights x fp16-staged activations), fp32 accumulate"
+        out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                           "kernel": "moe_vq_prefill_gemm (prefill_fc_kernel FC1 + FC2, grouped fp16 MFMA)",
+                           "flops_per_launch": flops, "launch_us": spread(fc1_ms)}
+        out["prefill"] = {"code_bytes_per_step": step_b}
+        return out, dev, syn_dev, x_pool_np
+
+    achieved = fc1_b / fc1_med / 1e9
+    code_stream = step_b / (fc1_med + fc2_med) / 1e9
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_fc1_{args.config}.json")
+    tfile = os.path.join(ROOT, "profiles", f"traffic_fc1_{config}.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("source_hash") == source_hash():
             traffic = tr.get("bytes_per_launch")
+    out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                       "kernel": ("fc_stream_kernel" if T <= 1 else "fc_mfma_kernel")
+                       + " FC1 (gate/up code decode + SiLU*up)",
+                       "bytes_per_launch": fc1_b, "launch_us": spread(fc1_ms),
+                       "timing": "HIP events on the launch stream around the launch, median over the "
+                                 "timed steps, memory-side cache evicted by a 512 MiB read before each step"}
+    out["code_stream"] = {"GBps": code_stream, "frac": code_stream / HBM_PEAK_GBPS, "bytes_per_step": step_b,
+                          "fc1": spread(fc1_ms), "fc2": spread(fc2_ms)}
+    return out, dev, syn_dev, x_pool_np
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="b1", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-b32", action="store_true", help="with the default config, skip the batch-32 block")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--traffic-from", default=None)
+    ap.add_argument("--tier-slots", type=int, default=0,
+                    help="experts in pinned host RAM, this many device slots (host-RAM tier; "
+                         "PCIe-inclusive, not the headline)")
+    args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from, args.config)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the routed-expert step is measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import torch
+
+    import synth
+
+    torch.cuda.set_device(0)
+    res = measure(args, args.config)
+    if res is None:  # (the host-RAM tier mode printed its own line)
+        return
+    main_block, dev, syn_dev, x_pool_np = res
+    cfg = synth.PRESETS[args.config]
     out = {
         "metric": "MoE-VQ layer tokens/s and code-stream HBM GB/s (% peak), batch 1 & 32",
-        "value": args.steps * T / dt,
+        "value": main_block["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": dt * 1e3 / args.steps,
+        "ms_per_step": main_block["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16xfp16->fp32 (decoded VQ2 weights x fp16-staged activations, fp32 accumulate)",
+        "dtype": main_block.get("dtype", "fp16xfp16->fp32 (decoded VQ2 weights x fp16-staged activations, "
+                                         "fp32 accumulate)"),
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "tokens_per_step": T, "hidden": cfg.hidden,
-                   "inter": cfg.inter, "n_experts": cfg.n_experts, "top_k": k,
-                   "unique_experts_per_step": float(np.mean([uniq[b] for b in bidx])),
+        "config": {"workload": WORKLOADS[args.config], "tokens_per_step": cfg.n_tokens, "hidden": cfg.hidden,
+                   "inter": cfg.inter, "n_experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "unique_experts_per_step": main_block["unique_experts_per_step"],
                    "parallelism": "single GPU"},
+        "roofline": main_block["roofline"],
     }
-    if prefill:
-        # FC1 + FC2 as grouped MFMA GEMMs: 2 * 3 * H * I flops per routed pair
-        flops = 2.0 * 3 * cfg.hidden * cfg.inter * T * k
-        pf_s = fc1_avg_s  # the events bracket the whole prefill call (stage, GEMMs, combine)
-        tflops = flops / pf_s / 1e12
-        out["dtype"] = "fp16 MFMA (decoded weights x fp16-staged activations), fp32 accumulate"
-        out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
-                           "kernel": "moe_vq_prefill_gemm (prefill_fc_kernel FC1 + FC2, grouped fp16 MFMA)",
-                           "flops_per_launch": flops, "mean_launch_us": pf_s * 1e6}
-        out["prefill"] = {"ms": pf_s * 1e3, "code_bytes_per_step": step_b,
-                          "ms_p10_p90": [float(np.percentile(fc1_ms, q)) for q in (10, 90)]}
-    else:
-        out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                           "kernel": ("fc_stream_kernel" if T <= 1 else "fc_mfma_kernel")
-                           + " FC1 (gate/up code decode + SiLU*up)",
-                           "bytes_per_launch": fc1_b, "mean_launch_us": fc1_avg_s * 1e6}
-        out["code_stream"] = {"GBps": code_stream, "frac": code_stream / HBM_PEAK_GBPS,
-                              "fc1_us": fc1_avg_s * 1e6, "fc2_us": fc2_avg_s * 1e6, "bytes_per_step": step_b,
-                              "fc1_us_p10_p90": [float(np.percentile(fc1_ms, q)) * 1e3 for q in (10, 90)],
-                              "fc2_us_p10_p90": [float(np.percentile(fc2_ms, q)) * 1e3 for q in (10, 90)]}
+    for key in ("code_stream", "prefill"):
+        if key in main_block:
+            out[key] = main_block[key]
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         syn_or = synth.SynthLayer(cfg)
-        out["cpu_baseline"] = cpu_baseline(syn_or, x_pool_np, k, args.cpu_budget,
-                                           tokens_per_call=8 if prefill else None)
+        out["cpu_baseline"] = cpu_baseline(syn_or, x_pool_np, cfg.top_k, args.cpu_budget,
+                                           tokens_per_call=8 if args.config in PREFILL else None)
     else:
         out["cpu_baseline"] = None
+    del dev
+    torch.cuda.empty_cache()
+    # the metric's second batch size, in the same line
+    if args.config == "b1" and not args.no_b32:
+        b32, dev32, _, _ = measure(args, "b32")
+        out["b32"] = {k: b32[k] for k in ("value", "unit", "ms_per_step", "workload", "tokens_per_step",
+                                           "unique_experts_per_step", "roofline", "code_stream")}
+        del dev32
+        torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

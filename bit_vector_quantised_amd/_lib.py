@@ -19,7 +19,7 @@ FMT_ABSENT, FMT_VQ2, FMT_MXFP4 = 0, 1, 2
 MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 
 EXPORTS = ("moe_vq_expert_bytes", "moe_vq_slot_layout", "moe_vq_workspace_bytes", "moe_vq_route_topk",
-           "moe_vq_fc1_silu", "moe_vq_fc2_combine", "moe_vq_prefill_gemm", "moe_vq_decode_expert",
+           "moe_vq_fc1_silu", "moe_vq_fc2_combine", "moe_vq_forward", "moe_vq_prefill_gemm", "moe_vq_decode_expert",
            "moe_vq_check", "moe_vq_step_info", "moe_vq_tier_init", "moe_vq_tier_plan", "moe_vq_tier_resolve",
            "moe_vq_last_hip_error", "moe_vq_strerror")
 
@@ -68,8 +68,9 @@ def _load():
         "moe_vq_slot_layout": (i32, [i32, i32, i32, ctypes.POINTER(ctypes.c_uint64)]),
         "moe_vq_workspace_bytes": (sz, [LP, i32]),
         "moe_vq_route_topk": (i32, [LP, vp, i32, i32, vp, vp, vp, sz, vp]),
-        "moe_vq_fc1_silu": (i32, [LP, i32, vp, sz, vp, vp]),
+        "moe_vq_fc1_silu": (i32, [LP, vp, i32, i32, vp, sz, vp, vp]),
         "moe_vq_fc2_combine": (i32, [LP, vp, i32, vp, sz, vp, vp]),
+        "moe_vq_forward": (i32, [LP, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "moe_vq_prefill_gemm": (i32, [LP, vp, i32, i32, vp, sz, vp, vp]),
         "moe_vq_decode_expert": (i32, [LP, i32, i32, i32, vp, vp, vp]),
         "moe_vq_check": (i32, [vp, vp, ctypes.POINTER(ctypes.c_int32)]),
@@ -125,12 +126,19 @@ def route_topk(layer: Layer, x: int, x_dtype: int, n_tokens: int, topk_ids: int,
                                stream), "route_topk")
 
 
-def fc1_silu(layer: Layer, n_tokens: int, ws: int, ws_bytes: int, h: int, stream: int = 0) -> None:
-    _ok(_lib.moe_vq_fc1_silu(ctypes.byref(layer), n_tokens, ws, ws_bytes, h, stream), "fc1_silu")
+def fc1_silu(layer: Layer, x: int, x_dtype: int, n_tokens: int, ws: int, ws_bytes: int, h: int,
+             stream: int = 0) -> None:
+    _ok(_lib.moe_vq_fc1_silu(ctypes.byref(layer), x, x_dtype, n_tokens, ws, ws_bytes, h, stream), "fc1_silu")
 
 
 def fc2_combine(layer: Layer, h: int, n_tokens: int, ws: int, ws_bytes: int, y: int, stream: int = 0) -> None:
     _ok(_lib.moe_vq_fc2_combine(ctypes.byref(layer), h, n_tokens, ws, ws_bytes, y, stream), "fc2_combine")
+
+
+def forward(layer: Layer, x: int, x_dtype: int, n_tokens: int, topk_ids: int, topk_w: int, h: int, y: int,
+            ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _ok(_lib.moe_vq_forward(ctypes.byref(layer), x, x_dtype, n_tokens, topk_ids, topk_w, h, y, ws, ws_bytes,
+                            stream), "forward")
 
 
 def prefill_gemm(layer: Layer, x: int, x_dtype: int, n_tokens: int, ws: int, ws_bytes: int, y: int,

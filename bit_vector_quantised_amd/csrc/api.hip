@@ -64,7 +64,7 @@ FcArgs make_fc_args(const moe_vq_layer* L, int T, void* ws, const WsLayout& W, b
   FcArgs a{};
   a.pool = L->pool;
   a.codebook = static_cast<const uint16_t*>(L->codebook);
-  a.hdr = at<const uint32_t>(ws, W.hdr);
+  a.hdr = at<uint32_t>(ws, W.hdr);
   a.act_start = at<const int32_t>(ws, W.act_start);
   a.act_off = at<const uint64_t>(ws, W.act_off);
   a.act_fmt = at<const uint32_t>(ws, W.act_fmt);
@@ -84,6 +84,88 @@ FcArgs make_fc_args(const moe_vq_layer* L, int T, void* ws, const WsLayout& W, b
   a.vq2 = slot_layout(MOE_VQ_FMT_VQ2, L->hidden, L->inter);
   a.mx4 = slot_layout(MOE_VQ_FMT_MXFP4, L->hidden, L->inter);
   return a;
+}
+
+// The launches of one call, after its arguments have been checked.
+hipError_t route_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, int32_t* topk_ids, float* topk_w,
+                    void* ws, hipStream_t stream) {
+  const int E = L->n_experts, H = L->hidden, I = L->inter, k = L->top_k;
+  const WsLayout W = ws_layout(E, H, I, k, T);
+  RouteArgs ra{};
+  ra.router_w = static_cast<const uint16_t*>(L->router_w);
+  ra.x = x;
+  ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.KS = W.KS;
+  ra.ksp = (W.KS + 3) & ~3;
+  ra.logits = at<float>(ws, W.logits);
+  ra.x_h = at<uint16_t>(ws, W.x_h);
+  ra.x_sc = at<float>(ws, W.x_sc);
+  ra.topk_ids = topk_ids;
+  ra.topk_w = topk_w;
+  ra.pair_w = at<float>(ws, W.pair_w);
+  WorklistArgs wa{};
+  wa.x = x;
+  wa.x_dtype = x_dtype;
+  wa.topk_ids = topk_ids;
+  wa.slots = L->slots;
+  wa.pool_bytes = L->pool_bytes;
+  wa.T = T; wa.E = E; wa.k = k; wa.H = H; wa.I = I;
+  wa.MT1 = W.MT1;
+  wa.MT2 = W.MT2;
+  wa.rec1 = at<GroupRec>(ws, W.rec1);
+  wa.rec2 = at<GroupRec>(ws, W.rec2);
+  wa.G1 = W.G1;
+  wa.G2 = W.G2;
+  wa.hdr = at<uint32_t>(ws, W.hdr);
+  wa.act_expert = at<int32_t>(ws, W.act_expert);
+  wa.act_start = at<int32_t>(ws, W.act_start);
+  wa.act_off = at<uint64_t>(ws, W.act_off);
+  wa.act_fmt = at<uint32_t>(ws, W.act_fmt);
+  wa.grp1 = at<int32_t>(ws, W.grp1);
+  wa.grp2 = at<int32_t>(ws, W.grp2);
+  wa.pair_list = at<int32_t>(ws, W.pair_list);
+  wa.key = shape_key(T, E, k, H, I);
+  return launch_route(ra, x_dtype, wa, stream);
+}
+
+hipError_t fc1_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, void* ws, float* h, hipStream_t stream) {
+  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, T);
+  FcArgs a = make_fc_args(L, T, ws, W, true);
+  a.x_addr = (uint64_t)(uintptr_t)x;
+  a.x_dtype = x_dtype;
+  a.out = h;
+  a.max_groups = W.G1;
+  return launch_fc1(a, W.MT1, W.G1, device_cu_count(), stream);
+}
+
+hipError_t fc2_on(const moe_vq_layer* L, const float* h, int T, void* ws, float* y, hipStream_t stream) {
+  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, T);
+  FcArgs a = make_fc_args(L, T, ws, W, false);
+  a.h_in = h;
+  a.out = at<float>(ws, W.o_buf);
+  a.y = y;
+  a.max_groups = W.G2;
+  return launch_fc2(a, W.MT2, W.G2, device_cu_count(), stream);
+}
+
+// Arguments of moe_vq_forward and its static-workspace variant, workspace aside.
+int check_forward(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens, const int32_t* topk_ids,
+                  const float* topk_w, const float* h, const float* y) {
+  int st = check_layer(L);
+  if (st) return st;
+  if (n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
+  if (x_dtype != MOE_VQ_F32 && x_dtype != MOE_VQ_BF16) return MOE_VQ_EINVAL;
+  if (n_tokens == 0) return MOE_VQ_OK;
+  if (!x || !topk_ids || !topk_w || !h || !y) return MOE_VQ_EINVAL;
+  if (((uintptr_t)x & 15) || ((uintptr_t)h & 15) || ((uintptr_t)y & 15)) return MOE_VQ_EINVAL;
+  return MOE_VQ_OK;
+}
+
+hipError_t forward_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, int32_t* topk_ids, float* topk_w,
+                      float* h, float* y, void* ws, hipStream_t stream) {
+  hipError_t e = route_on(L, x, x_dtype, T, topk_ids, topk_w, ws, stream);
+  if (e == hipSuccess) e = fc1_on(L, x, x_dtype, T, ws, h, stream);
+  if (e == hipSuccess) e = fc2_on(L, h, T, ws, y, stream);
+  return e;
 }
 
 }  // namespace
@@ -121,54 +203,19 @@ int moe_vq_route_topk(const moe_vq_layer* L, const void* x, int x_dtype, int n_t
   if (n_tokens == 0) return MOE_VQ_OK;
   if (!x || !topk_ids || !topk_w || ((uintptr_t)x & 15)) return MOE_VQ_EINVAL;
   if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
-  const int E = L->n_experts, H = L->hidden, I = L->inter, k = L->top_k, T = n_tokens;
-  const WsLayout W = ws_layout(E, H, I, k, T);
-  RouteArgs ra{};
-  ra.router_w = static_cast<const uint16_t*>(L->router_w);
-  ra.x = x;
-  ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.KS = W.KS;
-  ra.ksp = (W.KS + 3) & ~3;
-  ra.logits = at<float>(ws, W.logits);
-  ra.x_h = at<uint16_t>(ws, W.x_h);
-  ra.x_sc = at<float>(ws, W.x_sc);
-  ra.topk_ids = topk_ids;
-  ra.topk_w = topk_w;
-  ra.pair_w = at<float>(ws, W.pair_w);
-  WorklistArgs wa{};
-  wa.topk_ids = topk_ids;
-  wa.slots = L->slots;
-  wa.pool_bytes = L->pool_bytes;
-  wa.T = T; wa.E = E; wa.k = k; wa.H = H; wa.I = I;
-  wa.MT1 = W.MT1;
-  wa.MT2 = W.MT2;
-  wa.rec1 = at<GroupRec>(ws, W.rec1);
-  wa.rec2 = at<GroupRec>(ws, W.rec2);
-  wa.G1 = W.G1;
-  wa.G2 = W.G2;
-  wa.hdr = at<uint32_t>(ws, W.hdr);
-  wa.act_expert = at<int32_t>(ws, W.act_expert);
-  wa.act_start = at<int32_t>(ws, W.act_start);
-  wa.act_off = at<uint64_t>(ws, W.act_off);
-  wa.act_fmt = at<uint32_t>(ws, W.act_fmt);
-  wa.grp1 = at<int32_t>(ws, W.grp1);
-  wa.grp2 = at<int32_t>(ws, W.grp2);
-  wa.pair_list = at<int32_t>(ws, W.pair_list);
-  wa.key = shape_key(T, E, k, H, I);
-  return hip_status(launch_route(ra, x_dtype, wa, static_cast<hipStream_t>(stream)));
+  return hip_status(route_on(L, x, x_dtype, n_tokens, topk_ids, topk_w, ws, static_cast<hipStream_t>(stream)));
 }
 
-int moe_vq_fc1_silu(const moe_vq_layer* L, int n_tokens, void* ws, size_t ws_bytes, float* h, void* stream) {
+int moe_vq_fc1_silu(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens, void* ws, size_t ws_bytes,
+                    float* h, void* stream) {
   int st = check_layer(L);
   if (st) return st;
   if (n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
+  if (x_dtype != MOE_VQ_F32 && x_dtype != MOE_VQ_BF16) return MOE_VQ_EINVAL;
   if (n_tokens == 0) return MOE_VQ_OK;
-  if (!h || ((uintptr_t)h & 15)) return MOE_VQ_EINVAL;
+  if (!x || !h || ((uintptr_t)x & 15) || ((uintptr_t)h & 15)) return MOE_VQ_EINVAL;
   if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
-  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens);
-  FcArgs a = make_fc_args(L, n_tokens, ws, W, true);
-  a.out = h;
-  a.max_groups = W.G1;
-  return hip_status(launch_fc1(a, W.MT1, W.G1, device_cu_count(), static_cast<hipStream_t>(stream)));
+  return hip_status(fc1_on(L, x, x_dtype, n_tokens, ws, h, static_cast<hipStream_t>(stream)));
 }
 
 int moe_vq_fc2_combine(const moe_vq_layer* L, const float* h, int n_tokens, void* ws, size_t ws_bytes,
@@ -179,13 +226,15 @@ int moe_vq_fc2_combine(const moe_vq_layer* L, const float* h, int n_tokens, void
   if (n_tokens == 0) return MOE_VQ_OK;
   if (!h || !y || ((uintptr_t)h & 15) || ((uintptr_t)y & 15)) return MOE_VQ_EINVAL;
   if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
-  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens);
-  FcArgs a = make_fc_args(L, n_tokens, ws, W, false);
-  a.h_in = h;
-  a.out = at<float>(ws, W.o_buf);
-  a.y = y;
-  a.max_groups = W.G2;
-  return hip_status(launch_fc2(a, W.MT2, W.G2, device_cu_count(), static_cast<hipStream_t>(stream)));
+  return hip_status(fc2_on(L, h, n_tokens, ws, y, static_cast<hipStream_t>(stream)));
+}
+
+int moe_vq_forward(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens, int32_t* topk_ids,
+                   float* topk_w, float* h, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_forward(L, x, x_dtype, n_tokens, topk_ids, topk_w, h, y);
+  if (st || n_tokens == 0) return st;
+  if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
+  return hip_status(forward_on(L, x, x_dtype, n_tokens, topk_ids, topk_w, h, y, ws, static_cast<hipStream_t>(stream)));
 }
 
 int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens, void* ws,
@@ -202,13 +251,14 @@ int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n
   PrefillArgs a{};
   a.pool = L->pool;
   a.codebook = static_cast<const uint16_t*>(L->codebook);
-  a.hdr = at<const uint32_t>(ws, W.hdr);
+  a.hdr = at<uint32_t>(ws, W.hdr);
   a.act_start = at<const int32_t>(ws, W.act_start);
   a.act_off = at<const uint64_t>(ws, W.act_off);
   a.act_fmt = at<const uint32_t>(ws, W.act_fmt);
   a.pair_list = at<const int32_t>(ws, W.pair_list);
   a.pair_w = at<const float>(ws, W.pair_w);
   a.x = x;
+  a.x_dtype = x_dtype;
   a.x16 = at<uint16_t>(ws, W.x16);
   a.x16_e = at<int32_t>(ws, W.x16_e);
   a.mt_pre = at<int32_t>(ws, W.mt_pre);

@@ -52,7 +52,10 @@ __global__ __launch_bounds__(F2S_THREADS, 1) void fc2_single_kernel(FcArgs a) {
   asm volatile("" ::"s"(a.h_in), "s"(a.vq2.s_down));
   if (!ws_ok(a, false, 1)) return;
   const int G = (int)a.hdr[HDR_GROUPS2];  // one group per routed pair
-  if (G > F2S_KMAX) return;               // (the launcher takes this kernel only for k <= 8)
+  if (G > F2S_KMAX) {                     // (the launcher takes this kernel only for k <= 8)
+    if (blockIdx.x == 0 && tid == 0) a.hdr[HDR_STATUS] = MOE_VQ_EINVAL;
+    return;
+  }
   const bool live = g < G;
   const uint64_t slot_off = ((uint64_t)(uint32_t)uni(w0.y) << 32) | (uint32_t)uni(w0.x);
   const uint32_t fmt = live ? (uint32_t)uni(w1.x) : (uint32_t)MOE_VQ_FMT_ABSENT;

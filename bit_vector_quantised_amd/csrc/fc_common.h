@@ -65,11 +65,23 @@ __device__ __forceinline__ float mx4_chunk_dot(const uint4& q, const uint32_t* x
   return p;
 }
 
-// All four header words are read before any is tested (one round trip, not four).
+// The workspace was routed for this call: shape key, counts within their bounds, the
+// token-group size this kernel is built for, and (FC1) the same activations.  All header
+// words are read before any is tested (one round trip, not several).  A refused call
+// writes MOE_VQ_EINVAL into the status word (one lane of workgroup 0) and computes
+// nothing, so moe_vq_check() reports it: nothing is skipped silently.
 __device__ __forceinline__ bool ws_ok(const FcArgs& a, bool fc1, int MT) {
   const uint32_t key = a.hdr[HDR_KEY], n_active = a.hdr[HDR_N_ACTIVE];
   const uint32_t groups = a.hdr[fc1 ? HDR_GROUPS1 : HDR_GROUPS2], mt = a.hdr[fc1 ? HDR_MT1 : HDR_MT2];
-  return (key == a.key) & (n_active <= (uint32_t)a.E) & (groups <= (uint32_t)a.max_groups) & (mt == (uint32_t)MT);
+  const uint32_t xlo = a.hdr[HDR_X_LO], xhi = a.hdr[HDR_X_HI], xdt = a.hdr[HDR_X_DTYPE];
+  bool ok = (key == a.key) & (n_active <= (uint32_t)a.E) & (groups <= (uint32_t)a.max_groups) &
+            (mt == (uint32_t)MT);
+  if (fc1) ok = ok & x_matches(xlo, xhi, xdt, a.x_addr, a.x_dtype);
+  if (!ok && blockIdx.x == 0 && threadIdx.x == 0) {
+    a.hdr[HDR_STATUS] = MOE_VQ_EINVAL;
+    a.hdr[HDR_INFO] = 0xFFFFFFFFu;
+  }
+  return ok;
 }
 
 // The fields of a GroupRec a tile needs, held in scalar registers (uniform per workgroup).

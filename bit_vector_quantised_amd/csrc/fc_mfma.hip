@@ -18,7 +18,16 @@
 // only LDS traffic of the inner loop is the codebook lookups.  FC1 takes the staged
 // fp16 x (one power-of-two factor per token and 1024 columns, exact for bf16 x); FC2
 // converts the fp32 h of each pair to fp16 with one power-of-two factor per 128-column
-// scale group.  The factor multiplies the group's product in fp32.
+// scale group.  The factor multiplies the group's product in fp32; FC2's routing weight
+// multiplies each pair's output in fp32.
+//
+// MXFP4 B operand: a lane's 32 weights of a group are one E8M0 block.  The four blocks of
+// a 128-wide group (held by the four lanes of a row) share one product, so each block is
+// converted to fp16 with 2^(e - e_max), e_max the largest of the four exponents, and
+// 2^(e_max - 127) multiplies the group's fp32 sum.  The converted values are at most 6 in
+// magnitude (no overflow for any exponent) and exact while e >= e_max - 23; elements of a
+// block more than 23 binades below its group's largest are rounded (each is below
+// 2^-22 of that block's unit).
 //
 // B operand: a lane's code bytes of one 128-wide scale group are table lookups of signed
 // codebook vectors, which are exact fp16 values.  The group scale multiplies the group's
@@ -118,10 +127,12 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   // the pair of each token row of the current and the next token group: the outputs'
   // rows, read from LDS rather than from global memory at the end of every tile (a load
   // there would wait for every older load, i.e. for the ring in flight).
-  __shared__ __attribute__((aligned(16))) uint8_t lds[TAB_BYTES + NBUF * RED * 4 + 2 * MF_MT * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[TAB_BYTES + NBUF * RED * 4 + 2 * MF_MT * 4 * (FC1 ? 1 : 2)];
   uint2* const tab = reinterpret_cast<uint2*>(lds);
   float* const red = reinterpret_cast<float*>(lds + TAB_BYTES);
   int (*const s_pair)[MF_MT] = reinterpret_cast<int (*)[MF_MT]>(lds + TAB_BYTES + NBUF * RED * 4);
+  // FC2: the routing weight of each token row, next to its pair
+  float (*const s_w)[MF_MT] = reinterpret_cast<float (*)[MF_MT]>(lds + TAB_BYTES + NBUF * RED * 4 + 2 * MF_MT * 4);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, kq = lane >> 4;
@@ -180,7 +191,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     for (int q = 0; q < 4; ++q) t.drow[q] = FC1 ? opaque(t_in.drow[q]) : 0;
     return t;
   };
-  float hw = 0.f;  // FC2: routing weight of the pair of A row i16 (folded into h)
+  float hw = 0.f;  // FC2: routing weight of the pair of A row i16 (kept in LDS for the output)
   auto act_load = [&](const Tok& t, const RecS& r) __attribute__((always_inline)) {
     if (FC1) {
       const int tokA = t.arow / a.k;
@@ -208,22 +219,14 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
         for (int i = 0; i < 8; ++i) A32[FC1 ? 0 : gi][i] = *reinterpret_cast<const float4*>(hr + gid(gi) * 128 + 4 * i);
     }
   };
-  // FC2: fp32 h times the pair's routing weight -> fp16 A fragments with one power-of-two
-  // factor per (pair, group); the factor of D row r (pair 4 kq + r) comes from the lanes
-  // holding that A row.  (The weighted sum then needs no weight at the output.)
+  // FC2: fp32 h -> fp16 A fragments with one power-of-two factor per (pair, group); the
+  // factor of D row r (pair 4 kq + r) comes from the lanes holding that A row.
   auto convert_h = [&](const RecS& r) __attribute__((always_inline)) {
     if (!FC1) {
 #pragma unroll
       for (int gi = 0; gi < NGQ; ++gi) {
         const int gk = FC1 ? 0 : gi;
         float m = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          A32[gk][i].x *= hw;
-          A32[gk][i].y *= hw;
-          A32[gk][i].z *= hw;
-          A32[gk][i].w *= hw;
-        }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           m = fmaxf(m, fmaxf(fmaxf(fabsf(A32[gk][i].x), fabsf(A32[gk][i].y)),
@@ -431,7 +434,11 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   // MXFP4 tile (not in the ring): the groups of the wave's part of K load in passes of up
   // to MXG groups.  Each lane reads the 32 weights of its k-part p(q) of a group.
   auto mx_unit = [&](int gi, const uint4& q, uint32_t e, int m, int nb) __attribute__((always_inline)) {
-    const float es = e8m0_to_f32(e);
+    // e_max over the four blocks of this row's group (lanes i16, i16 + 16, + 32, + 48)
+    int em = (int)(e & 0xFFu);
+    em = max(em, __shfl_xor(em, 16));
+    em = max(em, __shfl_xor(em, 32));
+    const float es = ldexp2(1.0f, (int)(e & 0xFFu) - em);  // 2^(e - e_max), in (0, 1]
     half8_t bfr[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -442,7 +449,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
       const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, es, 3);
       bfr[s] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
     }
-    group_mma(gi, bfr, 1.0f, acc[m][nb]);
+    group_mma(gi, bfr, e8m0_to_f32((uint32_t)em), acc[m][nb]);
   };
   auto compute_mx = [&](const RecS& r, int rb) __attribute__((always_inline)) {
     const MfAddr d = vq_addr(r, rb);
@@ -504,7 +511,10 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
         for (int q = 0; q < 4; ++q)
           if (4 * kq + q < r.mcount) R[((wave * NM + m) * MF_MT + 4 * kq + q) * QS + nb * 16 + i16] = acc[m][nb][q];
     __syncthreads();
-    if (wr_next && wave == 0 && kq == 0) s_pair[gb ^ 1][i16] = arow_next;
+    if (wr_next && wave == 0 && kq == 0) {
+      s_pair[gb ^ 1][i16] = arow_next;
+      if (!FC1) s_w[gb ^ 1][i16] = hw;  // (act_load has loaded the next group's weights)
+    }
     const int nout = ROWS * r.mcount;
     for (int o = tid; o < nout; o += MF_THREADS) {
       const int q = o / ROWS, ri = o % ROWS;
@@ -520,7 +530,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
         }
         const int p = s_pair[gb][q];
         if (FC1) a.out[(size_t)p * a.I + n] = silu_fast(v[0]) * v[NM - 1];
-        else a.out[(size_t)p * a.H + n] = v[0];  // (h carries the routing weight)
+        else a.out[(size_t)p * a.H + n] = v[0] * s_w[gb][q];
       }
     }
   };
@@ -585,12 +595,14 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   const RecRaw raw_n = load_rec_raw(a.rec, (t + 1 < t_end ? t + 1 : t) / RB);
   RecS rc = rec_from_raw(raw_c);
   RecS rn = rec_from_raw(raw_n);
-  {
-    const Tok t0 = tok_load(rc);
-    act_load(t0, rc);
-    if (wave == 0 && kq == 0) s_pair[0][i16] = t0.arow;
-  }
+  const Tok t0 = tok_load(rc);
+  act_load(t0, rc);
   if (rc.fmt == MOE_VQ_FMT_VQ2) ring_load(rc, t % RB);
+  // (after the ring's loads: the weight's load is then waited for with the ring in flight)
+  if (wave == 0 && kq == 0) {
+    s_pair[0][i16] = t0.arow;
+    if (!FC1) s_w[0][i16] = hw;
+  }
   bool ring_ok = rc.fmt == MOE_VQ_FMT_VQ2;  // the ring holds this tile's codes
   if (tid < 256) write_table_entry(tab, cbv, tid);  // (every block has >= 256 threads)
   __syncthreads();

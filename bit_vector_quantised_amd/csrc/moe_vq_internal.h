@@ -42,6 +42,9 @@ enum HdrField {
   HDR_MT1 = 7,
   HDR_MT2 = 8,
   HDR_KEY = 9,        // shape key of the step that built the worklist
+  HDR_X_LO = 10,      // address of the activations the step was routed with (low, high
+  HDR_X_HI = 11,      // word) and their dtype: FC1 and prefill read the staged copy of x
+  HDR_X_DTYPE = 12,   // and refuse a call made with other activations
   HDR_WORDS = 64
 };
 
@@ -214,6 +217,8 @@ struct RouteArgs {
 };
 
 struct WorklistArgs {
+  const void* x;             // the activations routed (recorded in the header)
+  int x_dtype;
   const int32_t* topk_ids;
   const moe_vq_slot* slots;
   uint64_t pool_bytes;
@@ -235,7 +240,7 @@ struct WorklistArgs {
 struct FcArgs {
   const uint8_t* pool;
   const uint16_t* codebook;  // fp16 [128][4]
-  const uint32_t* hdr;
+  uint32_t* hdr;             // read; the status word is written when the call is refused
   const int32_t* act_start;
   const uint64_t* act_off;
   const uint32_t* act_fmt;
@@ -251,13 +256,15 @@ struct FcArgs {
   int T, H, I, k, KS, E;
   uint32_t key;
   int max_groups;            // upper bound on token groups for this T
+  uint64_t x_addr;           // FC1: the activations the caller passes (must be the routed ones)
+  int x_dtype;
   SlotLayout vq2, mx4;
 };
 
 struct PrefillArgs {
   const uint8_t* pool;
   const uint16_t* codebook;  // fp16 [128][4]
-  const uint32_t* hdr;
+  uint32_t* hdr;             // read; the status word is written when the call is refused
   const int32_t* act_start;  // [n_active + 1] first pair of each active expert
   const uint64_t* act_off;
   const uint32_t* act_fmt;
@@ -272,8 +279,15 @@ struct PrefillArgs {
   float* o_buf;              // [P][H]
   float* y;                  // [T][H]
   int T, H, I, k, E;
+  int x_dtype;
   uint32_t key;
   SlotLayout vq2, mx4;
 };
+
+// A workspace that was routed for this call: the shape key, and (FC1, prefill) the same
+// activations.  Header words are read together, before any is tested.
+__host__ __device__ inline bool x_matches(uint32_t lo, uint32_t hi, uint32_t dt, uint64_t addr, int dtype) {
+  return (lo == (uint32_t)addr) & (hi == (uint32_t)(addr >> 32)) & (dt == (uint32_t)dtype);
+}
 
 }  // namespace mvq

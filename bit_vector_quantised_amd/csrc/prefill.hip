@@ -14,8 +14,10 @@
 // for bf16 values no smaller than 2^-24 of the token's largest), h with one per pair.
 // B (weights) is decoded per lane: a VQ2 word through the LDS table of signed codebook
 // vectors, times its group scale in fp16 (one rounding, relative error <= 2^-11); MXFP4
-// bytes with the gfx950 FP4->FP16 convert and the E8M0 scale (exact within the fp16
-// range).  The contraction index is permuted the same way in A and B: within a
+// bytes with the gfx950 FP4->FP16 convert, scaled by 2^(e - e_row) where e_row is the
+// largest E8M0 exponent of the weight row, and 2^(e_row - 127) multiplies the row's fp32
+// outputs: converted values are at most 6 in magnitude for any exponent, and exact while
+// e >= e_row - 23.  The contraction index is permuted the same way in A and B: within a
 // 128-wide scale group, lanes 16q..16q+15 hold k = 32q + 8s + (0..7) at MFMA step s, so
 // one lane's codes for a group are contiguous (8 VQ2 bytes or 16 MXFP4 bytes).
 //
@@ -46,8 +48,19 @@ struct PfGeom {
   static_assert(BN == (FC1 ? 128 : 256), "tile rows");
 };
 
+// The workspace was routed for this call (shape key, count of active experts, the same
+// activations).  A refused call writes MOE_VQ_EINVAL into the status word (one lane of
+// workgroup 0 of each kernel) and computes nothing, so moe_vq_check() reports it.
 __device__ __forceinline__ bool pf_ws_ok(const PrefillArgs& a) {
-  return a.hdr[HDR_KEY] == a.key && a.hdr[HDR_N_ACTIVE] <= (uint32_t)a.E;
+  const uint32_t key = a.hdr[HDR_KEY], n_active = a.hdr[HDR_N_ACTIVE];
+  const uint32_t xlo = a.hdr[HDR_X_LO], xhi = a.hdr[HDR_X_HI], xdt = a.hdr[HDR_X_DTYPE];
+  const bool ok = (key == a.key) & (n_active <= (uint32_t)a.E) &
+                  x_matches(xlo, xhi, xdt, (uint64_t)(uintptr_t)a.x, a.x_dtype);
+  if (!ok && blockIdx.x == 0 && threadIdx.x == 0) {
+    a.hdr[HDR_STATUS] = MOE_VQ_EINVAL;
+    a.hdr[HDR_INFO] = 0xFFFFFFFFu;
+  }
+  return ok;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -147,9 +160,9 @@ __device__ __forceinline__ PfCodes pf_load_codes(const uint8_t* qb, const uint8_
   return c;
 }
 
-// B fragment (8 fp16 for k = 32q + 8s + 0..7) of step s.
+// B fragment (8 fp16 for k = 32q + 8s + 0..7) of step s.  erow: MXFP4 row exponent.
 template <int FMT, int S>
-__device__ __forceinline__ half8_t pf_decode(const uint2* tab, const PfCodes& c, uint32_t laneoff) {
+__device__ __forceinline__ half8_t pf_decode(const uint2* tab, const PfCodes& c, uint32_t laneoff, int erow) {
   half8_t b;
   if (FMT == MOE_VQ_FMT_VQ2) {
     const uint32_t wd = (S < 2) ? c.q.x : c.q.y;
@@ -163,7 +176,7 @@ __device__ __forceinline__ half8_t pf_decode(const uint2* tab, const PfCodes& c,
     b[4] = p2[0]; b[5] = p2[1]; b[6] = p3[0]; b[7] = p3[1];
   } else if (FMT == MOE_VQ_FMT_MXFP4) {
     const uint32_t wd = S == 0 ? c.q.x : S == 1 ? c.q.y : S == 2 ? c.q.z : c.q.w;
-    const float sc = e8m0_to_f32(c.s);
+    const float sc = ldexp2(1.0f, (int)c.s - erow);  // 2^(e - e_row), in (0, 1]
     const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 0);
     const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 1);
     const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 2);
@@ -184,11 +197,13 @@ struct PfTile {
   uint64_t off;
 };
 
-// Main loop of one tile for one weight format.
+// Main loop of one tile for one weight format.  rowf receives the factor of each of the
+// lane's output rows (MXFP4: 2^(e_row - 127); VQ2: 1).
 template <bool FC1, int FMT>
 __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>& tl, const uint2* tab,
                                         _Float16 (*As)[PF_BM * PF_AROW], f32x4_t (&acc)[PfGeom<FC1>::NM][PfGeom<FC1>::NB][4],
-                                        const int* s_pair, const float* s_fac) {
+                                        const int* s_pair, const float* s_fac,
+                                        float (&rowf)[PfGeom<FC1>::NM][PfGeom<FC1>::NB]) {
   using G = PfGeom<FC1>;
   constexpr int NM = G::NM, NB = G::NB, BN = G::BN;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -208,6 +223,55 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)  // rows past the end re-read the last row; the epilogue drops them
     rows[nb] = min(tl.nt * BN + wave * NB * 16 + nb * 16 + i16, NROWS - 1);
+  // MXFP4: the largest E8M0 exponent of each of the lane's rows.  The four lanes of a row
+  // (kq = 0..3) read every fourth dword of its K/32 exponent bytes, eight dwords per row
+  // and pass, every load of a pass issued before any is used.
+  int erow[NM][NB];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      erow[m][nb] = 0;
+      rowf[m][nb] = 1.0f;
+    }
+  if (FMT == MOE_VQ_FMT_MXFP4) {
+    const int nd = K / 128;  // dwords of E8M0 bytes per row
+    uint32_t mx[NM][NB];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) mx[m][nb] = 0u;
+    for (int d0 = kq; d0 < nd; d0 += 32) {
+      uint32_t w[NM][NB][8];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t* er = reinterpret_cast<const uint32_t*>(sb[m] + (size_t)rows[nb] * (K / 32));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[m][nb][i] = d0 + 4 * i < nd ? er[d0 + 4 * i] : 0u;
+        }
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t v = w[m][nb][i];
+            mx[m][nb] = max(mx[m][nb], max(max(v & 0xFFu, (v >> 8) & 0xFFu), max((v >> 16) & 0xFFu, v >> 24)));
+          }
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        int e = (int)mx[m][nb];
+        e = max(e, __shfl_xor(e, 16));
+        e = max(e, __shfl_xor(e, 32));
+        erow[m][nb] = e;
+        rowf[m][nb] = e8m0_to_f32((uint32_t)e);
+      }
+  }
 
   // staging: thread tid stages 32 consecutive k of token row tid/4 (FC1: fp16 x; FC2:
   // the bf16 h that FC1 wrote, scaled by the pair's power-of-two factor into fp16)
@@ -283,7 +347,7 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const half8_t bf = pf_decode<FMT, S>(tab, cur[m][nb], laneoff);
+          const half8_t bf = pf_decode<FMT, S>(tab, cur[m][nb], laneoff, erow[m][nb]);
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
             acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf, acc[m][nb][mb], 0, 0, 0);
@@ -365,14 +429,17 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a
   __syncthreads();
 
   f32x4_t acc[NM][NB][4];
+  float rowf[NM][NB];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+      rowf[m][nb] = 1.0f;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[m][nb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (tl.fmt == MOE_VQ_FMT_VQ2) pf_tile<FC1, MOE_VQ_FMT_VQ2>(a, tl, tab, As, acc, s_pair, s_fac);
-  else if (tl.fmt == MOE_VQ_FMT_MXFP4) pf_tile<FC1, MOE_VQ_FMT_MXFP4>(a, tl, tab, As, acc, s_pair, s_fac);
+    }
+  if (tl.fmt == MOE_VQ_FMT_VQ2) pf_tile<FC1, MOE_VQ_FMT_VQ2>(a, tl, tab, As, acc, s_pair, s_fac, rowf);
+  else if (tl.fmt == MOE_VQ_FMT_MXFP4) pf_tile<FC1, MOE_VQ_FMT_MXFP4>(a, tl, tab, As, acc, s_pair, s_fac, rowf);
   // (an absent expert keeps zeros; the worklist has set MOE_VQ_ENOTRESIDENT)
 
   // epilogue: D lane holds column i16 (output row) and token rows 4*kq + 0..3 of each block
@@ -389,7 +456,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const int n = tl.nt * BN + wave * NB * 16 + nb * 16 + i16;
-            const float gv = acc[0][nb][mb][r] * f, uv = acc[1][nb][mb][r] * f;
+            const float gv = acc[0][nb][mb][r] * (f * rowf[0][nb]), uv = acc[1][nb][mb][r] * (f * rowf[1][nb]);
             const float h = silu_fast(gv) * uv;
             if (n < NROWS) {
               a.h[(size_t)p * a.I + n] = f32_to_bf16_rne(h);
@@ -401,7 +468,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const int n = tl.nt * BN + wave * NB * 16 + nb * 16 + i16;
-            if (n < NROWS) a.o_buf[(size_t)p * a.H + n] = acc[0][nb][mb][r] * f;
+            if (n < NROWS) a.o_buf[(size_t)p * a.H + n] = acc[0][nb][mb][r] * (f * rowf[0][nb]);
           }
         }
       }

@@ -394,6 +394,9 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
     a.hdr[HDR_MT1] = a.MT1;
     a.hdr[HDR_MT2] = a.MT2;
     a.hdr[HDR_KEY] = a.key;
+    a.hdr[HDR_X_LO] = (uint32_t)(uintptr_t)a.x;
+    a.hdr[HDR_X_HI] = (uint32_t)((uint64_t)(uintptr_t)a.x >> 32);
+    a.hdr[HDR_X_DTYPE] = (uint32_t)a.x_dtype;
   }
 }
 
@@ -651,6 +654,9 @@ __global__ __launch_bounds__(64) void worklist_one_kernel(RouteArgs ra, Worklist
     a.hdr[HDR_MT1] = a.MT1;
     a.hdr[HDR_MT2] = a.MT2;
     a.hdr[HDR_KEY] = a.key;
+    a.hdr[HDR_X_LO] = (uint32_t)(uintptr_t)a.x;
+    a.hdr[HDR_X_HI] = (uint32_t)((uint64_t)(uintptr_t)a.x >> 32);
+    a.hdr[HDR_X_DTYPE] = (uint32_t)a.x_dtype;
   }
 }
 

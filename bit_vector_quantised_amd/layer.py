@@ -142,7 +142,7 @@ def tiered_forward(step: "Step", layer: TieredLayer, x: torch.Tensor):
                           step.ws.data_ptr(), step.stream())
     if n:
         step.route(x)
-    step.fc1(T)
+    step.fc1(x)
     step.fc2(T)
     return step.y[:T], n
 
@@ -181,8 +181,10 @@ class Step:
         _lib.route_topk(self.layer.c, x.data_ptr(), x_dtype_code(x), T, self.ids.data_ptr(), self.w.data_ptr(),
                         self.ws.data_ptr(), self.ws_bytes, self.stream())
 
-    def fc1(self, T: int) -> None:
-        _lib.fc1_silu(self.layer.c, T, self.ws.data_ptr(), self.ws_bytes, self.h.data_ptr(), self.stream())
+    def fc1(self, x: torch.Tensor) -> None:
+        """FC1 of the step routed on x (the same tensor route() was given)."""
+        _lib.fc1_silu(self.layer.c, x.data_ptr(), x_dtype_code(x), x.shape[0], self.ws.data_ptr(), self.ws_bytes,
+                      self.h.data_ptr(), self.stream())
 
     def fc2(self, T: int) -> None:
         _lib.fc2_combine(self.layer.c, self.h.data_ptr(), T, self.ws.data_ptr(), self.ws_bytes,
@@ -194,11 +196,20 @@ class Step:
                           self.y.data_ptr(), self.stream())
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        """route -> FC1 -> FC2; returns a view of y [T, H] (valid until the next call)."""
+        """route -> FC1 -> FC2 as three calls; returns a view of y [T, H] (valid until the
+        next call)."""
         T = x.shape[0]
         self.route(x)
-        self.fc1(T)
+        self.fc1(x)
         self.fc2(T)
+        return self.y[:T]
+
+    def step(self, x: torch.Tensor) -> torch.Tensor:
+        """The same step through the single-call entry point moe_vq_forward."""
+        T = x.shape[0]
+        assert x.is_contiguous() and x.shape[1] == self.layer.hidden and T <= self.max_tokens
+        _lib.forward(self.layer.c, x.data_ptr(), x_dtype_code(x), T, self.ids.data_ptr(), self.w.data_ptr(),
+                     self.h.data_ptr(), self.y.data_ptr(), self.ws.data_ptr(), self.ws_bytes, self.stream())
         return self.y[:T]
 
     def check(self):

@@ -39,9 +39,13 @@
  *  - stream is a hipStream_t (NULL = the default stream).  Every compute call only
  *    enqueues work on it and returns; nothing synchronises except moe_vq_check().
  *  - Argument errors are returned synchronously, before any HIP call is made.
- *  - Errors found on the device (an absent expert, a slot outside the pool) are
- *    recorded in the workspace's status word; the affected contribution is left
- *    out of y and moe_vq_check() reports it.  Nothing is ever silently skipped.
+ *  - Errors found on the device are recorded in the workspace's status word and
+ *    reported by moe_vq_check(): an absent expert or a slot outside the pool
+ *    (MOE_VQ_ENOTRESIDENT; that contribution is left out of y), or a compute call
+ *    made on a workspace routed for other shapes or other activations
+ *    (MOE_VQ_EINVAL; the call computes nothing from the experts, and its outputs
+ *    must not be used).  Nothing is ever silently skipped (Tandem-vLLM 0.2.0 announcement,
+ *    "How it works": nothing is skipped or substituted).
  *  - Calls on one workspace must be stream-ordered: a workspace holds one step.
  *  - Results are deterministic: repeated calls on the same inputs give the same bits.
  */
@@ -113,39 +117,76 @@ size_t moe_vq_workspace_bytes(const moe_vq_layer *layer, int n_tokens);
 /* Route n_tokens tokens: router product (bf16 weights, fp32 accumulation), softmax
  * over all experts, top-k (descending logit, equal logits -> lower expert id),
  * renormalised weights, and the per-expert worklist with slot lookups, all on the
- * device.  x: [n_tokens][H] in x_dtype.  Outputs topk_ids [n_tokens][k] (int32)
- * and topk_w [n_tokens][k] (fp32).  Also stages x for FC1 in the workspace and
- * resets the status word.  n_tokens == 0 is a no-op.  n_tokens <= 65536. */
+ * device.  Source: Tandem-vLLM 0.2.0 announcement, "How it works" (each token's routed
+ * experts are looked up in the GPU's expert cache); vLLM-Moet README, "What we changed
+ * against official vLLM", row "MoE at decode" (router -> FC1 -> FC2).  The pages do not
+ * print the routing function; it is read as a softmax over all logits, renormalised
+ * over the chosen k.
+ * x: [n_tokens][H] in x_dtype, 16-byte aligned.  Outputs topk_ids [n_tokens][k]
+ * (int32) and topk_w [n_tokens][k] (fp32).  Also stages x for FC1 in the workspace,
+ * records which x was routed, and resets the status word.  n_tokens == 0 is a no-op;
+ * n_tokens <= 65536.  Errors: MOE_VQ_EINVAL (bad argument), MOE_VQ_ENOSPACE (ws_bytes <
+ * moe_vq_workspace_bytes), MOE_VQ_EHIP (launch failed); an absent or out-of-pool slot of
+ * a selected expert is MOE_VQ_ENOTRESIDENT in the status word. */
 int moe_vq_route_topk(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
                       int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
 /* FC1 of every routed (token, expert) pair with SiLU*up fused: for pair p = t*k + i
- * (expert topk_ids[t][i]), h[p][:] = silu(W_g x_t) * (W_u x_t), fp32 [n_tokens*k][I].
- * Uses the activations and worklist staged by moe_vq_route_topk in ws. */
-int moe_vq_fc1_silu(const moe_vq_layer *layer, int n_tokens, void *ws, size_t ws_bytes,
-                    float *h, void *stream);
+ * (expert topk_ids[t][i]), h[p][:] = silu(W_g x_t) * (W_u x_t), fp32 [n_tokens*k][I],
+ * with W_g and W_u decoded from the expert's codes on the fly.  Source: Tandem-vLLM
+ * 0.2.0 announcement, "How it works" (routed experts as 2-bit vector codes); vLLM-Moet
+ * README, "2-bit experts on vLLM v0.24.0" (sign-symmetric codebook) and
+ * "Qwen3.8-Flash-Next-FP8 on 4x RTX PRO 6000" (silu*up fused into the expert GEMV).
+ * x and x_dtype must be the activations moe_vq_route_topk was called with on ws (the
+ * call reads the fp16 copy of x that routing staged, and the worklist); otherwise the
+ * call computes nothing and sets MOE_VQ_EINVAL in the status word.  h: 16-byte aligned,
+ * owned by the caller.  Errors: as moe_vq_route_topk. */
+int moe_vq_fc1_silu(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
+                    void *ws, size_t ws_bytes, float *h, void *stream);
 
 /* FC2 and the weighted combine: y[t][:] = sum_i topk_w[t][i] * (W_d h[t*k+i]),
- * fp32 [n_tokens][H], overwritten.  h as written by moe_vq_fc1_silu. */
+ * fp32 [n_tokens][H], overwritten, with W_d decoded from the codes on the fly and the
+ * routing weights of the worklist in ws.  Source: Tandem-vLLM 0.2.0 announcement, "How it
+ * works" (expert outputs added back with the routing weights; nothing skipped or
+ * substituted); vLLM-Moet README, "What we changed against official vLLM", row "MoE at
+ * decode" (no padding rows written back).  h: [n_tokens*k][I] fp32 (any values: FC1's
+ * output normally), 16-byte aligned; y 16-byte aligned.  A workspace routed for other
+ * shapes sets MOE_VQ_EINVAL in the status word and y is then not valid.  Errors: as
+ * moe_vq_route_topk. */
 int moe_vq_fc2_combine(const moe_vq_layer *layer, const float *h, int n_tokens,
                        void *ws, size_t ws_bytes, float *y, void *stream);
+
+/* The whole routed-expert step in one call: moe_vq_route_topk, moe_vq_fc1_silu and
+ * moe_vq_fc2_combine on ws, in that order on stream, with the same results bit for bit
+ * (Tandem-vLLM 0.2.0 announcement, "How it works"; vLLM-Moet README, "What we changed
+ * against official vLLM", rows "MoE at decode" and "launch gaps": router -> FC1 -> FC2 in
+ * as few launches as possible).  Outputs topk_ids, topk_w (as route), h [n_tokens*k][I]
+ * fp32 (as FC1) and y [n_tokens][H] fp32 (as FC2), all caller-owned; x, h and y 16-byte
+ * aligned.  Errors: as moe_vq_route_topk; check the status word with moe_vq_check. */
+int moe_vq_forward(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
+                   int32_t *topk_ids, float *topk_w, float *h, float *y,
+                   void *ws, size_t ws_bytes, void *stream);
 
 /* Prefill form of FC1 + FC2 + combine for large n_tokens (vLLM-Moet README, "What we
  * changed against official vLLM", rows "MoE at decode" and "prefill": tokens grouped per
  * expert, no padding to a fixed row count).  The routed pairs of each expert are cut into
  * tiles of 64 tokens; FC1 (gate/up, SiLU*up fused) and FC2 (down, routing weight fused)
  * run as fp16 matrix-core (MFMA) products with fp32 accumulation over weights decoded in
- * registers (VQ2: codebook vector times group scale, rounded once to fp16; MXFP4: exact
- * within the fp16 range).  x is staged as fp16 with one power-of-two factor per token, h
- * with one per routed pair.  Requires moe_vq_route_topk on the same x and n_tokens first
- * (it builds the worklist this call reads).  x: [n_tokens][H] in x_dtype, 16-byte
- * aligned; y: [n_tokens][H] fp32, 16-byte aligned, overwritten.  Errors: as
- * moe_vq_fc2_combine; an absent expert contributes 0 and is reported by moe_vq_check. */
+ * registers (VQ2: codebook vector times group scale, rounded once to fp16; MXFP4: E2M1
+ * values times 2^(e - e_row), e_row the largest exponent of the weight row, with
+ * 2^(e_row - 127) applied to the row's fp32 outputs -- exact while e >= e_row - 23).  x is
+ * staged as fp16 with one power-of-two factor per token, h with one per routed pair.
+ * Requires moe_vq_route_topk on the same x, x_dtype and n_tokens first (it builds the
+ * worklist this call reads); other activations set MOE_VQ_EINVAL in the status word and
+ * y is then not valid.  x: [n_tokens][H] in x_dtype, 16-byte aligned; y: [n_tokens][H]
+ * fp32, 16-byte aligned, overwritten.  Errors: as moe_vq_fc2_combine; an absent expert
+ * contributes 0 and is reported by moe_vq_check. */
 int moe_vq_prefill_gemm(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
                         void *ws, size_t ws_bytes, float *y, void *stream);
 
 /* Test hook: decode one matrix (enum moe_vq_matrix) of one expert into out, [rows][in]
- * row-major.  out_dtype MOE_VQ_F32 gives the exact decoded values, MOE_VQ_BF16 their
+ * row-major (the VQ2 and MXFP4 formats above; Tandem-vLLM 0.2.0 announcement, "How it
+ * works" and "Quality vs the official FP4 checkpoint").  out_dtype MOE_VQ_F32 gives the exact decoded values, MOE_VQ_BF16 their
  * round-to-nearest-even.  It uses the same LDS decode tables as the FC kernels.  The
  * slot is read on the device: if it is absent or lies outside the pool, out is left
  * untouched and *status_dev (a device int32, may be NULL) is set to
@@ -154,8 +195,8 @@ int moe_vq_decode_expert(const moe_vq_layer *layer, int expert, int matrix, int 
                          void *out, int32_t *status_dev, void *stream);
 
 /* Synchronise stream, then return the device-side status of the last step run on ws
- * (MOE_VQ_OK or MOE_VQ_ENOTRESIDENT).  If info is not NULL, *info receives the
- * first offending expert id (or -1). */
+ * (MOE_VQ_OK, MOE_VQ_ENOTRESIDENT, or MOE_VQ_EINVAL for a refused compute call).  If
+ * info is not NULL, *info receives the first offending expert id (or -1). */
 int moe_vq_check(const void *ws, void *stream, int32_t *info);
 
 /* Synchronise stream and copy the routing summary of the last step on ws to the host:

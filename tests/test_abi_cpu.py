@@ -148,9 +148,13 @@ def test_fc_and_prefill_and_decode_reject_bad_arguments():
     P = ctypes.byref
     ws_ok = _lib.workspace_bytes(L, 4)
     WS, H_, Y = 0x700000, 0x800000, 0x900000
-    assert raw.moe_vq_fc1_silu(P(L), 4, WS, ws_ok - 256, H_, None) == _lib.ENOSPACE
-    assert raw.moe_vq_fc1_silu(P(L), 4, WS, ws_ok, None, None) == _lib.EINVAL
-    assert raw.moe_vq_fc1_silu(P(L), 0, WS, ws_ok, H_, None) == _lib.OK
+    X = 0x40000
+    assert raw.moe_vq_fc1_silu(P(L), X, _lib.F32, 4, WS, ws_ok - 256, H_, None) == _lib.ENOSPACE
+    assert raw.moe_vq_fc1_silu(P(L), X, _lib.F32, 4, WS, ws_ok, None, None) == _lib.EINVAL
+    assert raw.moe_vq_fc1_silu(P(L), None, _lib.F32, 4, WS, ws_ok, H_, None) == _lib.EINVAL
+    assert raw.moe_vq_fc1_silu(P(L), X + 8, _lib.F32, 4, WS, ws_ok, H_, None) == _lib.EINVAL
+    assert raw.moe_vq_fc1_silu(P(L), X, 9, 4, WS, ws_ok, H_, None) == _lib.EINVAL
+    assert raw.moe_vq_fc1_silu(P(L), X, _lib.F32, 0, WS, ws_ok, H_, None) == _lib.OK
     assert raw.moe_vq_fc2_combine(P(L), H_, 4, WS, ws_ok, None, None) == _lib.EINVAL
     assert raw.moe_vq_fc2_combine(P(L), None, 4, WS, ws_ok, Y, None) == _lib.EINVAL
     assert raw.moe_vq_fc2_combine(P(L), H_, 4, None, ws_ok, Y, None) == _lib.EINVAL
@@ -168,9 +172,26 @@ def test_fc_and_prefill_and_decode_reject_bad_arguments():
     assert raw.moe_vq_prefill_gemm(P(L), 0x40000, _lib.BF16, 0, WS, ws_ok, Y, None) == _lib.OK
     for T in (-1, 65537):
         assert raw.moe_vq_route_topk(P(L), 0x40000, _lib.F32, T, 0x50000, 0x60000, WS, ws_ok, None) == _lib.EINVAL
-        assert raw.moe_vq_fc1_silu(P(L), T, WS, ws_ok, H_, None) == _lib.EINVAL
+        assert raw.moe_vq_fc1_silu(P(L), 0x40000, _lib.F32, T, WS, ws_ok, H_, None) == _lib.EINVAL
         assert raw.moe_vq_fc2_combine(P(L), H_, T, WS, ws_ok, Y, None) == _lib.EINVAL
         assert raw.moe_vq_prefill_gemm(P(L), 0x40000, _lib.BF16, T, WS, ws_ok, Y, None) == _lib.EINVAL
+
+
+def test_forward_rejects_bad_arguments():
+    raw = _lib.raw()
+    L = fake_layer()
+    P = ctypes.byref
+    ws_ok = _lib.workspace_bytes(L, 4)
+    X, IDS, W, H_, Y, WS = 0x40000, 0x50000, 0x60000, 0x800000, 0x900000, 0x700000
+    fwd = raw.moe_vq_forward
+    assert fwd(P(L), X, _lib.BF16, 4, IDS, W, H_, Y, WS, ws_ok - 1, None) == _lib.ENOSPACE
+    assert fwd(P(L), X, 5, 4, IDS, W, H_, Y, WS, ws_ok, None) == _lib.EINVAL
+    assert fwd(P(L), None, _lib.BF16, 4, IDS, W, H_, Y, WS, ws_ok, None) == _lib.EINVAL
+    assert fwd(P(L), X, _lib.BF16, 4, IDS, W, None, Y, WS, ws_ok, None) == _lib.EINVAL
+    assert fwd(P(L), X, _lib.BF16, 4, IDS, W, H_, Y + 4, WS, ws_ok, None) == _lib.EINVAL
+    assert fwd(P(L), X, _lib.BF16, 4, IDS, W, H_, Y, WS + 16, ws_ok, None) == _lib.EINVAL
+    assert fwd(P(L), X, _lib.BF16, 65537, IDS, W, H_, Y, WS, ws_ok, None) == _lib.EINVAL
+    assert fwd(P(L), X, _lib.BF16, 0, IDS, W, H_, Y, WS, ws_ok, None) == _lib.OK
 
 
 def test_strerror():

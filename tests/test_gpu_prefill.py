@@ -138,6 +138,10 @@ def test_p4096_prefill_sampled_tokens(p4096):
     info = g["step"].info(4096)
     assert info["n_pairs"] == 4096 * 8
     hot = int(np.bincount(g["ids"].reshape(-1)).argmax())
-    tokens = sorted({0, 1, 2047, 4095} | {int(t) for t in np.nonzero((g["ids"] == hot).any(axis=1))[0][:4]})
+    tokens = {0, 1, 2047, 4095} | {int(t) for t in np.nonzero((g["ids"] == hot).any(axis=1))[0][:4]}
+    rng = np.random.default_rng(4096)
+    tokens |= {int(t) for t in rng.choice(4096, size=40, replace=False)}
+    tokens = sorted(tokens)[:40]
+    assert len(tokens) >= 32
     res = compare(syn, x, "bf16", g, 8, tokens=tokens, check_h=False)
     say("p4096", {k: v for k, v in res.items() if k != "ref"})

@@ -1,7 +1,8 @@
 """Host-RAM expert tier on the GPU: a layer with every expert in a pinned host pool and
 only some device slots gives, step after step, the same bits as the layer with every
 expert resident (the kernels read the same bytes), while experts are copied in and
-evicted; a step selecting more experts than the tier has slots is refused."""
+evicted, and every tiered step matches the fp64 oracle under the parity rules; a step
+selecting more experts than the tier has slots is refused."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +11,7 @@ import synth
 from bit_vector_quantised_amd import _lib
 from bit_vector_quantised_amd.layer import DeviceLayer, Step, TieredLayer, tiered_forward
 
-from gpu_util import say, x_tensor
+from gpu_util import compare, say, x_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -29,11 +30,19 @@ def test_tier_steps_match_all_resident_bits(mini_syn, mixed):
     full = DeviceLayer.from_synth(syn, formats=fm)
     tiered = TieredLayer.from_synth(syn, n_dev_slots=8, formats=fm)
     st_full, st_tier = Step(full, 2), Step(tiered, 2)
+
+    class View:  # the layer as the oracle reads it: each expert in its slot's format
+        pass
+    view = View()
+    view.cfg, view.codebook, view.router_w = syn.cfg, syn.codebook, syn.router_w
+    fmts = fm if fm is not None else list(syn.formats)
+    view.expert = lambda e: syn.expert_as(e, fmts[e])
     copied, hits = 0, 0
     # each input twice in a row: the repeat finds its experts resident
     for i, T in enumerate([1, 1, 2, 2, 1, 1, 1, 1, 2, 2, 1, 1]):
         say(f"tier step {i} T={T} mixed={mixed}")
-        x = x_tensor(syn.x(n=T, stream=300 + i // 2), "bf16")
+        x_np = syn.x(n=T, stream=300 + i // 2)
+        x = x_tensor(x_np, "bf16")
         y_ref = st_full.forward(x).clone()
         y, n = tiered_forward(st_tier, tiered, x)
         torch.cuda.synchronize()
@@ -41,6 +50,11 @@ def test_tier_steps_match_all_resident_bits(mini_syn, mixed):
         assert st_tier.check()[0] == _lib.OK, "an expert the step selected is still absent"
         assert torch.equal(y, y_ref), f"step {i}: tiered output differs from the all-resident one"
         assert torch.equal(st_tier.ids[:T], st_full.ids[:T])
+        g = {"ids": st_tier.ids[:T].cpu().numpy().astype(np.int64),
+             "w": st_tier.w[:T].cpu().numpy().astype(np.float64),
+             "h": st_tier.h[:T * MINI.top_k].cpu().numpy().astype(np.float64).reshape(T, MINI.top_k, -1),
+             "y": y.cpu().numpy().astype(np.float64)}
+        compare(view, x_np, "bf16", g, MINI.top_k)
         copied += n
         if i % 2 == 1:
             assert n == 0, "a repeated step copied experts"
