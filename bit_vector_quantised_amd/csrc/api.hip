@@ -3,6 +3,8 @@
 // library allocates nothing and keeps no per-call state.
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_vq_internal.h"
 #include "moe_vq_launch.h"
 
@@ -168,6 +170,39 @@ hipError_t forward_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, 
   return e;
 }
 
+// ---- Workspace of moe_vq_forward_static: one array per GPU, in the library's own device
+// memory, held until the process ends.  Host code never uses the array's name as an
+// address: its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)16 << 20;
+constexpr int MAX_DEVICES = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's address of `scratch`, looked up on the device's first call.
+hipError_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -235,6 +270,22 @@ int moe_vq_forward(const moe_vq_layer* L, const void* x, int x_dtype, int n_toke
   if (st || n_tokens == 0) return st;
   if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
   return hip_status(forward_on(L, x, x_dtype, n_tokens, topk_ids, topk_w, h, y, ws, static_cast<hipStream_t>(stream)));
+}
+
+int moe_vq_forward_static(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens, int32_t* topk_ids,
+                          float* topk_w, float* h, float* y, int32_t* status, void* stream) {
+  int st = check_forward(L, x, x_dtype, n_tokens, topk_ids, topk_w, h, y);
+  if (st || n_tokens == 0) return st;
+  if ((uintptr_t)status & 3) return MOE_VQ_EINVAL;
+  if (ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens).total > STATIC_SCRATCH_BYTES)
+    return MOE_VQ_ENOSPACE;
+  void* ws = nullptr;
+  if ((st = hip_status(static_scratch(&ws)))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(forward_on(L, x, x_dtype, n_tokens, topk_ids, topk_w, h, y, ws, s)))) return st;
+  if (status)  // the status word and the offending expert, for the caller to read
+    return hip_status(hipMemcpyAsync(status, ws, 2 * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+  return MOE_VQ_OK;
 }
 
 int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens, void* ws,

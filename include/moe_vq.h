@@ -167,6 +167,22 @@ int moe_vq_forward(const moe_vq_layer *layer, const void *x, int x_dtype, int n_
                    int32_t *topk_ids, float *topk_w, float *h, float *y,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* moe_vq_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same step and
+ * the same kernels, with the workspace in a static device array of the library (16 MiB
+ * per GPU, held until the process ends) instead of a caller buffer.  It calls no
+ * allocating routine.  status (device int32[2], may be NULL) receives the step's status
+ * word and offending expert id (as moe_vq_check reports them) at the end of the step, on
+ * stream.  Every call on one GPU shares that GPU's array and each call overwrites it:
+ * calls that overlap on one GPU (other streams, other threads) race, so they must be
+ * serialised by the caller.  Nothing in the array needs clearing between calls (every
+ * word a step reads is written earlier in the same step).  Errors: as moe_vq_forward, and
+ * MOE_VQ_ENOSPACE when the step's workspace (moe_vq_workspace_bytes for n_tokens) exceeds
+ * 16 MiB, about 56 tokens at H = 7168, I = 2048, 256 experts, top-8. */
+int moe_vq_forward_static(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
+                          int32_t *topk_ids, float *topk_w, float *h, float *y, int32_t *status,
+                          void *stream);
+
 /* Prefill form of FC1 + FC2 + combine for large n_tokens (vLLM-Moet README, "What we
  * changed against official vLLM", rows "MoE at decode" and "prefill": tokens grouped per
  * expert, no padding to a fixed row count).  The routed pairs of each expert are cut into
