@@ -7,7 +7,9 @@
 
 One step = route (router product, softmax/top-k/renormalise, worklist) -> FC1 with
 SiLU*up -> FC2 with the weighted combine, for one batch of synthetic tokens whose
-activations already sit in HBM.  The default workload is decode batch 1 of a
+activations already sit in HBM, through the single-call entry point moe_vq_forward.  The
+kernel-timing pass runs the same step as its three calls (route_topk, fc1_silu,
+fc2_combine: the same kernels) so that events can bracket FC1 and FC2.  The default workload is decode batch 1 of a
 DeepSeek-style layer (H=7168, I=2048, 256 experts, top-8, VQ2 experts at 2.125
 bits/weight, all resident in one HBM slot pool).  Tokens are cycled from a pool of
 256 distinct pre-drawn tokens so consecutive steps touch different experts (the
@@ -251,6 +253,9 @@ def measure(args, config, with_events=True):
 
     def run_step(i, ev=None):
         xb = x_pool[(i % n_batches) * T:(i % n_batches + 1) * T]
+        if ev is None and not prefill:
+            step.step(xb)  # the whole step in one call (moe_vq_forward)
+            return
         step.route(xb)
         if ev is not None:
             ev[0].record(stream)

@@ -88,12 +88,12 @@ FcArgs make_fc_args(const moe_vq_layer* L, int T, void* ws, const WsLayout& W, b
   return a;
 }
 
-// The launches of one call, after its arguments have been checked.
-hipError_t route_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, int32_t* topk_ids, float* topk_w,
-                    void* ws, hipStream_t stream) {
+// Kernel arguments of the routing launches.
+void route_args(const moe_vq_layer* L, const void* x, int x_dtype, int T, int32_t* topk_ids, float* topk_w, void* ws,
+                RouteArgs& ra, WorklistArgs& wa) {
   const int E = L->n_experts, H = L->hidden, I = L->inter, k = L->top_k;
   const WsLayout W = ws_layout(E, H, I, k, T);
-  RouteArgs ra{};
+  ra = RouteArgs{};
   ra.router_w = static_cast<const uint16_t*>(L->router_w);
   ra.x = x;
   ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.KS = W.KS;
@@ -104,7 +104,7 @@ hipError_t route_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, in
   ra.topk_ids = topk_ids;
   ra.topk_w = topk_w;
   ra.pair_w = at<float>(ws, W.pair_w);
-  WorklistArgs wa{};
+  wa = WorklistArgs{};
   wa.x = x;
   wa.x_dtype = x_dtype;
   wa.topk_ids = topk_ids;
@@ -126,6 +126,14 @@ hipError_t route_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, in
   wa.grp2 = at<int32_t>(ws, W.grp2);
   wa.pair_list = at<int32_t>(ws, W.pair_list);
   wa.key = shape_key(T, E, k, H, I);
+}
+
+// The launches of one call, after its arguments have been checked.
+hipError_t route_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, int32_t* topk_ids, float* topk_w,
+                    void* ws, hipStream_t stream) {
+  RouteArgs ra;
+  WorklistArgs wa;
+  route_args(L, x, x_dtype, T, topk_ids, topk_w, ws, ra, wa);
   return launch_route(ra, x_dtype, wa, stream);
 }
 

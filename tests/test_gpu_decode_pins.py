@@ -180,6 +180,54 @@ def test_fc2_onehot_every_kernel(name, mixed):
         say(f"  worst error / sum of term magnitudes {worst:.2e}")
 
 
+@pytest.mark.parametrize("name", ["h2048_i1024", "h1024_i2048", "h7168_i2048", "h2048_i1024_k12"])
+@pytest.mark.parametrize("mixed", [False, True])
+def test_forward_one_token_onehot(name, mixed):
+    """moe_vq_forward at one token: every h element against the oracle's decode, and y
+    against the three-call step bit for bit."""
+    v, dev = make_layer(name, mixed=mixed)
+    H, k = dev.hidden, dev.top_k
+    dec = Decoded(v)
+    for j, val in ((0, 1.0), (H // 2 + 5, -2.0), (H - 1, 0.5)):
+        xt = x_tensor(onehot_x(1, H, [j], [val], "bf16"), "bf16")
+        st = Step(dev, 1)
+        y = st.step(xt).clone()
+        torch.cuda.synchronize()
+        assert st.check()[0] == _lib.OK
+        ids = st.ids[:1].cpu().numpy()
+        h = st.h[:k].cpu().numpy().astype(np.float64)
+        for i in range(k):
+            Wg, Wu, _ = dec(int(ids[0, i]))
+            ref = oracle.silu(val * Wg[:, j]) * (val * Wu[:, j])
+            bad = np.abs(h[i] - ref) > H_TOL * np.abs(ref) + 2.0 ** -126
+            assert not bad.any(), (name, j, i, np.nonzero(bad)[0][:8].tolist())
+        g = run(dev, onehot_x(1, H, [j], [val], "bf16"), "bf16")
+        assert np.array_equal(g["ids"], ids) and np.array_equal(g["y"], y.cpu().numpy().astype(np.float64))
+
+
+def test_forward_one_token_absent_experts():
+    """moe_vq_forward at one token reports the lowest absent selected expert and leaves it
+    out of y."""
+    v0, dev0 = make_layer("h2048_i1024")
+    x = synth.f64_to_bf16_bits(np.random.default_rng(77).standard_normal((1, 2048)))
+    st0 = Step(dev0, 1)
+    st0.step(x_tensor(x, "bf16"))
+    ids = st0.ids[0].cpu().numpy()
+    gone = sorted(int(e) for e in ids[1:3])
+    fm = [synth.FMT_VQ2] * 16
+    for e in gone:
+        fm[e] = synth.FMT_ABSENT
+    v, dev = tiny_variant(v0, formats=fm)
+    st = Step(dev, 1)
+    y = st.step(x_tensor(x, "bf16")).cpu().numpy().astype(np.float64)
+    status, info = st.check()
+    assert status == _lib.ENOTRESIDENT and info == gone[0]
+    r = oracle.forward(v0, oracle.x_value(x, "bf16"), 4, forced_selection=st.ids[:1].cpu().numpy())
+    keep = ~np.isin(st.ids[:1].cpu().numpy(), gone)[:, :, None]
+    y_ref = (r["w"][:, :, None] * r["o"] * keep).sum(axis=1)
+    assert (np.abs(y - y_ref).max() / np.abs(y_ref).max()) <= 1e-2
+
+
 def test_fc1_onehot_fp32_activations():
     v, dev = make_layer("h2048_i1024")
     for T in (1, 12):
