@@ -20,7 +20,7 @@ MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 
 EXPORTS = ("moe_vq_expert_bytes", "moe_vq_slot_layout", "moe_vq_workspace_bytes", "moe_vq_route_topk",
            "moe_vq_fc1_silu", "moe_vq_fc2_combine", "moe_vq_forward", "moe_vq_forward_static", "moe_vq_prefill_gemm", "moe_vq_decode_expert",
-           "moe_vq_check", "moe_vq_step_info", "moe_vq_tier_init", "moe_vq_tier_plan", "moe_vq_tier_resolve",
+           "moe_vq_check", "moe_vq_step_info", "moe_vq_tier_init", "moe_vq_tier_plan", "moe_vq_tier_resolve", "moe_vq_cpu_experts",
            "moe_vq_last_hip_error", "moe_vq_strerror")
 
 
@@ -81,6 +81,8 @@ def _load():
                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int)]),
         "moe_vq_tier_resolve": (i32, [LP, ctypes.POINTER(Tier), vp, vp, i32, vp, vp, ctypes.POINTER(ctypes.c_int32)]),
+        "moe_vq_cpu_experts": (i32, [LP, vp, ctypes.c_uint64, ctypes.POINTER(Slot), vp, vp, i32, i32, vp, vp, vp,
+                                     vp, i32]),
         "moe_vq_last_hip_error": (ctypes.c_char_p, []),
         "moe_vq_strerror": (ctypes.c_char_p, [i32]),
     }
@@ -232,6 +234,13 @@ def tier_resolve(layer: Layer, tier: ExpertTier, pool: int, slots: int, n_tokens
     _ok(_lib.moe_vq_tier_resolve(ctypes.byref(layer), ctypes.byref(tier.c), pool, slots, n_tokens, ws, stream,
                                  ctypes.byref(n)), "tier_resolve")
     return int(n.value)
+
+
+def cpu_experts(layer: Layer, host_pool: int, host_pool_bytes: int, host_slots, codebook: int, x: int,
+                x_dtype: int, n_tokens: int, topk_ids: int, topk_w: int, compute: int, y: int, n_threads: int) -> None:
+    """The CPU miss path (host pointers only); host_slots is a ctypes Slot array."""
+    _ok(_lib.moe_vq_cpu_experts(ctypes.byref(layer), host_pool, host_pool_bytes, host_slots, codebook, x, x_dtype,
+                                n_tokens, topk_ids, topk_w, compute, y, n_threads), "cpu_experts")
 
 
 def raw():

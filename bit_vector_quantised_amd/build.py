@@ -28,6 +28,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_vq.so")
 SOURCES = ["api.hip", "route.hip", "fc.hip", "fc_mfma.hip", "fc2_single.hip", "decode.hip", "prefill.hip"]
+CPP_SOURCES = ["cpu_experts.cpp"]  # host code (the expert path on the host cores), built with g++
 ARCH = "gfx950"
 
 
@@ -81,9 +82,19 @@ def build(verbose: bool = False) -> str:
             print(out)
         return obj, kernel_resources(text)
 
+    def compile_cpp(src):
+        obj = os.path.join(objdir, src + ".o")
+        cmd = ["g++", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-fvisibility-inlines-hidden", "-pthread", "-Wall", "-I", INCLUDE,
+               "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"g++ failed on {src}:\n{r.stdout}{r.stderr}")
+        return obj
+
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         results = list(ex.map(compile_one, SOURCES))
-    objs = [o for o, _ in results]
+        cpp_objs = list(ex.map(compile_cpp, CPP_SOURCES))
+    objs = [o for o, _ in results] + cpp_objs
     res = [k for _, ks in results for k in ks]
     with open(os.path.join(objdir, "kernel_resources.txt"), "w") as f:
         for name, v in res:
@@ -92,7 +103,7 @@ def build(verbose: bool = False) -> str:
     if spilling:
         raise RuntimeError("kernels use scratch memory: " + ", ".join(spilling))
     tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-Bsymbolic", "-o", tmp, *objs]
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-Wl,-Bsymbolic", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")

@@ -6,6 +6,7 @@ and passes pointers.
 """
 from __future__ import annotations
 
+import os
 from typing import Callable, Dict, Optional, Sequence
 
 import numpy as np
@@ -119,6 +120,8 @@ class TieredLayer:
         self.slots = torch.zeros(n_experts * 16, dtype=torch.uint8, device=self.device)
         self.router_w = torch.from_numpy(np.ascontiguousarray(router_w_bits).view(np.int16)).to(self.device)
         self.codebook = torch.from_numpy(np.ascontiguousarray(codebook).view(np.int16)).to(self.device)
+        self.codebook_host = torch.from_numpy(np.ascontiguousarray(codebook).view(np.int16).copy())
+        self.host_formats = [f for _, f in host_slots]
         self.c = _lib.Layer(hidden, inter, n_experts, top_k, self.router_w.data_ptr(), self.codebook.data_ptr(),
                             self.pool.data_ptr(), self.pool_bytes, self.slots.data_ptr())
         self.tier = _lib.ExpertTier(n_experts, self.host_pool.data_ptr(), host_slots,
@@ -145,6 +148,33 @@ def tiered_forward(step: "Step", layer: TieredLayer, x: torch.Tensor):
     step.fc1(x)
     step.fc2(T)
     return step.y[:T], n
+
+
+def cpu_miss_forward(step: "Step", layer: TieredLayer, x: torch.Tensor, n_threads: Optional[int] = None):
+    """One step with the CPU miss path: route on the GPU; the selected experts that hold a
+    device slot run on the GPU (FC1, FC2), and at the same time the host cores compute the
+    others from the tier's host pool (moe_vq_cpu_experts); y is the sum.  No expert is
+    copied.  Returns (y view [T, H] on the device, list of experts computed on the host).
+    The GPU step's status reports the lowest expert it left out, which the host computed."""
+    T = x.shape[0]
+    step.route(x)
+    ids = step.ids[:T].cpu()  # (synchronises the stream: the routing is needed here)
+    w = step.w[:T].cpu()
+    x_host = x.cpu()
+    held = set(e for e in layer.tier.held() if e >= 0)
+    miss = sorted(set(int(e) for e in ids.reshape(-1).tolist()) - held)
+    step.fc1(x)
+    step.fc2(T)  # (asynchronous: the host computes its experts meanwhile)
+    y_host = torch.zeros((T, layer.hidden), dtype=torch.float32)
+    if miss:
+        compute = torch.zeros(layer.n_experts, dtype=torch.uint8)
+        compute[miss] = 1
+        threads = n_threads or max(1, min(64, len(os.sched_getaffinity(0))))
+        _lib.cpu_experts(layer.c, layer.host_pool.data_ptr(), layer.host_pool.numel(), layer.tier._host_slots,
+                         layer.codebook_host.data_ptr(), x_host.data_ptr(), x_dtype_code(x), T, ids.data_ptr(),
+                         w.data_ptr(), compute.data_ptr(), y_host.data_ptr(), threads)
+        step.y[:T].add_(y_host.to(layer.device))
+    return step.y[:T], miss
 
 
 def x_dtype_code(x: torch.Tensor) -> int:

@@ -274,6 +274,26 @@ int moe_vq_tier_plan(const moe_vq_tier *tier, int n_experts, const int32_t *acti
 int moe_vq_tier_resolve(const moe_vq_layer *layer, moe_vq_tier *tier, uint8_t *pool, moe_vq_slot *slots,
                         int n_tokens, const void *ws, void *stream, int32_t *n_installed);
 
+/* [host] The CPU miss path: routed experts computed on the host cores, for the experts
+ * of a step that are not resident in the device pool, while the GPU computes the resident
+ * ones (Tandem-vLLM 0.2.0 announcement, "How it works": experts that miss the GPU's cache
+ * are computed by the CPU in parallel with the GPU; "What you need": an AVX2 or AVX-512
+ * CPU).  For every pair p = t*k + i with compute[topk_ids[p]] != 0 it adds
+ * topk_w[p] * W_d (silu(W_g x_t) * (W_u x_t)) to y[t], the expert's matrices read from its
+ * slot in host_pool (host_slots[e], the device pool's slot layout) and decoded exactly;
+ * fp32 products and sums; experts in ascending id, pairs in order.  Only layer's four
+ * sizes are read (its pointers are device memory and are not used).  All pointers are
+ * host memory: host_pool [host_pool_bytes], host_slots [E], codebook fp16 [128][4], x
+ * [n_tokens][H] in x_dtype, topk_ids and topk_w [n_tokens][k], compute u8 [E], y fp32
+ * [n_tokens][H] (accumulated, not overwritten).  n_threads host threads (1..256) run
+ * the call and are joined before it returns.  Errors: MOE_VQ_EINVAL for a bad argument
+ * or an expert id out of range; MOE_VQ_ENOTRESIDENT when an expert to compute has no
+ * slot in the host pool (nothing is added then). */
+int moe_vq_cpu_experts(const moe_vq_layer *layer, const uint8_t *host_pool, uint64_t host_pool_bytes,
+                       const moe_vq_slot *host_slots, const void *codebook, const void *x, int x_dtype,
+                       int n_tokens, const int32_t *topk_ids, const float *topk_w, const uint8_t *compute,
+                       float *y, int n_threads);
+
 /* [host] Text of the last HIP runtime error seen by a call of this library on the
  * calling thread (the reason behind MOE_VQ_EHIP), or "" if none. */
 const char *moe_vq_last_hip_error(void);
