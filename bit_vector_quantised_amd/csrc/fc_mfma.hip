@@ -15,11 +15,12 @@
 // happens inside the matrix core, with no per-row cross-lane sums.
 //
 // A operand: held in registers for the whole token group, never in LDS, so that the
-// only LDS traffic of the inner loop is the codebook lookups.  FC1 takes the staged
-// fp16 x (one power-of-two factor per token and 1024 columns, exact for bf16 x); FC2
-// converts the fp32 h of each pair to fp16 with one power-of-two factor per 128-column
-// scale group.  The factor multiplies the group's product in fp32; FC2's routing weight
-// multiplies each pair's output in fp32.
+// only LDS traffic of the inner loop is the codebook lookups.  Each wave holds its part
+// of K of the group's activations in fp16 with one power-of-two factor per token (FC1:
+// the staged x, brought to a common factor over the part, exact for bf16 x) or per pair
+// (FC2: fp32 h rounded to fp16).  The factor multiplies the wave's partial sums once
+// per tile, so a scale group costs four fp32 FMAs beyond its matrix ops; FC2's routing
+// weight multiplies each pair's output in fp32.
 //
 // MXFP4 B operand: a lane's 32 weights of a group are one E8M0 block.  The four blocks of
 // a 128-wide group (held by the four lanes of a row) share one product, so each block is
@@ -66,6 +67,7 @@ struct MfGeom {
   static constexpr int K = 1024 * CPL;
   static constexpr int NM = FC1 ? 2 : 1;
   static constexpr int NGQ = 8 * CPL / W;  // 128-wide scale groups in a wave's part of K
+  static constexpr int KS = CPL;           // activation slices of 1024 columns (FC1 factors)
   static constexpr int NPAIR = NGQ / 2;  // groups read two at a time (16-byte loads)
   static constexpr bool ODD = (NGQ & 1) != 0;  // the last group is read alone (8 bytes)
   // 16-row blocks per tile: ring slots per wave for several KB of codes in flight (a
@@ -76,8 +78,6 @@ struct MfGeom {
   static constexpr int NB_CAP = W == 8 ? (FC1 ? 4 : 8) : 8 / NM;
   static constexpr int NB = NB_RULE < NB_CAP ? NB_RULE : NB_CAP;
   static constexpr int ROWS = 16 * NB;
-  static constexpr int KS = CPL;       // activation slices of 1024 columns (FC1 factors)
-  static constexpr int NSLW = (NGQ + 6) / 8 + 1;  // slices a wave's groups can touch
   static constexpr int QS = ROWS + 1;  // LDS stride of one token's partial sums
   static constexpr int RED = W * NM * MF_MT * QS;  // floats per reduction buffer
   static constexpr int NBUF = (size_t)TAB_BYTES + 2 * (size_t)RED * 4 <= (size_t)150 * 1024 ? 2 : 1;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   using G = MfGeom<CPL, FC1>;
   constexpr int MF_WAVES = G::W, MF_THREADS = G::THREADS;
   constexpr int K = G::K, NM = G::NM, NB = G::NB, ROWS = G::ROWS, NGQ = G::NGQ, KS = G::KS;
-  constexpr int NPAIR = G::NPAIR, QS = G::QS, RED = G::RED, NBUF = G::NBUF, NSLW = G::NSLW;
+  constexpr int NPAIR = G::NPAIR, QS = G::QS, RED = G::RED, NBUF = G::NBUF;
   constexpr bool ODD = G::ODD;
   // LDS, in one array so that the decode table starts at address 0: a lookup's address
   // is then the v_perm result itself (past 64 KB it would need an add per lookup, the
@@ -161,38 +161,34 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 
   // ---- activations of the current token group, in registers
   half8_t A[NGQ][4];                            // A fragments, group gi, step s
-  float fx1[FC1 ? NSLW : 1][4];                 // FC1: factor of D row r, slice sl0 + j
-  float fx2[FC1 ? 1 : NGQ][4];                  // FC2: factor of D row r, group gi
+  float fw[4];                                  // factor of D row 4 kq + r (0 past the group)
   float4 A32[FC1 ? 1 : NGQ][8];                 // FC2: the next group's h, as loaded
 
-  // Per-lane token (FC1) or pair (FC2) of A row i16 and of the lane's four D rows
-  // (4 kq + r) for group record r; padding rows repeat the last real one.
+  // Per-lane pair of A row i16 for group record r; padding rows repeat the last real one.
   struct Tok {
     int arow;
-    int drow[4];
   };
   auto tok_load = [&](const RecS& r) __attribute__((always_inline)) -> Tok {
     Tok t;
-    const int last = r.mcount - 1;
-    t.arow = a.pair_list[r.p0 + min(i16, last)];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) t.drow[q] = FC1 ? a.pair_list[r.p0 + min(4 * kq + q, last)] : 0;
+    t.arow = a.pair_list[r.p0 + min(i16, r.mcount - 1)];
     return t;
   };
-  // Issue the loads of a token group's activations (FC1: fp16 x and its factors; FC2:
-  // fp32 h, converted by convert_h when the group's first tile starts).
+  // Issue the loads of a token group's activations (FC1: the staged fp16 x and its
+  // slice factors; FC2: fp32 h), converted by convert_x / convert_h.
   // The token rows of the next group are loaded at the top of a tile and used after it:
   // arithmetic on them next to their load would wait there for every older load, i.e.
   // for the ring in flight.  This fence keeps their first use where it is written.
   auto tok_fence = [&](const Tok& t_in) __attribute__((always_inline)) -> Tok {
     Tok t;
     t.arow = opaque(t_in.arow);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) t.drow[q] = FC1 ? opaque(t_in.drow[q]) : 0;
     return t;
   };
   float hw = 0.f;  // FC2: routing weight of the pair of A row i16 (kept in LDS for the output)
+  // FC1: slice factors of A row i16's token for the (at most two) 1024-column slices
+  // the wave's groups touch
+  float xs[2];
   auto act_load = [&](const Tok& t, const RecS& r) __attribute__((always_inline)) {
+    (void)r;
     if (FC1) {
       const int tokA = t.arow / a.k;
       const uint16_t* xr = a.x_h + (size_t)tokA * K + 32 * pq;
@@ -201,15 +197,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 #pragma unroll
         for (int s = 0; s < 4; ++s) A[gi][s] = *reinterpret_cast<const half8_t*>(xr + gid(gi) * 128 + 8 * s);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int tokD = t.drow[q] / a.k;
-        const bool live = 4 * kq + q < r.mcount;
-#pragma unroll
-        for (int j = 0; j < (FC1 ? NSLW : 1); ++j) {
-          const float v = a.x_sc[(size_t)tokD * KS + min(sl0 + j, KS - 1)];
-          fx1[j][q] = live ? v : 0.f;
-        }
-      }
+      for (int j = 0; j < 2; ++j) xs[j] = a.x_sc[(size_t)tokA * KS + min(sl0 + j, KS - 1)];
     } else {
       hw = a.pair_w[t.arow];
       const float* hr = a.h_in + (size_t)t.arow * K + 32 * pq;
@@ -219,48 +207,68 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
         for (int i = 0; i < 8; ++i) A32[FC1 ? 0 : gi][i] = *reinterpret_cast<const float4*>(hr + gid(gi) * 128 + 4 * i);
     }
   };
-  // FC2: fp32 h -> fp16 A fragments with one power-of-two factor per (pair, group); the
-  // factor of D row r (pair 4 kq + r) comes from the lanes holding that A row.
-  auto convert_h = [&](const RecS& r) __attribute__((always_inline)) {
-    if (!FC1) {
+  // D row 4 kq + r takes the factor f of A row 4 kq + r (0 past the group's tokens)
+  auto row_factors = [&](float f, const RecS& r) __attribute__((always_inline)) {
 #pragma unroll
-      for (int gi = 0; gi < NGQ; ++gi) {
-        const int gk = FC1 ? 0 : gi;
-        float m = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          m = fmaxf(m, fmaxf(fmaxf(fabsf(A32[gk][i].x), fabsf(A32[gk][i].y)),
-                             fmaxf(fabsf(A32[gk][i].z), fabsf(A32[gk][i].w))));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        int ex = 0;
-        if (m > 0.f && m < INFINITY) ex = frexp_exponent(m) - 15;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float4 u = A32[gk][2 * s], v = A32[gk][2 * s + 1];
-          A[gi][s] = half8_t{(_Float16)ldexp2(u.x, -ex), (_Float16)ldexp2(u.y, -ex), (_Float16)ldexp2(u.z, -ex),
-                             (_Float16)ldexp2(u.w, -ex), (_Float16)ldexp2(v.x, -ex), (_Float16)ldexp2(v.y, -ex),
-                             (_Float16)ldexp2(v.z, -ex), (_Float16)ldexp2(v.w, -ex)};
-        }
-        const float f = ldexp2(1.0f, ex);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v = __shfl(f, 4 * kq + q);
-          fx2[gk][q] = 4 * kq + q < r.mcount ? v : 0.f;
-        }
-      }
+    for (int q = 0; q < 4; ++q) {
+      const float v = __shfl(f, 4 * kq + q);
+      fw[q] = 4 * kq + q < r.mcount ? v : 0.f;
     }
   };
-  // factor of D row q for group gi of the wave's part
-  auto factor = [&](int gi, int q) __attribute__((always_inline)) -> float {
+  // FC1: the staged x has one power-of-two factor per (token, 1024-column slice), 0 for
+  // an all-zero slice.  The wave's part takes the largest factor F of the slices it
+  // touches, and the A fragments of a slice with factor f are multiplied by f / F (a
+  // power of two, at most 1), exactly unless a result falls below fp16's normal range
+  // with bits to lose: for bf16 x, values more than 2^32 below the largest of their
+  // part.
+  auto convert_x = [&](const RecS& r) __attribute__((always_inline)) {
     if (FC1) {
-      const int j = (gid(gi) >> 3) - sl0;  // uniform; picks among the wave's slices
-      float f = fx1[0][q];
+      const bool two = ((g0 + NGQ - 1) >> 3) > sl0;  // uniform: the part spans two slices
+      const float F = two ? fmaxf(xs[0], xs[1]) : xs[0];
+      const int eF = frexp_exponent(F);
+      _Float16 rs[2];
 #pragma unroll
-      for (int i = 1; i < (FC1 ? NSLW : 1); ++i) f = j == i ? fx1[i][q] : f;
-      return f;
+      for (int j = 0; j < 2; ++j)
+        rs[j] = xs[j] > 0.f ? (_Float16)ldexp2(1.0f, frexp_exponent(xs[j]) - eF) : (_Float16)0.f;
+#pragma unroll
+      for (int gi = 0; gi < NGQ; ++gi) {
+        const int j = (gid(gi) >> 3) - sl0;  // uniform
+        const _Float16 m = j == 0 ? rs[0] : rs[1];
+        const half8_t mv = {m, m, m, m, m, m, m, m};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) A[gi][s] = A[gi][s] * mv;
+      }
+      row_factors(F, r);
     }
-    return fx2[FC1 ? 0 : gi][q];
+  };
+  // FC2: fp32 h -> fp16 A fragments with one power-of-two factor per (pair, wave part).
+  auto convert_h = [&](const RecS& r) __attribute__((always_inline)) {
+    if (!FC1) {
+      float m = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < NGQ; ++gi)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 u = A32[FC1 ? 0 : gi][i];
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w))));
+        }
+      // the largest |h| of the row's part (the four lanes of the row hold a quarter
+      // each), scaled below 2^15
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      int ex = 0;
+      if (m > 0.f && m < INFINITY) ex = frexp_exponent(m) - 15;
+      row_factors(ldexp2(1.0f, ex), r);
+#pragma unroll
+      for (int gi = 0; gi < NGQ; ++gi)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float4 u = A32[FC1 ? 0 : gi][2 * s], w = A32[FC1 ? 0 : gi][2 * s + 1];
+          A[gi][s] = half8_t{(_Float16)ldexp2(u.x, -ex), (_Float16)ldexp2(u.y, -ex), (_Float16)ldexp2(u.z, -ex),
+                             (_Float16)ldexp2(u.w, -ex), (_Float16)ldexp2(w.x, -ex), (_Float16)ldexp2(w.y, -ex),
+                             (_Float16)ldexp2(w.z, -ex), (_Float16)ldexp2(w.w, -ex)};
+        }
+    }
   };
 
   // Addresses of one tile's codes in the ring's shape: uniform matrix bases, 32-bit
@@ -346,12 +354,14 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
       bfr[s] = __builtin_bit_cast(half8_t, make_uint4(e0.x, e0.y, e1.x, e1.y));
     }
   };
+  // (the activation factors are one per D row for the wave's whole part of K: they
+  // multiply the tile's sums once, after its last group)
   auto group_mma = [&](int gi, const half8_t (&bfr)[4], float sc, f32x4_t& ac) __attribute__((always_inline)) {
     f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[gi][s], bfr[s], tmp, 0, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ac[q] = fmaf(sc * factor(gi, q), tmp[q], ac[q]);
+    for (int q = 0; q < 4; ++q) ac[q] = fmaf(sc, tmp[q], ac[q]);
   };
 
   // VQ2 tile: consume the ring, refilling each slot with the next tile's codes.  Slot j
@@ -607,8 +617,8 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   if (tid < 256) write_table_entry(tab, cbv, tid);  // (every block has >= 256 threads)
   __syncthreads();
 
-  bool fresh = true;  // the tile is the first of its token group (FC2 converts h)
-  if (!FC1) { convert_h(rc); fresh = false; }
+  if (FC1) convert_x(rc);
+  else convert_h(rc);
   int buf = 0, gb = 0;
   for (;;) {
     const int tn = t + 1;
@@ -618,7 +628,6 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     const bool next_group = more && tn / RB != t / RB;
     Tok tk;  // (no initial value: writing one would wait for the last group's row loads)
     if (next_group) tk = tok_load(rn);
-    if (fresh) convert_h(rc);
     zero_acc();
     // The ring is defined in this branch only (a second definition elsewhere in the loop
     // makes the compiler keep it in other registers and copy it back at the loop's back
@@ -631,11 +640,20 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
       compute_mx(rc, t % RB);
     }
     // (an absent expert keeps zeros; the worklist has recorded MOE_VQ_ENOTRESIDENT)
+    // The activation factors of this token group, before a group change replaces them.
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[m][nb][q] *= fw[q];
     ring_ok = rc.fmt == MOE_VQ_FMT_VQ2 && next_vq;
     if (next_group) {
       tk = tok_fence(tk);
       act_load(tk, rn);  // this tile was the last use of the activations
-      if (!FC1) convert_h(rn);  // (waits for the h loads here: fp32 h is not kept across tiles)
+      // (waits for the loads here: fp32 h and bf16 x are not kept across tiles)
+      if (FC1) convert_x(rn);
+      else convert_h(rn);
       // The activations are complete before the next tile, on this path: otherwise the
       // tile body would carry a wait for them that, on every other tile, waits for the
       // ring in flight too.  (s_waitcnt vmcnt(0); expcnt and lgkmcnt left alone.)
@@ -644,7 +662,6 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     finish(rc, t % RB, buf, gb, next_group, tk.arow);
     if (!more) break;
     if (next_group) gb ^= 1;
-    fresh = false;
     rc = rn;
     rn = rnn;
     t = tn;

@@ -18,7 +18,8 @@ constexpr int RT_TOKENS = 32;   // tokens per router workgroup
 // [T][E][ksp] (slice fastest, ksp = slices rounded up to 4) so the top-k stage sums
 // them with 16-byte loads.  (The matrix-core router writes complete logits, ksp = 1.)
 // Workgroups of expert group 0 also stage x as fp16 with a power-of-two factor per
-// (token, slice): x = x_h * x_sc exactly for bf16 inputs (|x_h| < 2^15).
+// (token, slice): x = x_h * x_sc exactly for bf16 inputs (|x_h| < 2^15; x_sc = 0 for an
+// all-zero slice).
 template <bool XF32>
 __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -149,7 +150,8 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouteArgs a) {
             dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
             dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
           }
-          if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = ldexpf(1.0f, ex);
+          // (an all-zero slice has factor 0, so that it never sets a common factor)
+          if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = m == 0.f ? 0.f : ldexpf(1.0f, ex);
         }
       }
     }
@@ -421,7 +423,8 @@ __device__ __forceinline__ void stage_x_row(const RouteArgs& a, int t, int s, in
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
   }
-  if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = ldexp2(1.0f, ex);
+  // (an all-zero slice has factor 0, so that it never sets a common factor)
+  if (lane == 0) a.x_sc[(size_t)t * a.KS + s] = m == 0.f ? 0.f : ldexp2(1.0f, ex);
 }
 
 template <bool XF32>
