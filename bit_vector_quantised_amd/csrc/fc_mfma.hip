@@ -92,20 +92,45 @@ struct MfGeom {
     return best;
   }
   static constexpr int MXG = mxg();
+  // VQ2 scales staged through LDS (SST): a tile's scale rows are contiguous per matrix,
+  // so the workgroup reads them with one 16-byte load per thread instead of one 4-byte
+  // load per lane and group pair (16 rows per instruction: half of the memory requests
+  // for 3 % of the bytes).  Measured faster for FC2 and the small-K kernels, slightly
+  // slower for FC1 at K = 7168, which keeps its scales in the ring.  Bytes per row, LDS
+  // row stride (an odd number of dwords: the 16 rows a wave reads at once fall in
+  // distinct banks), 16-byte chunks per row, chunks per tile, bytes per buffer.
+  static constexpr bool SST = !(FC1 && CPL >= 4);
+  static constexpr int SROWB = K / 64;
+  static constexpr int SRS = SROWB + 4;
+  static constexpr int SCH = SROWB / 16;
+  static constexpr int SCHUNKS = NM * ROWS * SCH;
+  static constexpr int SCB = NM * ROWS * SRS;
+  static_assert(!SST || SCHUNKS <= THREADS, "one 16-byte chunk of scales per thread");
 };
 
 // VQ2 codes one lane holds for one (group pair, matrix, row block): 16 code bytes (8 of
-// each group once swapped) and the two groups' fp16 scale bits.  Pairs start at an even
-// group, so the two scales are one aligned dword.
+// each group once swapped) and, where the scales are not staged through LDS (RS), the
+// two groups' fp16 scale bits.  Pairs start at an even group, so the two scales are one
+// aligned dword.
+template <bool RS>
 struct MfPair {
   uint4 q;
   uint32_t s;  // scale bits: low half the first group, high half the second
 };
+template <>
+struct MfPair<false> {
+  uint4 q;
+};
 
 // The same for a group read alone.
+template <bool RS>
 struct MfOne {
   uint2 q;
   uint32_t s;
+};
+template <>
+struct MfOne<false> {
+  uint2 q;
 };
 
 // MXFP4 codes of one (group, matrix, row block): 16 bytes (32 weights, one E8M0 block).
@@ -121,18 +146,25 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   constexpr int K = G::K, NM = G::NM, NB = G::NB, ROWS = G::ROWS, NGQ = G::NGQ, KS = G::KS;
   constexpr int NPAIR = G::NPAIR, QS = G::QS, RED = G::RED, NBUF = G::NBUF;
   constexpr bool ODD = G::ODD;
+  constexpr bool SST = G::SST;
+  constexpr int SROWB = G::SROWB, SRS = G::SRS, SCH = G::SCH, SCHUNKS = G::SCHUNKS, SCB = G::SCB;
+  using Pair = MfPair<!SST>;
+  using One = MfOne<!SST>;
   // LDS, in one array so that the decode table starts at address 0: a lookup's address
   // is then the v_perm result itself (past 64 KB it would need an add per lookup, the
   // immediate offset of a ds_read being 16 bits).  Then the per-wave partial sums, and
   // the pair of each token row of the current and the next token group: the outputs'
   // rows, read from LDS rather than from global memory at the end of every tile (a load
-  // there would wait for every older load, i.e. for the ring in flight).
-  __shared__ __attribute__((aligned(16))) uint8_t lds[TAB_BYTES + NBUF * RED * 4 + 2 * MF_MT * 4 * (FC1 ? 1 : 2)];
+  // there would wait for every older load, i.e. for the ring in flight).  Last (SST),
+  // the VQ2 scales of the current and the next tile.
+  constexpr int LDS_SC = TAB_BYTES + NBUF * RED * 4 + 2 * MF_MT * 4 * (FC1 ? 1 : 2);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_SC + (SST ? 2 * SCB : 0)];
   uint2* const tab = reinterpret_cast<uint2*>(lds);
   float* const red = reinterpret_cast<float*>(lds + TAB_BYTES);
   int (*const s_pair)[MF_MT] = reinterpret_cast<int (*)[MF_MT]>(lds + TAB_BYTES + NBUF * RED * 4);
   // FC2: the routing weight of each token row, next to its pair
   float (*const s_w)[MF_MT] = reinterpret_cast<float (*)[MF_MT]>(lds + TAB_BYTES + NBUF * RED * 4 + 2 * MF_MT * 4);
+  uint8_t* const sc_lds = lds + LDS_SC;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, kq = lane >> 4;
@@ -321,19 +353,54 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     d.ds1 = mx ? 0u - us0 : lone_ds;
     return d;
   };
-  auto load_pair = [&](const MfAddr& d, int pi, int m, int nb) __attribute__((always_inline)) -> MfPair {
-    MfPair c;
+  auto load_pair = [&](const MfAddr& d, int pi, int m, int nb) __attribute__((always_inline)) -> Pair {
+    Pair c;
     c.q = *reinterpret_cast<const uint4*>(d.qb[m] + d.qo[nb] + pi * 64);
-    c.s = *reinterpret_cast<const uint32_t*>(d.sb[m] + d.so[nb] + pi * 4);
+    if constexpr (!SST) c.s = *reinterpret_cast<const uint32_t*>(d.sb[m] + d.so[nb] + pi * 4);
     return c;
   };
-  auto load_one = [&](const MfAddr& d, int m, int nb) __attribute__((always_inline)) -> MfOne {
-    MfOne c;
+  auto load_one = [&](const MfAddr& d, int m, int nb) __attribute__((always_inline)) -> One {
+    One c;
     // (the sums wrap in 32 bits: the lone group can lie before slot 0; the true sum is
     // never negative)
     c.q = *reinterpret_cast<const uint2*>(d.qb[m] + (uint32_t)(d.qo[nb] + d.dq1));
-    c.s = *reinterpret_cast<const uint16_t*>(d.sb[m] + (uint32_t)(d.so[nb] + d.ds1));
+    if constexpr (!SST) c.s = *reinterpret_cast<const uint16_t*>(d.sb[m] + (uint32_t)(d.so[nb] + d.ds1));
     return c;
+  };
+
+  // SST: thread tid's 16-byte chunk of a tile's scales is loaded at the start of the
+  // previous tile (before its ring refills, so that waiting for it never waits for
+  // them) and written to LDS before that tile's closing barrier.  Buffer sbuf holds the
+  // current tile's scales, sbuf ^ 1 the next tile's.
+  int sbuf = 0;
+  const bool sc_thr = tid < SCHUNKS;
+  const int sc_m = tid / (ROWS * SCH), sc_r = (tid / SCH) % ROWS, sc_j = tid % SCH;
+  const uint32_t sc_wr = (uint32_t)((sc_m * ROWS + sc_r) * SRS + 16 * sc_j);
+  const uint32_t sc_rd = (uint32_t)(i16 * SRS + 2 * gpair);  // the lane's row, first pair
+  uint4 scv = make_uint4(0u, 0u, 0u, 0u);
+  auto sc_load = [&](const RecS& r, int rb) __attribute__((always_inline)) {
+    if (sc_thr) {
+      const uint8_t* slot = a.pool + r.slot_off;
+      const uint8_t* sbm = slot + (sc_m == 0 ? (FC1 ? a.vq2.s_gate : a.vq2.s_down) : a.vq2.s_up);
+      const uint32_t n = (uint32_t)min(rb * ROWS + sc_r, NROWS - 1);
+      scv = *reinterpret_cast<const uint4*>(sbm + n * (uint32_t)SROWB + 16 * sc_j);
+    }
+  };
+  auto sc_store = [&](int b) __attribute__((always_inline)) {
+    if (sc_thr) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(sc_lds + b * SCB + sc_wr);
+      dst[0] = scv.x;
+      dst[1] = scv.y;
+      dst[2] = scv.z;
+      dst[3] = scv.w;
+    }
+  };
+  // the two scales of pair slot pi (row block nb of matrix m), and the lone group's
+  auto sc_pair = [&](int m, int nb, int pi) __attribute__((always_inline)) -> uint32_t {
+    return *reinterpret_cast<const uint32_t*>(sc_lds + sbuf * SCB + (m * ROWS + nb * 16) * SRS + sc_rd + 4 * pi);
+  };
+  auto sc_lone = [&](int m, int nb) __attribute__((always_inline)) -> uint32_t {
+    return *reinterpret_cast<const uint16_t*>(sc_lds + sbuf * SCB + (m * ROWS + nb * 16) * SRS + sc_rd + 2 * (gone - gpair));
   };
 
   f32x4_t acc[NM][NB];
@@ -371,8 +438,8 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   // latency hides behind them.  The refill is issued for every slot; without a next
   // VQ2 tile it re-reads this tile's codes (cache hits), which keeps the loop free of
   // branches.
-  MfPair ringP[NPAIR > 0 ? NPAIR : 1][NM][NB];
-  MfOne ringS[ODD ? NM : 1][ODD ? NB : 1];
+  Pair ringP[NPAIR > 0 ? NPAIR : 1][NM][NB];
+  One ringS[ODD ? NM : 1][ODD ? NB : 1];
   constexpr int NPS = NPAIR * NM * NB;                // pair slots
   constexpr int NU = 2 * NPS + (ODD ? NM * NB : 0);   // units
   struct UDec {
@@ -388,12 +455,14 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
       if ((u & 1) == 0) {
         // the slot is consumed (swap, scales) before its refill is issued, so the refill
         // can land in the same registers
-        const MfPair c = ringP[pi][m][nb];
+        const Pair c = ringP[pi][m][nb];
         const auto lo = __builtin_amdgcn_permlane32_swap(reg_copy(c.q.x), reg_copy(c.q.z), false, false);
         const auto hi = __builtin_amdgcn_permlane32_swap(reg_copy(c.q.y), reg_copy(c.q.w), false, false);
         pw2 = lo[1];
         pw3 = hi[1];
-        const uint32_t cs = reg_copy(c.s);
+        uint32_t cs;
+        if constexpr (SST) cs = sc_pair(m, nb, pi);
+        else cs = reg_copy(c.s);
         ps = cs >> 16;
         d.sc = f16_bits_to_f32(cs & 0xFFFFu);
         ringP[pi][m][nb] = load_pair(dn, pi, m, nb);
@@ -404,9 +473,10 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
       }
     } else {
       const int m = ((u - 2 * NPS) / NB) % NM, nb = (u - 2 * NPS) % NB;
-      const MfOne c = ringS[ODD ? m : 0][ODD ? nb : 0];
+      const One c = ringS[ODD ? m : 0][ODD ? nb : 0];
       const uint32_t c0 = reg_copy(c.q.x), c1 = reg_copy(c.q.y);
-      d.sc = f16_bits_to_f32(reg_copy(c.s));
+      if constexpr (SST) d.sc = f16_bits_to_f32(sc_lone(m, nb));
+      else d.sc = f16_bits_to_f32(reg_copy(c.s));
       ringS[ODD ? m : 0][ODD ? nb : 0] = load_one(dn, m, nb);
       b_frags(c0, c1, d.b);
     }
@@ -576,18 +646,21 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) ringP[pi][m][nb] = MfPair{make_uint4(0u, 0u, 0u, 0u), 0u};
+        for (int nb = 0; nb < NB; ++nb) ringP[pi][m][nb] = Pair{};
 #pragma unroll
     for (int m = 0; m < (ODD ? NM : 1); ++m)
 #pragma unroll
-      for (int nb = 0; nb < (ODD ? NB : 1); ++nb) ringS[m][nb] = MfOne{make_uint2(0u, 0u), 0u};
+      for (int nb = 0; nb < (ODD ? NB : 1); ++nb) ringS[m][nb] = One{};
   };
 
-  // Records are read one tile ahead of their use (rn is needed for the refill addresses
-  // while this tile decodes).  They are read-only for the whole launch, so they are read
-  // through the constant address space, i.e. with scalar loads: a vector load's value
-  // waits for every older vector load (they complete in order), here the whole ring in
-  // flight.
+  // A workgroup's tiles run group by group (row blocks of one token group, then the
+  // next group's), so a record is needed once per group change: the current group's and
+  // the next one's are held, and the record after them is read when the group changes.
+  // Records are read-only for the whole launch and read through the constant address
+  // space (scalar loads): a vector load's value waits for every older vector load (they
+  // complete in order), here the whole ring in flight.  A scalar load in flight holds up
+  // every LDS wait of the wave (they share a counter), so it is issued only where the
+  // group change drains the loads anyway, never once per tile.
   typedef const int __attribute__((address_space(4))) cint_t;
   auto load_rec_c = [&](int g) __attribute__((always_inline)) -> RecS {
     cint_t* w = reinterpret_cast<cint_t*>(reinterpret_cast<uintptr_t>(a.rec + g));
@@ -599,15 +672,29 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     return r;
   };
 
+  auto sel_rec = [&](bool c, const RecS& x, const RecS& y) __attribute__((always_inline)) -> RecS {
+    RecS r{};
+    r.slot_off = c ? x.slot_off : y.slot_off;
+    r.p0 = c ? x.p0 : y.p0;
+    r.mcount = c ? x.mcount : y.mcount;
+    r.fmt = c ? x.fmt : y.fmt;
+    return r;
+  };
+
   // ---- prologue
   int t = t_begin;
-  const RecRaw raw_c = load_rec_raw(a.rec, t / RB);
-  const RecRaw raw_n = load_rec_raw(a.rec, (t + 1 < t_end ? t + 1 : t) / RB);
+  int g = t / RB, rb = t - g * RB;      // the tile's token group and row block
+  const int g_last = (t_end - 1) / RB;  // the last group of the workgroup's tiles
+  const RecRaw raw_c = load_rec_raw(a.rec, g);
+  const RecRaw raw_n = load_rec_raw(a.rec, min(g + 1, g_last));
   RecS rc = rec_from_raw(raw_c);
-  RecS rn = rec_from_raw(raw_n);
+  RecS rg1 = rec_from_raw(raw_n);  // the next group (the last one again at the end)
   const Tok t0 = tok_load(rc);
   act_load(t0, rc);
-  if (rc.fmt == MOE_VQ_FMT_VQ2) ring_load(rc, t % RB);
+  if (rc.fmt == MOE_VQ_FMT_VQ2) {
+    if (SST) sc_load(rc, rb);
+    ring_load(rc, rb);
+  }
   // (after the ring's loads: the weight's load is then waited for with the ring in flight)
   if (wave == 0 && kq == 0) {
     s_pair[0][i16] = t0.arow;
@@ -615,17 +702,19 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   }
   bool ring_ok = rc.fmt == MOE_VQ_FMT_VQ2;  // the ring holds this tile's codes
   if (tid < 256) write_table_entry(tab, cbv, tid);  // (every block has >= 256 threads)
+  if (SST && rc.fmt == MOE_VQ_FMT_VQ2) sc_store(0);
   __syncthreads();
 
   if (FC1) convert_x(rc);
   else convert_h(rc);
   int buf = 0, gb = 0;
   for (;;) {
-    const int tn = t + 1;
-    const bool more = tn < t_end;
-    const RecS rnn = load_rec_c((tn + 1 < t_end ? tn + 1 : tn) / RB);  // (a valid record either way)
+    const bool more = t + 1 < t_end;
+    const bool next_group = more && rb + 1 == RB;
+    const int rbn = next_group ? 0 : rb + 1;  // the next tile's row block
+    const RecS rn = sel_rec(next_group, rg1, rc);
     const bool next_vq = more && rn.fmt == MOE_VQ_FMT_VQ2;  // the ring takes the next tile's codes
-    const bool next_group = more && tn / RB != t / RB;
+    if (SST && next_vq) sc_load(rn, rbn);  // (before this tile's refills)
     Tok tk;  // (no initial value: writing one would wait for the last group's row loads)
     if (next_group) tk = tok_load(rn);
     zero_acc();
@@ -634,10 +723,10 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     // edge, waiting for every load in flight).  After a tile of another format it is
     // stale, and the VQ2 tile loads its own codes first.
     if (rc.fmt == MOE_VQ_FMT_VQ2) {
-      if (!ring_ok) ring_load(rc, t % RB);
-      compute_vq(next_vq, rn, tn % RB, rc, t % RB);  // refills the ring with tile tn's codes
+      if (!ring_ok) ring_load(rc, rb);
+      compute_vq(next_vq, rn, rbn, rc, rb);  // refills the ring with the next tile's codes
     } else if (rc.fmt == MOE_VQ_FMT_MXFP4) {
-      compute_mx(rc, t % RB);
+      compute_mx(rc, rb);
     }
     // (an absent expert keeps zeros; the worklist has recorded MOE_VQ_ENOTRESIDENT)
     // The activation factors of this token group, before a group change replaces them.
@@ -648,23 +737,31 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[m][nb][q] *= fw[q];
     ring_ok = rc.fmt == MOE_VQ_FMT_VQ2 && next_vq;
+    RecS rg2 = rg1;
     if (next_group) {
+      rg2 = load_rec_c(min(g + 2, g_last));  // the group after the next one
       tk = tok_fence(tk);
       act_load(tk, rn);  // this tile was the last use of the activations
       // (waits for the loads here: fp32 h and bf16 x are not kept across tiles)
       if (FC1) convert_x(rn);
       else convert_h(rn);
-      // The activations are complete before the next tile, on this path: otherwise the
-      // tile body would carry a wait for them that, on every other tile, waits for the
-      // ring in flight too.  (s_waitcnt vmcnt(0); expcnt and lgkmcnt left alone.)
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      // The activations and the record are complete before the next tile, on this
+      // path: otherwise the tile body would carry a wait for them that, on every other
+      // tile, waits for the ring in flight too.  (s_waitcnt vmcnt(0) lgkmcnt(0).)
+      __builtin_amdgcn_s_waitcnt(0x0070);
     }
-    finish(rc, t % RB, buf, gb, next_group, tk.arow);
+    if (SST && next_vq) sc_store(sbuf ^ 1);  // (read after finish's barrier)
+    finish(rc, rb, buf, gb, next_group, tk.arow);
     if (!more) break;
-    if (next_group) gb ^= 1;
-    rc = rn;
-    rn = rnn;
-    t = tn;
+    sbuf ^= 1;
+    if (next_group) {
+      gb ^= 1;
+      g += 1;
+      rc = rg1;
+      rg1 = rg2;
+    }
+    rb = rbn;
+    t += 1;
     buf ^= NBUF - 1;
   }
 }
