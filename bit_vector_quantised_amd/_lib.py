@@ -19,7 +19,7 @@ FMT_ABSENT, FMT_VQ2, FMT_MXFP4 = 0, 1, 2
 MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 
 EXPORTS = ("moe_vq_expert_bytes", "moe_vq_slot_layout", "moe_vq_workspace_bytes", "moe_vq_route_topk",
-           "moe_vq_fc1_silu", "moe_vq_fc2_combine", "moe_vq_forward", "moe_vq_forward_static", "moe_vq_prefill_gemm", "moe_vq_decode_expert",
+           "moe_vq_fc1_silu", "moe_vq_fc2_combine", "moe_vq_forward", "moe_vq_forward_static", "moe_vq_shared_expert", "moe_vq_prefill_gemm", "moe_vq_decode_expert",
            "moe_vq_check", "moe_vq_step_info", "moe_vq_tier_init", "moe_vq_tier_plan", "moe_vq_tier_resolve", "moe_vq_cpu_experts",
            "moe_vq_last_hip_error", "moe_vq_strerror")
 
@@ -38,7 +38,8 @@ class Slot(ctypes.Structure):
 class Layer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
-                ("pool", ctypes.c_void_p), ("pool_bytes", ctypes.c_uint64), ("slots", ctypes.c_void_p)]
+                ("pool", ctypes.c_void_p), ("pool_bytes", ctypes.c_uint64), ("slots", ctypes.c_void_p),
+                ("swiglu_limit", ctypes.c_float)]
 
 
 class Tier(ctypes.Structure):
@@ -72,6 +73,7 @@ def _load():
         "moe_vq_fc2_combine": (i32, [LP, vp, i32, vp, sz, vp, vp]),
         "moe_vq_forward": (i32, [LP, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "moe_vq_forward_static": (i32, [LP, vp, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "moe_vq_shared_expert": (i32, [LP, vp, i32, i32, vp, sz, vp, vp, vp]),
         "moe_vq_prefill_gemm": (i32, [LP, vp, i32, i32, vp, sz, vp, vp]),
         "moe_vq_decode_expert": (i32, [LP, i32, i32, i32, vp, vp, vp]),
         "moe_vq_check": (i32, [vp, vp, ctypes.POINTER(ctypes.c_int32)]),
@@ -148,6 +150,12 @@ def forward_static(layer: Layer, x: int, x_dtype: int, n_tokens: int, topk_ids: 
                    y: int, status: int = 0, stream: int = 0) -> None:
     _ok(_lib.moe_vq_forward_static(ctypes.byref(layer), x, x_dtype, n_tokens, topk_ids, topk_w, h, y, status,
                                    stream), "forward_static")
+
+
+def shared_expert(layer: Layer, x: int, x_dtype: int, n_tokens: int, ws: int, ws_bytes: int, h: int, y: int,
+                  stream: int = 0) -> None:
+    _ok(_lib.moe_vq_shared_expert(ctypes.byref(layer), x, x_dtype, n_tokens, ws, ws_bytes, h, y, stream),
+        "shared_expert")
 
 
 def prefill_gemm(layer: Layer, x: int, x_dtype: int, n_tokens: int, ws: int, ws_bytes: int, y: int,

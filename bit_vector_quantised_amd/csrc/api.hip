@@ -37,6 +37,7 @@ int check_layer(const moe_vq_layer* L) {
       ((uintptr_t)L->slots & 7))
     return MOE_VQ_EINVAL;
   if (L->pool_bytes == 0) return MOE_VQ_EINVAL;
+  if (!(L->swiglu_limit >= 0.f && L->swiglu_limit <= 3.4e38f)) return MOE_VQ_EINVAL;  // finite, >= 0 (NaN fails)
   return MOE_VQ_OK;
 }
 
@@ -83,6 +84,7 @@ FcArgs make_fc_args(const moe_vq_layer* L, int T, void* ws, const WsLayout& W, b
   a.KS = W.KS;
   a.E = L->n_experts;
   a.key = shape_key(T, L->n_experts, L->top_k, L->hidden, L->inter);
+  a.lim = L->swiglu_limit;
   a.vq2 = slot_layout(MOE_VQ_FMT_VQ2, L->hidden, L->inter);
   a.mx4 = slot_layout(MOE_VQ_FMT_MXFP4, L->hidden, L->inter);
   return a;
@@ -147,12 +149,14 @@ hipError_t fc1_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, void
   return launch_fc1(a, W.MT1, W.G1, device_cu_count(), stream);
 }
 
-hipError_t fc2_on(const moe_vq_layer* L, const float* h, int T, void* ws, float* y, hipStream_t stream) {
+hipError_t fc2_on(const moe_vq_layer* L, const float* h, int T, void* ws, float* y, hipStream_t stream,
+                  bool accumulate = false) {
   const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, T);
   FcArgs a = make_fc_args(L, T, ws, W, false);
   a.h_in = h;
   a.out = at<float>(ws, W.o_buf);
   a.y = y;
+  a.accumulate = accumulate ? 1 : 0;
   a.max_groups = W.G2;
   return launch_fc2(a, W.MT2, W.G2, device_cu_count(), stream);
 }
@@ -296,6 +300,30 @@ int moe_vq_forward_static(const moe_vq_layer* L, const void* x, int x_dtype, int
   return MOE_VQ_OK;
 }
 
+int moe_vq_shared_expert(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens, void* ws,
+                         size_t ws_bytes, float* h, float* y, void* stream) {
+  int st = check_layer(L);
+  if (st) return st;
+  if (L->n_experts != 1 || L->top_k != 1) return MOE_VQ_EINVAL;
+  if (n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
+  if (x_dtype != MOE_VQ_F32 && x_dtype != MOE_VQ_BF16) return MOE_VQ_EINVAL;
+  if (n_tokens == 0) return MOE_VQ_OK;
+  if (!x || !h || !y || ((uintptr_t)x & 15) || ((uintptr_t)h & 15) || ((uintptr_t)y & 15)) return MOE_VQ_EINVAL;
+  if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
+  // The one-expert layer's routing (every token to expert 0 with weight 1), FC1 and FC2
+  // with the combine adding to y.  The selection goes to the workspace's per-pair
+  // arrays' neighbours: routing needs somewhere to write ids and weights, and with k = 1
+  // and one expert they carry nothing the caller needs.
+  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens);
+  int32_t* ids = at<int32_t>(ws, W.o_buf);
+  float* w = at<float>(ws, W.o_buf + (size_t)n_tokens * 4);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = route_on(L, x, x_dtype, n_tokens, ids, w, ws, s);
+  if (e == hipSuccess) e = fc1_on(L, x, x_dtype, n_tokens, ws, h, s);
+  if (e == hipSuccess) e = fc2_on(L, h, n_tokens, ws, y, s, true);
+  return hip_status(e);
+}
+
 int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens, void* ws,
                         size_t ws_bytes, float* y, void* stream) {
   int st = check_layer(L);
@@ -326,6 +354,7 @@ int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n
   a.o_buf = at<float>(ws, W.o_buf);
   a.y = y;
   a.T = T; a.H = H; a.I = I; a.k = k; a.E = E;
+  a.lim = L->swiglu_limit;
   a.key = shape_key(T, E, k, H, I);
   a.vq2 = slot_layout(MOE_VQ_FMT_VQ2, H, I);
   a.mx4 = slot_layout(MOE_VQ_FMT_MXFP4, H, I);

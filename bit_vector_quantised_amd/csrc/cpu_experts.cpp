@@ -5,7 +5,8 @@
 // GPU; "What you need": an AVX2 or AVX-512 CPU).
 //
 // For each selected expert e the call computes, for its tokens t (pairs (t, i) with
-// topk_ids[t][i] == e): g = W_g x_t, u = W_u x_t, h = silu(g) * u, o = W_d h, and adds
+// topk_ids[t][i] == e): g = W_g x_t, u = W_u x_t, h = silu(g) * u (with the layer's SwiGLU
+// clamp, if any), o = W_d h, and adds
 // topk_w[t][i] * o to y[t].  Weights are decoded exactly (VQ2: scale times the signed
 // codebook vector, a product of two fp16 values; MXFP4: E2M1 value times 2^(e - 127)),
 // products and sums are fp32, so the result differs from the GPU's only in summation
@@ -69,6 +70,16 @@ const float E2M1[16] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f, -0.f, -0.5f, -
 
 // 2^(e - 127) for an E8M0 byte (255 encodes NaN).
 float e8m0_to_f32(uint32_t e) { return e == 255 ? NAN : ldexpf(1.0f, (int)e - 127); }
+
+// silu(g) * u, or with the SwiGLU clamp of limit lim > 0, silu(min(g, lim)) *
+// clamp(u, -lim, lim) (a NaN stays NaN)
+float swiglu(float g, float u, float lim) {
+  if (lim > 0.f) {
+    g = g > lim ? lim : g;
+    u = u > lim ? lim : (u < -lim ? -lim : u);
+  }
+  return g / (1.0f + expf(-g)) * u;
+}
 
 struct Slot {
   int fmt;
@@ -160,6 +171,8 @@ int moe_vq_cpu_experts(const moe_vq_layer* layer, const uint8_t* host_pool, uint
       k > E)
     return MOE_VQ_EINVAL;
   if (n_tokens < 0 || n_tokens > 65536 || (x_dtype != MOE_VQ_F32 && x_dtype != MOE_VQ_BF16)) return MOE_VQ_EINVAL;
+  const float lim = layer->swiglu_limit;
+  if (!(lim >= 0.f && lim <= 3.4e38f)) return MOE_VQ_EINVAL;  // finite, >= 0 (NaN fails)
   if (n_tokens == 0) return MOE_VQ_OK;
   if (!host_pool || !host_slots || !codebook || !x || !topk_ids || !topk_w || !compute || !y) return MOE_VQ_EINVAL;
   if (n_threads < 1 || n_threads > CPU_MAX_THREADS) return MOE_VQ_EINVAL;
@@ -247,7 +260,7 @@ int moe_vq_cpu_experts(const moe_vq_layer* layer, const uint8_t* host_pool, uint
       decode_row(sl, tab, 1, n, H, wu);
       dot_rows(wg, xs.get() + rank[j] * H, m, H, g);
       dot_rows(wu, xs.get() + rank[j] * H, m, H, u);
-      for (int i = 0; i < m; ++i) hs[(rank[j] + i) * I + n] = g[i] / (1.0f + expf(-g[i])) * u[i];
+      for (int i = 0; i < m; ++i) hs[(rank[j] + i) * I + n] = swiglu(g[i], u[i], lim);
     }
   };
   auto fc2 = [&](int item) {

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(FC_THREADS, 2) void fc_stream_kernel(FcArgs a) {
           const int p = r.pair[t];
           if (FC1) {
             const float gv = acc[0][rr][t], uv = acc[NM - 1][rr][t];
-            a.out[(size_t)p * a.I + n] = silu_fast(gv) * uv;
+            a.out[(size_t)p * a.I + n] = swiglu(gv, uv, a.lim);
           } else {
             a.out[(size_t)p * a.H + n] = a.pair_w[p] * acc[0][rr][t];
           }
@@ -600,7 +600,7 @@ __global__ __launch_bounds__(FC_THREADS) void fc_generic_kernel(FcArgs a) {
           const int p = a.pair_list[p0 + t];
           if (FC1) {
             const float gv = acc[0][r][t], uv = acc[NM - 1][r][t];
-            a.out[(size_t)p * a.I + nrow[r]] = silu_fast(gv) * uv;
+            a.out[(size_t)p * a.I + nrow[r]] = swiglu(gv, uv, a.lim);
           } else {
             a.out[(size_t)p * a.H + nrow[r]] = a.pair_w[p] * acc[0][r][t];
           }
@@ -609,14 +609,16 @@ __global__ __launch_bounds__(FC_THREADS) void fc_generic_kernel(FcArgs a) {
   }
 }
 
-// y[t][n] = sum_{i<k} o_buf[t*k + i][n] in pair order (deterministic).  Pairs whose
-// expert was not resident hold zeros (their FC2 tiles still write them).
+// y[t][n] = sum_{i<k} o_buf[t*k + i][n] in pair order (deterministic), added to y's value
+// when accumulate is set (the shared expert).  Pairs whose expert was not resident hold
+// zeros (their FC2 tiles still write them).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_buf, float* __restrict__ y,
-                                                      int T, int H, int k) {
+                                                      int T, int H, int k, int accumulate) {
   const size_t n4 = (size_t)T * H / 4;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
     const size_t t = (i * 4) / H, n = (i * 4) % H;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (accumulate) acc = *reinterpret_cast<const float4*>(y + t * H + n);
     for (int j = 0; j < k; ++j) {
       const float4 v = *reinterpret_cast<const float4*>(o_buf + (t * k + j) * H + n);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
@@ -717,12 +719,12 @@ hipError_t launch_fc2(const FcArgs& a, int MT, int max_groups, int n_cu, hipStre
   if (e != hipSuccess) return e;
   const size_t n4 = (size_t)a.T * a.H / 4;
   const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
-  launch_combine(a.out, a.y, a.T, a.H, a.k, blocks, st);
+  launch_combine(a.out, a.y, a.T, a.H, a.k, a.accumulate, blocks, st);
   return hipGetLastError();
 }
 
-void launch_combine(const float* o_buf, float* y, int T, int H, int k, int blocks, hipStream_t st) {
-  combine_kernel<<<blocks, 256, 0, st>>>(o_buf, y, T, H, k);
+void launch_combine(const float* o_buf, float* y, int T, int H, int k, int accumulate, int blocks, hipStream_t st) {
+  combine_kernel<<<blocks, 256, 0, st>>>(o_buf, y, T, H, k, accumulate);
 }
 
 }  // namespace mvq

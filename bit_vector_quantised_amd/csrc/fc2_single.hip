@@ -188,7 +188,7 @@ __global__ __launch_bounds__(F2S_THREADS, 1) void fc2_single_kernel(FcArgs a) {
   }
   __syncthreads();
   if (tid < F2S_ROWS && row0 + tid < a.H) {
-    float y = 0.f;
+    float y = a.accumulate ? a.y[row0 + tid] : 0.f;  // (the shared expert adds to y)
 #pragma unroll
     for (int gg = 0; gg < F2S_KMAX; ++gg)
       if (gg < G) y += red[gg][tid];

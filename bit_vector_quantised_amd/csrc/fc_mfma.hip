@@ -609,7 +609,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
           v[m] = sum;
         }
         const int p = s_pair[gb][q];
-        if (FC1) a.out[(size_t)p * a.I + n] = silu_fast(v[0]) * v[NM - 1];
+        if (FC1) a.out[(size_t)p * a.I + n] = swiglu(v[0], v[NM - 1], a.lim);
         else a.out[(size_t)p * a.H + n] = v[0] * s_w[gb][q];
       }
     }

@@ -198,6 +198,16 @@ __device__ __forceinline__ float ldexp2(float x, int e) { return __builtin_amdgc
 // SiLU with the hardware exponential (v_exp_f32 of x * log2(e)).
 __device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(-g)); }
 
+// An expert's FC1 output from its gate and up values: silu(g) * u, or with the SwiGLU
+// clamp of limit lim > 0, silu(min(g, lim)) * clamp(u, -lim, lim) (a NaN stays NaN).
+__device__ __forceinline__ float swiglu(float g, float u, float lim) {
+  if (lim > 0.f) {
+    g = g > lim ? lim : g;
+    u = u > lim ? lim : (u < -lim ? -lim : u);
+  }
+  return silu_fast(g) * u;
+}
+
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 }  // namespace mvq

@@ -258,6 +258,8 @@ struct FcArgs {
   int max_groups;            // upper bound on token groups for this T
   uint64_t x_addr;           // FC1: the activations the caller passes (must be the routed ones)
   int x_dtype;
+  float lim;                 // FC1: SwiGLU clamp (0: none)
+  int accumulate;            // FC2: add to y instead of overwriting it
   SlotLayout vq2, mx4;
 };
 
@@ -280,6 +282,7 @@ struct PrefillArgs {
   float* y;                  // [T][H]
   int T, H, I, k, E;
   int x_dtype;
+  float lim;                 // SwiGLU clamp (0: none)
   uint32_t key;
   SlotLayout vq2, mx4;
 };

@@ -21,7 +21,7 @@ hipError_t launch_fc1(const FcArgs& a, int MT, int max_groups, int n_cu, hipStre
 hipError_t launch_fc2(const FcArgs& a, int MT, int max_groups, int n_cu, hipStream_t st);
 
 // y[t] = sum_i o_buf[t*k + i] (the per-pair outputs, already weighted).
-void launch_combine(const float* o_buf, float* y, int T, int H, int k, int blocks, hipStream_t st);
+void launch_combine(const float* o_buf, float* y, int T, int H, int k, int accumulate, int blocks, hipStream_t st);
 
 // Prefill: stage x, token tiles, FC1 and FC2 as grouped MFMA GEMMs, combine.
 hipError_t launch_prefill(const PrefillArgs& a, int x_dtype, hipStream_t st);

@@ -457,7 +457,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a
           for (int nb = 0; nb < NB; ++nb) {
             const int n = tl.nt * BN + wave * NB * 16 + nb * 16 + i16;
             const float gv = acc[0][nb][mb][r] * (f * rowf[0][nb]), uv = acc[1][nb][mb][r] * (f * rowf[1][nb]);
-            const float h = silu_fast(gv) * uv;
+            const float h = swiglu(gv, uv, a.lim);
             if (n < NROWS) {
               a.h[(size_t)p * a.I + n] = f32_to_bf16_rne(h);
               hm = fmaxf(hm, fabsf(h));
@@ -501,7 +501,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int x_dtype, hipStream_t st) {
   prefill_fc_kernel<false><<<(unsigned)g2, PF_THREADS, 0, st>>>(a);
   const size_t n4 = (size_t)a.T * a.H / 4;
   const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
-  launch_combine(a.o_buf, a.y, a.T, a.H, a.k, blocks, st);
+  launch_combine(a.o_buf, a.y, a.T, a.H, a.k, 0, blocks, st);
   return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ class DeviceLayer:
 
     def __init__(self, hidden: int, inter: int, n_experts: int, top_k: int, codebook: np.ndarray,
                  router_w_bits: np.ndarray, experts: Callable[[int], Dict[str, np.ndarray]],
-                 formats: Sequence[int], device: str = "cuda"):
+                 formats: Sequence[int], device: str = "cuda", swiglu_limit: float = 0.0):
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.device = torch.device(device)
         offsets = np.zeros(n_experts, dtype=np.uint64)
@@ -73,14 +73,15 @@ class DeviceLayer:
         self.router_w = torch.from_numpy(np.ascontiguousarray(router_w_bits).view(np.int16)).to(self.device)
         self.codebook = torch.from_numpy(np.ascontiguousarray(codebook).view(np.int16)).to(self.device)
         self.c = _lib.Layer(hidden, inter, n_experts, top_k, self.router_w.data_ptr(), self.codebook.data_ptr(),
-                            self.pool.data_ptr(), self.pool_bytes, self.slots.data_ptr())
+                            self.pool.data_ptr(), self.pool_bytes, self.slots.data_ptr(), float(swiglu_limit))
 
     @classmethod
-    def from_synth(cls, syn, device: str = "cuda", formats: Optional[Sequence[int]] = None):
+    def from_synth(cls, syn, device: str = "cuda", formats: Optional[Sequence[int]] = None,
+                   swiglu_limit: float = 0.0):
         cfg = syn.cfg
         fm = syn.formats if formats is None else formats
         return cls(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, syn.codebook, syn.router_w,
-                   lambda e: syn.expert_as(e, fm[e]), fm, device)
+                   lambda e: syn.expert_as(e, fm[e]), fm, device, swiglu_limit)
 
     def set_slots(self, offsets: np.ndarray, formats: Sequence[int]) -> None:
         """Rewrite the slot table (e.g. to mark experts absent)."""
@@ -88,6 +89,35 @@ class DeviceLayer:
         slots["byte_offset"] = offsets
         slots["format"] = np.asarray(formats, dtype=np.uint32)
         self.slots.copy_(torch.from_numpy(slots.view(np.uint8).copy()))
+
+
+class SharedExpert:
+    """The shared expert of a layer: a one-expert layer (n_experts = top_k = 1) holding its
+    weights in one slot, and the buffers of moe_vq_shared_expert for up to max_tokens
+    tokens.  add(x, y) adds S(x) to y [T, H] fp32 in place."""
+
+    def __init__(self, hidden: int, inter: int, codebook: np.ndarray, expert: Dict[str, np.ndarray],
+                 fmt: int, max_tokens: int, device: str = "cuda", swiglu_limit: float = 0.0):
+        # (the router row is only a placeholder: one expert always has weight 1)
+        self.layer = DeviceLayer(hidden, inter, 1, 1, codebook, np.zeros((1, hidden), dtype=np.uint16),
+                                 lambda e: expert, [fmt], device, swiglu_limit)
+        self.max_tokens = max_tokens
+        self.ws_bytes = _lib.workspace_bytes(self.layer.c, max_tokens)
+        if self.ws_bytes == 0:
+            raise ValueError("invalid layer shape")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.layer.device)
+        self.h = torch.empty((max_tokens, inter), dtype=torch.float32, device=self.layer.device)
+
+    def add(self, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+        T = x.shape[0]
+        assert x.is_contiguous() and x.shape[1] == self.layer.hidden and T <= self.max_tokens
+        assert y.is_contiguous() and y.dtype == torch.float32 and tuple(y.shape) == (T, self.layer.hidden)
+        _lib.shared_expert(self.layer.c, x.data_ptr(), x_dtype_code(x), T, self.ws.data_ptr(), self.ws_bytes,
+                           self.h.data_ptr(), y.data_ptr(), torch.cuda.current_stream(self.layer.device).cuda_stream)
+        return y
+
+    def check(self):
+        return _lib.check(self.ws.data_ptr(), torch.cuda.current_stream(self.layer.device).cuda_stream)
 
 
 class TieredLayer:

@@ -98,7 +98,15 @@ typedef struct moe_vq_layer {
   const uint8_t *pool;         /* slot pool                                 */
   uint64_t pool_bytes;         /* size of the pool in bytes                 */
   const moe_vq_slot *slots;    /* [E] expert id -> slot                     */
+  float swiglu_limit;          /* SwiGLU clamp L (0: none), see below       */
 } moe_vq_layer;
+/* swiglu_limit: with L > 0 every expert's FC1 output is h = silu(min(g, L)) * clamp(u,
+ * -L, L) instead of silu(g) * u, on every path (decode, prefill, the host miss path).
+ * The vLLM-Moet README ("Quality vs native", the audit of the W2 path) says the real
+ * checkpoint has a SwiGLU clamp that a port must not omit, but gives neither its form
+ * nor its constant; this form (gate capped above, up clamped on both sides) is the one
+ * read here.  L must be finite and >= 0 (MOE_VQ_EINVAL otherwise).  Zero-initialising
+ * the struct leaves the clamp off. */
 
 /* [host] Bytes of one expert slot of the given format, 0 if an argument is invalid. */
 size_t moe_vq_expert_bytes(int format, int hidden, int inter);
@@ -182,6 +190,26 @@ int moe_vq_forward(const moe_vq_layer *layer, const void *x, int x_dtype, int n_
 int moe_vq_forward_static(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
                           int32_t *topk_ids, float *topk_w, float *h, float *y, int32_t *status,
                           void *stream);
+
+/* The shared expert: y[t][:] += S(x_t) for every token, S a SwiGLU MLP that every token
+ * passes through with weight 1 besides its routed experts, so that after the routed step
+ * y = sum_i w_i E_i(x) + S(x).  Source: the DeepSeek V4 Flash article's llama.cpp
+ * comparison, whose GGUF file name marks a quantised shared expert ("SExpQ8"); the pages
+ * say no more, and this plain reading (weight 1, added after the routed combine) is the
+ * one taken.  shared: a layer descriptor with n_experts = 1 and top_k = 1 whose expert 0
+ * is the shared expert, in either slot format (its own pool, or the routed layer's pool
+ * and codebook), with its own swiglu_limit; its router_w must point at one bf16 row of H
+ * values, whose values do not matter (a single expert always has weight 1).  x, x_dtype,
+ * n_tokens: as moe_vq_route_topk.  ws: a workspace of moe_vq_workspace_bytes(shared,
+ * n_tokens) bytes (it may be the routed step's workspace once that step is done, if it
+ * is large enough).  h: [n_tokens][I] fp32, caller-owned scratch (receives S's FC1
+ * output).  y: [n_tokens][H] fp32, read and written (the shared output is added).  Runs
+ * route, FC1 and FC2 of the one-expert layer on stream; the same kernels as the routed
+ * step.  Errors: MOE_VQ_EINVAL (bad argument, or n_experts != 1 or top_k != 1), as
+ * moe_vq_route_topk otherwise; an absent slot is MOE_VQ_ENOTRESIDENT in the status word,
+ * and y is then unchanged. */
+int moe_vq_shared_expert(const moe_vq_layer *shared, const void *x, int x_dtype, int n_tokens,
+                         void *ws, size_t ws_bytes, float *h, float *y, void *stream);
 
 /* Prefill form of FC1 + FC2 + combine for large n_tokens (vLLM-Moet README, "What we
  * changed against official vLLM", rows "MoE at decode" and "prefill": tokens grouped per

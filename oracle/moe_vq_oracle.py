@@ -38,6 +38,20 @@ are silent are listed next to each function (R1..R12) and in the design notes.
   O7  FC2             o = W_d h
   O8  combine         y[t] = sum_i w_i o_i
                       [Tandem "How it works": nothing skipped or substituted.]
+  O9  shared expert   y[t] += S(x_t), S = O6 + O7 with the shared expert's own
+                      matrices, weight 1 for every token.  [DeepSeek V4 Flash article,
+                      llama.cpp comparison: the GGUF file name marks a shared expert
+                      ("SExpQ8"); the pages say nothing more, so this plain reading
+                      (every token, weight 1, added after the routed combine) is R13.]
+  O6' SwiGLU clamp    with a limit L > 0: g <- min(g, L), u <- clamp(u, -L, L)
+                      before h = silu(g) * u.  [Moet "Quality vs native": the W2 path
+                      had omitted the checkpoint's SwiGLU clamp.  The pages give
+                      neither the form nor the constant: R14 takes the common form
+                      (gate capped above, up clamped both ways) and leaves L a
+                      parameter, 0 = off.  Parity unpinned: nothing on the pages fixes
+                      a value to test the clamp against; the pins only check that it
+                      leaves values inside [-L, L] alone and that this module and the
+                      scalar brute force below agree.]
 
 Every value is computed in fp64 from the exact values of the stored fp16 / bf16 /
 fp32 inputs.  Decoding is exact in fp64 (a product of two fp16 numbers).
@@ -199,30 +213,44 @@ def route(router_w_bits: np.ndarray, x64: np.ndarray, k: int):
 # ---------------------------------------------------------------------------------
 
 def silu(g: np.ndarray) -> np.ndarray:
-    """R9: silu(g) = g * sigmoid(g) = g / (1 + exp(-g)); no clamp."""
+    """R9: silu(g) = g * sigmoid(g) = g / (1 + exp(-g))."""
     return g / (1.0 + np.exp(-g))
 
 
-def expert_mlp(Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, xs: np.ndarray) -> Dict[str, np.ndarray]:
+def swiglu(g: np.ndarray, u: np.ndarray, limit: float = 0.0) -> np.ndarray:
+    """O6 / O6': h = silu(g) * u; with limit L > 0 (R14), g is first capped at L and u
+    clamped to [-L, L] (a NaN stays NaN)."""
+    if limit > 0.0:
+        g = np.where(g > limit, limit, g)
+        u = np.where(u > limit, limit, np.where(u < -limit, -limit, u))
+    return silu(g) * u
+
+
+def expert_mlp(Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, xs: np.ndarray,
+               swiglu_limit: float = 0.0) -> Dict[str, np.ndarray]:
     """O6, O7 for tokens xs [m, H]: g, u, h [m, I] and o [m, H]."""
     g = xs @ Wg.T
     u = xs @ Wu.T
-    h = silu(g) * u
+    h = swiglu(g, u, swiglu_limit)
     o = h @ Wd.T
     return {"g": g, "u": u, "h": h, "o": o}
 
 
 def forward(layer, x64: np.ndarray, top_k: int,
-            forced_selection: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+            forced_selection: Optional[np.ndarray] = None, swiglu_limit: float = 0.0,
+            shared: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
     """The whole routed-expert step for tokens x64 [T, H].
 
     ``layer`` provides ``codebook`` (fp16 [128,4]), ``router_w`` (bf16 bits
     [E,H]) and ``expert(e)`` (the storage arrays of expert e).
     ``forced_selection`` [T, k] replaces the top-k ids (used when a fp32 router
     picks a different but equally valid expert at a near-tie); the weights are
-    then renormalised over the forced set.
+    then renormalised over the forced set.  ``swiglu_limit`` > 0 applies the clamp
+    (O6') in every expert; ``shared`` (the storage arrays of a shared expert) adds
+    O9.
 
-    Returns logits [T,E], ids [T,k], w [T,k], h [T,k,I], o [T,k,H], y [T,H].
+    Returns logits [T,E], ids [T,k], w [T,k], h [T,k,I], o [T,k,H], y [T,H], and
+    with ``shared`` also h_shared [T,I], o_shared [T,H] (y includes o_shared).
     Each expert is decoded once and applied to all of its tokens.
     """
     x64 = np.asarray(x64, dtype=np.float64)
@@ -239,7 +267,7 @@ def forward(layer, x64: np.ndarray, top_k: int,
         tokens = [t for t, _ in pairs]
         Wg, Wu, Wd = decode_expert(layer.expert(e), layer.codebook)
         I = Wg.shape[0]
-        r_ = expert_mlp(Wg, Wu, Wd, x64[tokens])
+        r_ = expert_mlp(Wg, Wu, Wd, x64[tokens], swiglu_limit)
         for r, (t, i) in enumerate(pairs):
             h_all[(t, i)] = r_["h"][r]
             o_all[(t, i)] = r_["o"][r]
@@ -252,7 +280,13 @@ def forward(layer, x64: np.ndarray, top_k: int,
             h_out[t, i] = h_all[(t, i)]
             o_out[t, i] = o_all[(t, i)]
             y[t] += w[t, i] * o_all[(t, i)]
-    return {"logits": logits, "p": p, "ids": ids, "w": w, "h": h_out, "o": o_out, "y": y}
+    out = {"logits": logits, "p": p, "ids": ids, "w": w, "h": h_out, "o": o_out, "y": y}
+    if shared is not None:
+        Wg, Wu, Wd = decode_expert(shared, layer.codebook)
+        r_ = expert_mlp(Wg, Wu, Wd, x64, swiglu_limit)
+        out["h_shared"], out["o_shared"] = r_["h"], r_["o"]
+        y += r_["o"]
+    return out
 
 
 # ---------------------------------------------------------------------------------
@@ -287,10 +321,12 @@ def topk_bruteforce(logits_row: Sequence[float], k: int):
     return sorted(best, key=lambda e: (-exact[e], e))
 
 
-def forward_bruteforce(layer, x64: np.ndarray, top_k: int) -> np.ndarray:
-    """y [T, H] from the dense all-expert form y[t] = sum_e M[t,e] * MLP_e(x_t), where
-    M[t,e] is the renormalised routing weight for selected experts and 0 otherwise.
-    Scalar Python loops only; meant for the tiny layer."""
+def forward_bruteforce(layer, x64: np.ndarray, top_k: int, swiglu_limit: float = 0.0,
+                       shared: Optional[Dict[str, np.ndarray]] = None) -> np.ndarray:
+    """y [T, H] from the dense all-expert form y[t] = sum_e M[t,e] * MLP_e(x_t) (+ the
+    shared expert's MLP with weight 1), where M[t,e] is the renormalised routing weight
+    for selected experts and 0 otherwise.  Scalar Python loops only; meant for the
+    tiny layer."""
     x = [[float(v) for v in row] for row in np.asarray(x64, dtype=np.float64)]
     T, H = len(x), len(x[0])
     rw = bf16_value(layer.router_w)
@@ -311,17 +347,22 @@ def forward_bruteforce(layer, x64: np.ndarray, top_k: int) -> np.ndarray:
         sel = topk_bruteforce(logits, top_k)
         psel = sum(p[e] for e in sel)
         M = [p[e] / psel if e in sel else 0.0 for e in range(E)]
-        for e in range(E):
-            ex_arr = layer.expert(e)
+        mlps = [(layer.expert(e), M[e]) for e in range(E)]
+        if shared is not None:
+            mlps.append((shared, 1.0))
+        for ex_arr, m_e in mlps:
             I = (ex_arr["codes_g"] if int(ex_arr["format"]) == FMT_VQ2 else ex_arr["nib_g"]).shape[0]
             h = []
             for n in range(I):
                 g = sum(_scalar_weight(ex_arr, cb, "g", n, j) * x[t][j] for j in range(H))
                 u = sum(_scalar_weight(ex_arr, cb, "u", n, j) * x[t][j] for j in range(H))
+                if swiglu_limit > 0.0:
+                    g = min(g, swiglu_limit)
+                    u = max(-swiglu_limit, min(u, swiglu_limit))
                 h.append(g / (1.0 + math.exp(-g)) * u)
             for n in range(H):
                 o = sum(_scalar_weight(ex_arr, cb, "d", n, j) * h[j] for j in range(I))
-                Y[t][n] += M[e] * o
+                Y[t][n] += m_e * o
     return np.asarray(Y)
 
 

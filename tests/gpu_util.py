@@ -52,8 +52,10 @@ def rel_err_rows(a: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return num / np.where(den > 0, den, 1.0)
 
 
-def compare(syn, x_np: np.ndarray, x_dtype: str, g: dict, top_k: int, tokens=None, check_h=True):
-    """Compare one GPU step with the oracle on the given tokens (all by default)."""
+def compare(syn, x_np: np.ndarray, x_dtype: str, g: dict, top_k: int, tokens=None, check_h=True,
+            swiglu_limit=0.0, shared=None):
+    """Compare one GPU step with the oracle on the given tokens (all by default); with
+    swiglu_limit / shared, against the oracle's clamped layer / with its shared expert."""
     x64 = oracle.x_value(x_np, x_dtype)
     T = x64.shape[0]
     tokens = list(range(T)) if tokens is None else list(tokens)
@@ -63,7 +65,7 @@ def compare(syn, x_np: np.ndarray, x_dtype: str, g: dict, top_k: int, tokens=Non
     assert oracle.selection_is_valid(g["ids"], logits, delta, top_k), "GPU selection is not a valid top-k"
     n_diff = int((g["ids"] != ref_ids).any(axis=1).sum())
     sel = g["ids"][tokens]
-    r = oracle.forward(syn, x64[tokens], top_k, forced_selection=sel)
+    r = oracle.forward(syn, x64[tokens], top_k, forced_selection=sel, swiglu_limit=swiglu_limit, shared=shared)
     werr = np.abs(g["w"][tokens] - r["w"]).max()
     assert werr <= W_TOL, f"routing weights off by {werr}"
     assert np.all(np.abs(g["w"].sum(axis=1) - 1.0) <= 4 * top_k * 2.0 ** -24)

@@ -207,3 +207,32 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     libs = sorted({ln.split()[-1] for ln in maps if "libamdhip64" in ln})
     assert len(libs) == 1, libs
+
+
+def test_swiglu_limit_and_shared_expert_arguments():
+    """The SwiGLU clamp's limit must be finite and >= 0 on every entry point, and the
+    shared expert takes a one-expert, top-1 layer; both refused before any HIP call."""
+    raw = _lib.raw()
+    P = ctypes.byref
+    X, IDS, W, WS, H_, Y = 0x40000, 0x50000, 0x60000, 0x700000, 0x800000, 0x900000
+    for lim in (float("nan"), -1.0, float("inf")):
+        L = fake_layer()
+        L.swiglu_limit = lim
+        ws_ok = _lib.workspace_bytes(L, 4)
+        assert raw.moe_vq_route_topk(P(L), X, _lib.F32, 4, IDS, W, WS, ws_ok, None) == _lib.EINVAL
+        assert raw.moe_vq_fc1_silu(P(L), X, _lib.F32, 4, WS, ws_ok, H_, None) == _lib.EINVAL
+        assert raw.moe_vq_forward(P(L), X, _lib.F32, 4, IDS, W, H_, Y, WS, ws_ok, None) == _lib.EINVAL
+        assert raw.moe_vq_prefill_gemm(P(L), X, _lib.F32, 4, WS, ws_ok, Y, None) == _lib.EINVAL
+    S = fake_layer(E=1, k=1)
+    ws_s = _lib.workspace_bytes(S, 4)
+    assert ws_s > 0
+    assert raw.moe_vq_shared_expert(P(fake_layer()), X, _lib.F32, 4, WS, ws_s, H_, Y, None) == _lib.EINVAL
+    assert raw.moe_vq_shared_expert(P(fake_layer(E=2, k=1)), X, _lib.F32, 4, WS, ws_s, H_, Y, None) == _lib.EINVAL
+    assert raw.moe_vq_shared_expert(P(S), X, _lib.F32, 4, WS, ws_s, None, Y, None) == _lib.EINVAL
+    assert raw.moe_vq_shared_expert(P(S), X, _lib.F32, 4, WS, ws_s, H_, None, None) == _lib.EINVAL
+    assert raw.moe_vq_shared_expert(P(S), X + 8, _lib.F32, 4, WS, ws_s, H_, Y, None) == _lib.EINVAL
+    assert raw.moe_vq_shared_expert(P(S), X, 5, 4, WS, ws_s, H_, Y, None) == _lib.EINVAL
+    assert raw.moe_vq_shared_expert(P(S), X, _lib.F32, 4, WS, ws_s - 256, H_, Y, None) == _lib.ENOSPACE
+    assert raw.moe_vq_shared_expert(P(S), X, _lib.F32, 0, WS, ws_s, H_, Y, None) == _lib.OK
+    S.swiglu_limit = float("nan")
+    assert raw.moe_vq_shared_expert(P(S), X, _lib.F32, 4, WS, ws_s, H_, Y, None) == _lib.EINVAL

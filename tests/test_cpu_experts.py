@@ -63,10 +63,10 @@ class HostLayer:
         return rc, y
 
 
-def _oracle_part(layer, x64, ids, compute):
+def _oracle_part(layer, x64, ids, compute, swiglu_limit=0.0):
     """y restricted to the pairs whose expert is in `compute`, from the oracle (with the
     given selection and its renormalised weights)."""
-    r = oracle.forward(layer, x64, ids.shape[1], forced_selection=ids)
+    r = oracle.forward(layer, x64, ids.shape[1], forced_selection=ids, swiglu_limit=swiglu_limit)
     keep = np.isin(ids, list(compute))[:, :, None]
     return (r["w"][:, :, None] * r["o"] * keep).sum(axis=1), r["w"]
 
@@ -153,3 +153,23 @@ def test_errors():
     assert rc == _lib.EINVAL
     rc, _ = L.run(x[:0], "f32", ids[:0], w[:0], [1])
     assert rc == _lib.OK
+
+
+def test_swiglu_clamp_on_the_host():
+    """The layer's SwiGLU clamp (reading R14) applies on the host path too: against the
+    oracle with the same limit, chosen so that it clamps, and different from no clamp."""
+    L = HostLayer(synth.PRESETS["tiny"])
+    x = L.syn.x(n=5, stream=4)
+    x64 = oracle.x_value(x, "f32")
+    ids = oracle.topk(oracle.router_logits(L.router_w, x64), 2)
+    ref0, w = _oracle_part(L, x64, ids, range(8))
+    lim = 0.02
+    ref, _ = _oracle_part(L, x64, ids, range(8), swiglu_limit=lim)
+    assert np.abs(ref - ref0).max() > 0.05 * np.abs(ref0).max()
+    L.c.swiglu_limit = lim
+    rc, y = L.run(x, "f32", ids, w, range(8))
+    assert rc == _lib.OK
+    _check(y, ref)
+    L.c.swiglu_limit = -1.0
+    rc, _ = L.run(x, "f32", ids, w, range(8))
+    assert rc == _lib.EINVAL

@@ -367,3 +367,86 @@ def test_fp32_bound_covers_fp32_dot(tiny):
     exact = oracle.router_logits(rw, x)
     f32 = (x.astype(np.float32) @ synth.bf16_bits_to_f32(rw).T).astype(np.float64)
     assert np.all(np.abs(f32 - exact) <= oracle.fp32_dot_error_bound(rw, x))
+
+
+# ---------------------------------------------------------------------------------
+# O6' SwiGLU clamp and O9 shared expert (readings R14 and R13)
+# ---------------------------------------------------------------------------------
+
+def _gate_up_extent(lay, x):
+    """max |g| and max |u| over every expert and token of the tiny layer."""
+    m = 0.0
+    for e in range(lay_experts(lay)):
+        Wg, Wu, Wd = oracle.decode_expert(lay.expert(e), lay.codebook)
+        r = oracle.expert_mlp(Wg, Wu, Wd, x)
+        m = max(m, float(np.abs(r["g"]).max()), float(np.abs(r["u"]).max()))
+    return m
+
+
+def lay_experts(lay):
+    return lay.cfg.n_experts if hasattr(lay, "cfg") else len(lay._experts)
+
+
+def test_clamp_leaves_values_inside_the_limit_alone(tiny):
+    """With L above every |g| and |u| of the batch the clamp changes nothing, bit for bit;
+    just below the largest it does."""
+    x = oracle.x_value(tiny.x(), "f32")
+    m = _gate_up_extent(tiny, x)
+    y0 = oracle.forward(tiny, x, 2)["y"]
+    assert np.array_equal(oracle.forward(tiny, x, 2, swiglu_limit=m * (1 + 1e-9))["y"], y0)
+    assert not np.array_equal(oracle.forward(tiny, x, 2, swiglu_limit=m * 0.999)["y"], y0)
+
+
+def test_clamp_form_gate_one_sided_up_two_sided():
+    """R14's form: the gate is only capped from above (a very negative gate keeps its
+    value), the up projection is clamped on both sides."""
+    L = 1.5
+    g = np.array([-10.0, -1.0, 0.5, 3.0, 3.0, -10.0])
+    u = np.array([1.0, -4.0, 0.25, 2.0, -7.0, 9.0])
+    h = oracle.swiglu(g, u, L)
+    sig = lambda v: 1.0 / (1.0 + math.exp(-v))
+    want = [-10.0 * sig(-10.0) * 1.0, -1.0 * sig(-1.0) * -1.5, 0.5 * sig(0.5) * 0.25,
+            1.5 * sig(1.5) * 1.5, 1.5 * sig(1.5) * -1.5, -10.0 * sig(-10.0) * 1.5]
+    np.testing.assert_allclose(h, want, rtol=1e-15)
+    assert np.isnan(oracle.swiglu(np.array([np.nan]), np.array([1.0]), L)[0])
+
+
+def test_clamped_forward_matches_scalar_bruteforce(tiny):
+    """With a limit that clamps a good share of g and u, the vectorised oracle equals the
+    scalar brute force of the dense form."""
+    x = oracle.x_value(tiny.x(), "f32")
+    m = _gate_up_extent(tiny, x)
+    L = 0.3 * m
+    r = oracle.forward(tiny, x, tiny.cfg.top_k, swiglu_limit=L)
+    yb = oracle.forward_bruteforce(tiny, x, tiny.cfg.top_k, swiglu_limit=L)
+    assert np.abs(r["y"] - yb).max() <= 1e-12 * np.abs(yb).max()
+    assert np.abs(r["y"] - oracle.forward(tiny, x, tiny.cfg.top_k)["y"]).max() > 1e-3 * np.abs(yb).max()
+
+
+def test_shared_expert_alone_is_a_plain_swiglu_mlp(tiny):
+    """O9 with every routed expert's down scales zeroed: y is the shared expert's MLP,
+    equal to the one-expert layer of SC1 (brute force) built from the same arrays."""
+    lay = tiny_arrays(tiny)
+    for e in range(tiny.cfg.n_experts):
+        lay._experts[e]["scales_d"][:] = 0
+    shared = copy.deepcopy(tiny.expert(3))
+    x = oracle.x_value(tiny.x(), "f32")
+    r = oracle.forward(lay, x, 2, shared=shared)
+    assert np.all(r["o"] == 0)
+    one = ArrLayer(tiny.codebook, tiny.router_w[:1].copy(), [shared])
+    yb = oracle.forward_bruteforce(one, x, 1)
+    assert np.abs(r["y"] - yb).max() <= 1e-12 * np.abs(yb).max()
+    assert np.array_equal(r["y"], r["o_shared"])
+
+
+def test_shared_expert_matches_scalar_bruteforce(tiny):
+    """Routed experts and the shared one (an MXFP4 expert), with the clamp: the sparse
+    oracle equals the dense scalar brute force."""
+    shared = synth.draw_expert(tiny.cfg, 99, synth.FMT_MXFP4)
+    x = oracle.x_value(tiny.x(), "f32")[:2]
+    L = 0.5 * _gate_up_extent(tiny, x)
+    r = oracle.forward(tiny, x, 2, swiglu_limit=L, shared=shared)
+    yb = oracle.forward_bruteforce(tiny, x, 2, swiglu_limit=L, shared=shared)
+    assert np.abs(r["y"] - yb).max() <= 1e-12 * np.abs(yb).max()
+    y_routed = oracle.forward(tiny, x, 2, swiglu_limit=L)["y"]
+    np.testing.assert_allclose(r["y"] - y_routed, r["o_shared"], rtol=1e-12, atol=1e-14 * np.abs(yb).max())
