@@ -188,10 +188,12 @@ def bench_tier(args, cfg, syn, x_pool, n_batches):
     st = Step(tl, T)
     fmts = [int(f) for f in syn.formats]
     start = 0
-    if args.cpu_miss:
-        # fill the device slots once from the first batches, then never copy again; the
-        # timed steps take the batches after them (whose experts the fill did not choose)
-        for i in range(n_batches):
+    if args.cpu_miss or args.tier_slots >= cfg.n_experts:
+        # fill the device slots once from the first batches.  With the CPU miss path the
+        # timed steps then take the batches after them (whose experts the fill did not
+        # choose); with a slot for every expert they measure the tier's own cost on
+        # steps that never miss.
+        for i in range(4 * n_batches):
             tiered_forward(st, tl, x_pool[(i % n_batches) * T:(i % n_batches + 1) * T])
             start = i + 1
             if all(e >= 0 for e in tl.tier.held()):
@@ -203,10 +205,15 @@ def bench_tier(args, cfg, syn, x_pool, n_batches):
         if args.cpu_miss:
             _, miss = cpu_miss_forward(st, tl, xb)
             return len(miss), sum(_lib.expert_bytes(fmts[e], cfg.hidden, cfg.inter) for e in miss)
-        before = set(tl.tier.held())
         _, n = tiered_forward(st, tl, xb)
-        new = set(tl.tier.held()) - before
+        if not n:
+            return 0, 0
+        now = set(tl.tier.held())
+        new = now - held[0]
+        held[0] = now
         return n, sum(_lib.expert_bytes(fmts[e], cfg.hidden, cfg.inter) for e in new if e >= 0)
+
+    held = [set(tl.tier.held())]
 
     for i in range(args.warmup):
         one(i)
@@ -231,7 +238,8 @@ def bench_tier(args, cfg, syn, x_pool, n_batches):
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp16/fp32", "data": "synthetic",
         "config": {"workload": f"{cfg.name} with a host-RAM tier", "tokens_per_step": T,
-                   "n_experts": cfg.n_experts, "device_slots": args.tier_slots},
+                   "n_experts": cfg.n_experts, "device_slots": args.tier_slots,
+                   "tier_mode": "cpu-miss" if args.cpu_miss else "copy"},
         "tier": ({"experts_on_host_per_step": copied / args.steps, "host_expert_bytes_per_step": nbytes / args.steps,
                   "host_GBps": nbytes / dt / 1e9, "host_threads": max(1, min(64, len(os.sched_getaffinity(0))))}
                  if args.cpu_miss else

@@ -47,7 +47,7 @@ class Tier(ctypes.Structure):
                 ("dev_slot_offsets", ctypes.POINTER(ctypes.c_uint64)),
                 ("dev_slot_expert", ctypes.POINTER(ctypes.c_int32)),
                 ("dev_slot_stamp", ctypes.POINTER(ctypes.c_uint64)), ("slot_mirror", ctypes.POINTER(Slot)),
-                ("step", ctypes.c_uint64)]
+                ("step", ctypes.c_uint64), ("readback", ctypes.c_void_p)]
 
 
 def _load():
@@ -193,9 +193,10 @@ class ExpertTier:
     """Caller-owned state of a host-RAM expert tier (struct moe_vq_tier): keeps the
     host arrays the C structure points to alive.  host_pool: address of a pinned host
     buffer holding every expert's slot; host_slots: [(byte_offset, format)] per expert;
-    dev_slot_offsets: offsets in the device pool of the slots the tier manages."""
+    dev_slot_offsets: offsets in the device pool of the slots the tier manages;
+    readback: address of a pinned host buffer of 64 + n_experts 32-bit words, or 0."""
 
-    def __init__(self, n_experts: int, host_pool: int, host_slots, dev_slot_offsets):
+    def __init__(self, n_experts: int, host_pool: int, host_slots, dev_slot_offsets, readback: int = 0):
         self.n_experts = n_experts
         self._host_slots = (Slot * n_experts)(*[Slot(int(o), int(f), 0) for o, f in host_slots])
         ns = len(dev_slot_offsets)
@@ -203,7 +204,8 @@ class ExpertTier:
         self._held = (ctypes.c_int32 * ns)(*([-1] * ns))
         self._stamp = (ctypes.c_uint64 * ns)()
         self._mirror = (Slot * n_experts)()
-        self.c = Tier(host_pool, self._host_slots, ns, self._offs, self._held, self._stamp, self._mirror, 0)
+        self.c = Tier(host_pool, self._host_slots, ns, self._offs, self._held, self._stamp, self._mirror, 0,
+                      readback or None)
 
     def held(self):
         """Expert held by each device slot (-1 = free)."""

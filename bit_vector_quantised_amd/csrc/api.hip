@@ -386,27 +386,38 @@ int moe_vq_check(const void* ws, void* stream, int32_t* info) {
   return (int)hdr[0];
 }
 
-int moe_vq_step_info(const moe_vq_layer* L, int n_tokens, const void* ws, int32_t summary[4],
-                     int32_t* experts, void* stream) {
+// The step's header and distinct experts (adjacent in the workspace) in one
+// stream-ordered copy.  With a pinned staging buffer of HDR_WORDS + E words the copy is
+// asynchronous and one stream synchronisation covers it; without one it goes through a
+// host array on the stack, which HIP copies synchronously.
+static int read_step(const moe_vq_layer* L, int n_tokens, const void* ws, int32_t summary[4], int32_t* experts,
+                     void* stream, uint32_t* pinned) {
   if (!L || !dims_ok(L->hidden, L->inter, L->n_experts, L->top_k)) return MOE_VQ_EINVAL;
   if (!ws || !summary || n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
-  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens);
-  uint32_t hdr[HDR_WORDS];
-  int st = hip_status(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  const int E = L->n_experts;
+  const WsLayout W = ws_layout(E, L->hidden, L->inter, L->top_k, n_tokens);
+  static_assert(HDR_WORDS * 4 % 256 == 0, "the expert list must follow the header");
+  uint32_t local[HDR_WORDS + MAX_E];
+  uint32_t* buf = pinned ? pinned : local;
+  const size_t words = experts ? HDR_WORDS + (size_t)E : HDR_WORDS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = hip_status(hipMemcpyAsync(buf, static_cast<const char*>(ws) + W.hdr, words * 4, hipMemcpyDeviceToHost, s));
   if (st) return st;
-  if ((st = hip_status(hipMemcpy(hdr, static_cast<const char*>(ws) + W.hdr, sizeof(hdr), hipMemcpyDeviceToHost))))
-    return st;
-  summary[0] = (int32_t)hdr[HDR_STATUS];
-  summary[1] = (int32_t)hdr[HDR_INFO];
-  summary[2] = (int32_t)hdr[HDR_N_ACTIVE];
-  summary[3] = (int32_t)hdr[HDR_N_PAIRS];
-  if (experts && hdr[HDR_N_ACTIVE] > 0) {
-    const size_t n = hdr[HDR_N_ACTIVE] <= (uint32_t)L->n_experts ? hdr[HDR_N_ACTIVE] : (size_t)L->n_experts;
-    if ((st = hip_status(hipMemcpy(experts, static_cast<const char*>(ws) + W.act_expert, n * 4,
-                                   hipMemcpyDeviceToHost))))
-      return st;
+  if ((st = hip_status(hipStreamSynchronize(s)))) return st;
+  summary[0] = (int32_t)buf[HDR_STATUS];
+  summary[1] = (int32_t)buf[HDR_INFO];
+  summary[2] = (int32_t)buf[HDR_N_ACTIVE];
+  summary[3] = (int32_t)buf[HDR_N_PAIRS];
+  if (experts && buf[HDR_N_ACTIVE] > 0) {
+    const size_t n = buf[HDR_N_ACTIVE] <= (uint32_t)E ? buf[HDR_N_ACTIVE] : (size_t)E;
+    memcpy(experts, buf + HDR_WORDS, n * 4);
   }
   return MOE_VQ_OK;
+}
+
+int moe_vq_step_info(const moe_vq_layer* L, int n_tokens, const void* ws, int32_t summary[4],
+                     int32_t* experts, void* stream) {
+  return read_step(L, n_tokens, ws, summary, experts, stream, nullptr);
 }
 
 // ---- Host-RAM expert tier (see moe_vq.h) ----------------------------------------------
@@ -496,7 +507,7 @@ int moe_vq_tier_resolve(const moe_vq_layer* L, moe_vq_tier* tier, uint8_t* pool,
   const int E = L->n_experts;
   int32_t summary[4];
   int32_t active[MAX_E];
-  int r = moe_vq_step_info(L, n_tokens, ws, summary, active, stream);  // (synchronises stream)
+  int r = read_step(L, n_tokens, ws, summary, active, stream, tier->readback);  // (synchronises stream)
   if (r) return r;
   const int n_active = summary[2] < 0 ? 0 : (summary[2] > E ? E : summary[2]);
   tier->step += 1;
@@ -509,6 +520,7 @@ int moe_vq_tier_resolve(const moe_vq_layer* L, moe_vq_tier* tier, uint8_t* pool,
   int32_t ie[MAX_E], is[MAX_E], ev[MAX_E];
   int n = 0;
   if ((r = moe_vq_tier_plan(tier, E, active, n_active, ie, is, ev, &n))) return r;
+  if (n == 0) return MOE_VQ_OK;  // nothing enqueued since the synchronisation above
   hipStream_t st = static_cast<hipStream_t>(stream);
   for (int i = 0; i < n; ++i) {
     const int e = ie[i], sl = is[i];
@@ -524,8 +536,8 @@ int moe_vq_tier_resolve(const moe_vq_layer* L, moe_vq_tier* tier, uint8_t* pool,
     tier->dev_slot_stamp[sl] = tier->step;
     if (n_installed) *n_installed = i + 1;
   }
-  if (n > 0 && (r = hip_status(hipMemcpyAsync(slots, tier->slot_mirror, (size_t)E * sizeof(moe_vq_slot),
-                                               hipMemcpyHostToDevice, st))))
+  if ((r = hip_status(hipMemcpyAsync(slots, tier->slot_mirror, (size_t)E * sizeof(moe_vq_slot),
+                                     hipMemcpyHostToDevice, st))))
     return r;
   return hip_status(hipStreamSynchronize(st));
 }

@@ -172,10 +172,12 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int T) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L.hdr = take(HDR_WORDS * 4);
+  // the distinct experts follow the header directly (HDR_WORDS * 4 is 256 bytes), so the
+  // host reads both back in one copy
+  L.act_expert = take((size_t)E * 4);
   L.logits = take((size_t)((L.KS + 3) & ~3) * T * E * 4);  // [T][E][KS rounded to 4]
   L.x_h = take((size_t)T * H * 2);
   L.x_sc = take((size_t)T * L.KS * 4);
-  L.act_expert = take((size_t)E * 4);
   L.act_start = take((size_t)(E + 1) * 4);
   L.act_off = take((size_t)E * 8);
   L.act_fmt = take((size_t)E * 4);

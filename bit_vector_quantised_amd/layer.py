@@ -154,8 +154,9 @@ class TieredLayer:
         self.host_formats = [f for _, f in host_slots]
         self.c = _lib.Layer(hidden, inter, n_experts, top_k, self.router_w.data_ptr(), self.codebook.data_ptr(),
                             self.pool.data_ptr(), self.pool_bytes, self.slots.data_ptr())
+        self.readback = torch.empty(64 + n_experts, dtype=torch.int32, pin_memory=True)
         self.tier = _lib.ExpertTier(n_experts, self.host_pool.data_ptr(), host_slots,
-                                    [s * slot_bytes for s in range(n_dev_slots)])
+                                    [s * slot_bytes for s in range(n_dev_slots)], self.readback.data_ptr())
         _lib.tier_init(self.c, self.tier, self.slots.data_ptr(), torch.cuda.current_stream(self.device).cuda_stream)
 
     @classmethod

@@ -270,6 +270,10 @@ typedef struct moe_vq_tier {
   uint64_t *dev_slot_stamp;          /* [host] [n_dev_slots] state: last step that used it       */
   moe_vq_slot *slot_mirror;          /* [host] [E] state: the device slot table's contents      */
   uint64_t step;                     /* state: steps resolved so far                            */
+  uint32_t *readback;                /* [host] [64 + E] words, pinned (hipHostMalloc), or NULL:
+                                        where moe_vq_tier_resolve reads the step's selection;
+                                        pinned, that read is one asynchronous copy and one
+                                        synchronisation; NULL, a synchronous copy (slower)  */
 } moe_vq_tier;
 
 /* [host] Start a tier: every device slot free, every expert absent.  Writes the device
@@ -290,11 +294,11 @@ int moe_vq_tier_plan(const moe_vq_tier *tier, int n_experts, const int32_t *acti
                      int32_t *install_expert, int32_t *install_slot, int32_t *evict_expert,
                      int *n_install);
 
-/* [host] Resolve the misses of the step last routed on ws: synchronise stream, read the
- * step's distinct experts from ws, mark the resident ones as used, then copy every
- * planned expert slot from tier->host_pool into the device pool (asynchronous on
- * stream) and update slots[E] and the tier state.  Synchronises stream before it
- * returns.  *n_installed (may be NULL) receives the number of experts copied; if it is
+/* [host] Resolve the misses of the step last routed on ws: read the step's distinct
+ * experts from ws (through tier->readback; this synchronises stream), mark the resident
+ * ones as used, then copy every planned expert slot from tier->host_pool into the device
+ * pool (asynchronous on stream) and update slots[E] and the tier state.  Synchronises
+ * stream again before it returns when it copied anything.  *n_installed (may be NULL) receives the number of experts copied; if it is
  * not 0 the step must be routed again (moe_vq_route_topk) before FC1.  pool and slots
  * are the writable device buffers behind layer->pool and layer->slots.  Errors: as
  * moe_vq_tier_plan, and MOE_VQ_EHIP if a copy fails (the tier state is then updated

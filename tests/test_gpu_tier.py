@@ -74,3 +74,20 @@ def test_tier_refuses_a_step_wider_than_its_slots(mini_syn):
                           st.ws.data_ptr(), st.stream())
     assert ei.value.status == _lib.ENOSPACE
     assert tiered.tier.held() == [-1, -1, -1]
+
+
+@pytest.mark.parametrize("T", [1, 5, 33])
+def test_step_info_reads_the_selection(mini_syn, T):
+    """moe_vq_step_info (and the tier's read of a step, which shares it) returns the
+    step's status, its distinct experts in ascending order and its pair count."""
+    say(f"step_info T={T}")
+    dev = DeviceLayer.from_synth(mini_syn)
+    st = Step(dev, T)
+    x = x_tensor(mini_syn.x(n=T, stream=900 + T), "bf16")
+    st.route(x)
+    info = _lib.step_info(dev.c, T, st.ws.data_ptr(), st.stream())
+    ids = st.ids[:T].cpu().numpy()
+    want = sorted(set(int(e) for e in ids.ravel()))
+    assert info["status"] == _lib.OK and info["info"] == -1
+    assert info["experts"] == want and info["n_active"] == len(want)
+    assert info["n_pairs"] == T * MINI.top_k
