@@ -9,7 +9,7 @@ One step = route (router product, softmax/top-k/renormalise, worklist) -> FC1 wi
 SiLU*up -> FC2 with the weighted combine, for one batch of synthetic tokens whose
 activations already sit in HBM, through the single-call entry point moe_vq_forward.  The
 kernel-timing pass runs the same step as its three calls (route_topk, fc1_silu,
-fc2_combine: the same kernels) so that events can bracket FC1 and FC2.  The default workload is decode batch 1 of a
+fc2_combine: the same kernels) so that FC1 and FC2 can be timed one by one.  The default workload is decode batch 1 of a
 DeepSeek-style layer (H=7168, I=2048, 256 experts, top-8, VQ2 experts at 2.125
 bits/weight, all resident in one HBM slot pool).  Tokens are cycled from a pool of
 256 distinct pre-drawn tokens so consecutive steps touch different experts (the
@@ -19,13 +19,14 @@ popularity) the same way and reports it as the "b32" block of the same line.
 
 Prints one JSON line.  `value` is tokens/s of K steps timed on the host between two
 device synchronisations, with nothing else on the stream.  The same K steps then run
-again with HIP events recorded on the launch stream around FC1 and FC2 (each event
-costs the device a few microseconds, so they stay out of the throughput region), each
-step preceded by a 512 MiB read that evicts the memory-side cache;
-`roofline` rates the dominant kernel (FC1) by its algorithmic code+scale bytes per
-launch over the median duration those events measure (mean, p10 and p90 beside it).
-An event pair also counts the launch's dispatch, so the event duration exceeds the
-kernel's own run time in a rocprofv3 trace by about the dispatch latency.
+again, each preceded by a 512 MiB read that evicts the memory-side cache, with FC1 and
+FC2 launched through hipExtLaunchKernel with HIP events that record each kernel's own
+start and end (moe_vq_time_next_kernel; events cost the device a few microseconds, so
+they stay out of the throughput region).  `roofline` rates the dominant kernel (FC1) by
+its algorithmic code+scale bytes per launch over the mean duration those events measure
+(median, p10 and p90 beside it): the same run time a rocprofv3 kernel trace reports,
+without the dispatch that events recorded on the stream around the launch would add.
+Prefill is timed by events on the stream around the whole call.
 
 `roofline.traffic` is the FC1 kernel's HBM traffic per launch as the hardware
 counters saw it: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc
@@ -283,20 +284,19 @@ def measure(args, config, with_events=True):
             step.step(xb)  # the whole step in one call (moe_vq_forward)
             return
         step.route(xb)
-        if ev is not None:
-            ev[0].record(stream)
         if prefill:
+            if ev is not None:
+                ev[0].record(stream)
             step.prefill(xb)
             if ev is not None:
                 ev[1].record(stream)
-                ev[2].record(stream)
             return
+        if ev is not None:  # FC1's kernel records ev[0] at its start and ev[1] at its end
+            _lib.time_next_kernel(ev[0].cuda_event, ev[1].cuda_event)
         step.fc1(xb)
         if ev is not None:
-            ev[1].record(stream)
+            _lib.time_next_kernel(ev[2].cuda_event, ev[3].cuda_event)
         step.fc2(T)
-        if ev is not None:
-            ev[2].record(stream)
 
     print(f"[bench] {config}: warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -333,12 +333,17 @@ def measure(args, config, with_events=True):
     if not with_events:
         return out, dev, syn_dev, x_pool_np
 
-    # kernel durations: the same K steps with HIP events around FC1 and FC2, on the
-    # launch stream, each step after a 512 MiB read that evicts the 256 MB memory-side
-    # cache (so the experts come from HBM: the cold case).  The scrub only reads: a
-    # read-modify-write would leave dirty lines whose write-back competes with FC1.
+    # kernel durations: the same K steps again, each after a 512 MiB read that evicts the
+    # 256 MB memory-side cache (so the experts come from HBM: the cold case).  The scrub
+    # only reads: a read-modify-write would leave dirty lines whose write-back competes
+    # with FC1.  The FC kernels are launched with HIP events that record their own start
+    # and end (moe_vq_time_next_kernel), so a duration is the kernel's run alone, as in a
+    # rocprofv3 kernel trace; prefill is timed by events on the stream around the call.
     scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for ev in events:  # (a torch event holds a HIP event only once it has been recorded)
+        for e in ev:
+            e.record(stream)
     print(f"[bench] {config}: kernel timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -347,9 +352,8 @@ def measure(args, config, with_events=True):
     torch.cuda.synchronize()
     del scrub
     fc1_ms = np.array([events[i][0].elapsed_time(events[i][1]) for i in range(args.steps)])
-    fc2_ms = np.array([events[i][1].elapsed_time(events[i][2]) for i in range(args.steps)])
-    fc1_med = float(np.median(fc1_ms)) * 1e-3
-    fc2_med = float(np.median(fc2_ms)) * 1e-3
+    fc2_ms = np.array([events[i][2].elapsed_time(events[i][3]) for i in range(args.steps)]) if not prefill else None
+    fc1_avg = float(np.mean(fc1_ms)) * 1e-3
 
     def spread(ms):
         return {"median_us": float(np.median(ms)) * 1e3, "mean_us": float(np.mean(ms)) * 1e3,
@@ -358,7 +362,7 @@ def measure(args, config, with_events=True):
     if prefill:
         # FC1 + FC2 as grouped MFMA GEMMs: 2 * 3 * H * I flops per routed pair
         flops = 2.0 * 3 * cfg.hidden * cfg.inter * T * k
-        tflops = flops / fc1_med / 1e12  # the events bracket the whole prefill call
+        tflops = flops / fc1_avg / 1e12  # the events bracket the whole prefill call
         out["dtype"] = "fp16 MFMA (decoded weights x fp16-staged activations), fp32 accumulate"
         out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
@@ -367,8 +371,9 @@ def measure(args, config, with_events=True):
         out["prefill"] = {"code_bytes_per_step": step_b}
         return out, dev, syn_dev, x_pool_np
 
-    achieved = fc1_b / fc1_med / 1e9
-    code_stream = step_b / (fc1_med + fc2_med) / 1e9
+    fc2_avg = float(np.mean(fc2_ms)) * 1e-3
+    achieved = fc1_b / fc1_avg / 1e9
+    code_stream = step_b / (fc1_avg + fc2_avg) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_fc1_{config}.json")
     if os.path.exists(tfile):
@@ -381,8 +386,9 @@ def measure(args, config, with_events=True):
                        "kernel": ("fc_stream_kernel" if T <= 1 else "fc_mfma_kernel")
                        + " FC1 (gate/up code decode + SiLU*up)",
                        "bytes_per_launch": fc1_b, "launch_us": spread(fc1_ms),
-                       "timing": "HIP events on the launch stream around the launch, median over the "
-                                 "timed steps, memory-side cache evicted by a 512 MiB read before each step"}
+                       "timing": "HIP events recorded by the kernel's own launch (hipExtLaunchKernel) at its "
+                                 "start and end, mean over the timed steps, memory-side cache evicted by a "
+                                 "512 MiB read before each step"}
     out["code_stream"] = {"GBps": code_stream, "frac": code_stream / HBM_PEAK_GBPS, "bytes_per_step": step_b,
                           "fc1": spread(fc1_ms), "fc2": spread(fc2_ms)}
     return out, dev, syn_dev, x_pool_np

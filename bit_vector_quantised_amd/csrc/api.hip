@@ -217,6 +217,13 @@ hipError_t static_scratch(void** out) {
 
 }  // namespace
 
+namespace mvq {
+KernelTiming& kernel_timing() {
+  thread_local KernelTiming t;
+  return t;
+}
+}  // namespace mvq
+
 extern "C" {
 
 size_t moe_vq_expert_bytes(int format, int hidden, int inter) {
@@ -540,6 +547,11 @@ int moe_vq_tier_resolve(const moe_vq_layer* L, moe_vq_tier* tier, uint8_t* pool,
                                      hipMemcpyHostToDevice, st))))
     return r;
   return hip_status(hipStreamSynchronize(st));
+}
+
+int moe_vq_time_next_kernel(void* start_event, void* stop_event) {
+  kernel_timing() = KernelTiming{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  return MOE_VQ_OK;
 }
 
 const char* moe_vq_last_hip_error(void) {

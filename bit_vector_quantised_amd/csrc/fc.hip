@@ -653,7 +653,7 @@ static hipError_t launch_stream(const FcArgs& a, int K, int MT, int max_groups, 
     if (tiles < grid) grid = tiles;                                                          \
     *done = true;                                                                            \
     if (grid <= 0) return hipSuccess;                                                        \
-    fc_stream_kernel<C, M, FC1><<<(unsigned)grid, FC_THREADS, 0, st>>>(a);                   \
+    launch_fc_kernel(fc_stream_kernel<C, M, FC1>, (unsigned)grid, FC_THREADS, 0, st, a);      \
     return hipGetLastError();                                                                \
   }
   MVQ_STREAM_CASE(1, 1) MVQ_STREAM_CASE(2, 1) MVQ_STREAM_CASE(7, 1)
@@ -687,7 +687,7 @@ static hipError_t launch_generic(const FcArgs& a, int K, int MT, int max_groups,
       if (e != hipSuccess) return e;                                                         \
       attr_set = true;                                                                       \
     }                                                                                        \
-    kern<<<(unsigned)grid, FC_THREADS, dyn, st>>>(a);                                        \
+    launch_fc_kernel(kern, (unsigned)grid, FC_THREADS, (uint32_t)dyn, st, a);                \
     return hipGetLastError();                                                                \
   }
   MVQ_GEN_CASE(16, 1) MVQ_GEN_CASE(16, 2) MVQ_GEN_CASE(16, 4)

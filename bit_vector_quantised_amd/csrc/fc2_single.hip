@@ -203,8 +203,8 @@ hipError_t launch_fc2_single(const FcArgs& a, int MT, hipStream_t st, bool* done
   if (a.T != 1 || MT != 1 || a.k > F2S_KMAX || (a.I != 1024 && a.I != 2048)) return hipSuccess;
   const int grid = (a.H + F2S_ROWS - 1) / F2S_ROWS;
   *done = true;
-  if (a.I == 1024) fc2_single_kernel<1><<<grid, F2S_THREADS, 0, st>>>(a);
-  else fc2_single_kernel<2><<<grid, F2S_THREADS, 0, st>>>(a);
+  if (a.I == 1024) launch_fc_kernel(fc2_single_kernel<1>, (unsigned)grid, F2S_THREADS, 0, st, a);
+  else launch_fc_kernel(fc2_single_kernel<2>, (unsigned)grid, F2S_THREADS, 0, st, a);
   return hipGetLastError();
 }
 

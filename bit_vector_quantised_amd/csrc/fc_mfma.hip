@@ -785,7 +785,7 @@ hipError_t launch_mfma(const FcArgs& a, int K, int MT, int max_groups, int n_cu,
     if (tiles < grid) grid = tiles;                                                          \
     *done = true;                                                                            \
     if (grid <= 0) return hipSuccess;                                                        \
-    fc_mfma_kernel<C, FC1><<<(unsigned)grid, MfGeom<C, FC1>::THREADS, 0, st>>>(a);           \
+    launch_fc_kernel(fc_mfma_kernel<C, FC1>, (unsigned)grid, MfGeom<C, FC1>::THREADS, 0, st, a); \
     return hipGetLastError();                                                                \
   }
   MVQ_MFMA_CASE(1) MVQ_MFMA_CASE(2)

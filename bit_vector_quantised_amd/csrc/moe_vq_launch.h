@@ -1,9 +1,33 @@
 // Host-side launch entry points of the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "moe_vq_internal.h"
 
 namespace mvq {
+
+// Measurement hook (moe_vq_time_next_kernel): events that the next FC kernel launched on
+// this thread records at its start and at its end.
+struct KernelTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+KernelTiming& kernel_timing();  // this thread's hook
+
+// Launch one FC kernel; with the thread's hook set, through hipExtLaunchKernelGGL with
+// the hook's events (which then time the kernel alone), clearing the hook.
+template <typename... KArgs, typename... Args>
+inline void launch_fc_kernel(void (*kern)(KArgs...), unsigned grid, unsigned block, uint32_t shmem,
+                             hipStream_t st, Args... args) {
+  KernelTiming& t = kernel_timing();
+  if (t.start || t.stop) {
+    const KernelTiming use = t;
+    t = KernelTiming{};
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(block), shmem, st, use.start, use.stop, 0, args...);
+  } else {
+    kern<<<grid, block, shmem, st>>>(args...);
+  }
+}
 
 hipError_t launch_route(const RouteArgs& ra, int x_dtype, const WorklistArgs& wa, hipStream_t st);
 

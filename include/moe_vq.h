@@ -35,7 +35,8 @@
  * Conventions.
  *  - Pointers are device memory unless marked [host].  The caller owns every buffer
  *    (pool, slots, router weights, codebook, x, h, y, workspace); the library
- *    allocates and frees nothing and keeps no mutable global state.
+ *    allocates and frees nothing and keeps no mutable global state (apart from the
+ *    per-thread measurement hook moe_vq_time_next_kernel and the last HIP error).
  *  - stream is a hipStream_t (NULL = the default stream).  Every compute call only
  *    enqueues work on it and returns; nothing synchronises except moe_vq_check().
  *  - Argument errors are returned synchronously, before any HIP call is made.
@@ -250,6 +251,18 @@ int moe_vq_check(const void *ws, void *stream, int32_t *info);
  * (room for n_experts entries).  layer and n_tokens must match the route call. */
 int moe_vq_step_info(const moe_vq_layer *layer, int n_tokens, const void *ws, int32_t summary[4],
                      int32_t *experts, void *stream);
+
+/* Measurement hook for benchmarks (timing the kernels against the pages' throughput
+ * figures; Tandem-vLLM 0.2.0 announcement, "Speed").  The next decode FC kernel that a
+ * call made on this thread launches -- FC1's in moe_vq_fc1_silu, moe_vq_forward and
+ * moe_vq_forward_static, FC2's in moe_vq_fc2_combine; not the combine kernel and not
+ * prefill -- is launched with hipExtLaunchKernel so that start_event records the
+ * kernel's start and stop_event its end (hipEvent_t, created with timing; either may be
+ * NULL).  hipEventElapsedTime of the two is then the kernel's own run time, without the
+ * dispatch that an event recorded on the stream before the launch also counts.  The
+ * hook is per thread, used by one launch, and stays set until a launch uses it; NULL,
+ * NULL clears it.  Returns MOE_VQ_OK. */
+int moe_vq_time_next_kernel(void *start_event, void *stop_event);
 
 /* ---- Host-RAM expert tier.  Experts can live in a pinned host pool, with the device
  * pool holding only some of them: a GPU cache of the experts in use in front of the rest
