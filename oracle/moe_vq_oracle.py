@@ -52,6 +52,20 @@ are silent are listed next to each function (R1..R12) and in the design notes.
                       a value to test the clamp against; the pins only check that it
                       leaves values inside [-L, L] alone and that this module and the
                       scalar brute force below agree.]
+  O10 FP4 delta cache with a confidence gate
+                      a routed pair (t, i) of expert e = S_i whose renormalised weight
+                      w_i >= tau, and whose expert has a copy in the FP4 delta cache,
+                      takes O6 and O7 with the copy's matrices (the expert in the
+                      original FP4, MXFP4 here) instead of its 2-bit ones; every other
+                      pair is unchanged, and so is its weight in O8.  [Moet "2-bit
+                      experts on vLLM v0.24.0", first bullet: a delta cache and a
+                      confidence gate bring FP4 back where it matters; "Benchmark
+                      results", row glm-5.2-nvfp4: FP4 delta (auto) with a confidence
+                      gate tau = 0.60.  The pages do not describe the mechanism: R15
+                      reads the delta as the FP4 weights that replace the 2-bit ones
+                      for a gated pair, R16 reads the gate's confidence as the pair's
+                      renormalised routing weight; with tau >= 0.5 at most one pair
+                      of a token (its first) can pass.]
 
 Every value is computed in fp64 from the exact values of the stored fp16 / bf16 /
 fp32 inputs.  Decoding is exact in fp64 (a product of two fp16 numbers).
@@ -236,9 +250,16 @@ def expert_mlp(Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, xs: np.ndarray,
     return {"g": g, "u": u, "h": h, "o": o}
 
 
+def gate_passes(w: float, tau: Optional[float], has_copy: bool) -> bool:
+    """O10 / R16: a pair uses its expert's FP4 copy when the expert has one and the
+    pair's renormalised routing weight is at least tau."""
+    return tau is not None and has_copy and w >= tau
+
+
 def forward(layer, x64: np.ndarray, top_k: int,
             forced_selection: Optional[np.ndarray] = None, swiglu_limit: float = 0.0,
-            shared: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
+            shared: Optional[Dict[str, np.ndarray]] = None,
+            fp4_copy=None, gate_tau: Optional[float] = None) -> Dict[str, np.ndarray]:
     """The whole routed-expert step for tokens x64 [T, H].
 
     ``layer`` provides ``codebook`` (fp16 [128,4]), ``router_w`` (bf16 bits
@@ -247,11 +268,13 @@ def forward(layer, x64: np.ndarray, top_k: int,
     picks a different but equally valid expert at a near-tie); the weights are
     then renormalised over the forced set.  ``swiglu_limit`` > 0 applies the clamp
     (O6') in every expert; ``shared`` (the storage arrays of a shared expert) adds
-    O9.
+    O9.  ``fp4_copy(e)`` (the storage arrays of expert e's FP4 copy, or None) with
+    ``gate_tau`` applies O10.
 
-    Returns logits [T,E], ids [T,k], w [T,k], h [T,k,I], o [T,k,H], y [T,H], and
-    with ``shared`` also h_shared [T,I], o_shared [T,H] (y includes o_shared).
-    Each expert is decoded once and applied to all of its tokens.
+    Returns logits [T,E], ids [T,k], w [T,k], h [T,k,I], o [T,k,H], y [T,H],
+    copy [T,k] (True where the pair took the FP4 copy), and with ``shared`` also
+    h_shared [T,I], o_shared [T,H] (y includes o_shared).  Each expert (and each copy)
+    is decoded once and applied to all of its tokens.
     """
     x64 = np.asarray(x64, dtype=np.float64)
     T, H = x64.shape
@@ -259,13 +282,19 @@ def forward(layer, x64: np.ndarray, top_k: int,
     p = softmax(logits)
     ids = topk(logits, top_k) if forced_selection is None else np.asarray(forced_selection, dtype=np.int64)
     w = renormalise(p, ids)
+    copies = {}
+    if fp4_copy is not None and gate_tau is not None:
+        for e in sorted(set(ids.reshape(-1).tolist())):
+            copies[e] = fp4_copy(e)
+    use = np.array([[gate_passes(float(w[t, i]), gate_tau, copies.get(int(ids[t, i])) is not None)
+                     for i in range(top_k)] for t in range(T)], dtype=bool).reshape(T, top_k)
     I = None
     h_all: Dict = {}
     o_all: Dict = {}
-    for e in sorted(set(ids.reshape(-1).tolist())):
-        pairs = [(t, i) for t in range(T) for i in range(top_k) if ids[t, i] == e]
+    for e, c in sorted(set((int(ids[t, i]), bool(use[t, i])) for t in range(T) for i in range(top_k))):
+        pairs = [(t, i) for t in range(T) for i in range(top_k) if ids[t, i] == e and use[t, i] == c]
         tokens = [t for t, _ in pairs]
-        Wg, Wu, Wd = decode_expert(layer.expert(e), layer.codebook)
+        Wg, Wu, Wd = decode_expert(copies[e] if c else layer.expert(e), layer.codebook)
         I = Wg.shape[0]
         r_ = expert_mlp(Wg, Wu, Wd, x64[tokens], swiglu_limit)
         for r, (t, i) in enumerate(pairs):
@@ -280,7 +309,7 @@ def forward(layer, x64: np.ndarray, top_k: int,
             h_out[t, i] = h_all[(t, i)]
             o_out[t, i] = o_all[(t, i)]
             y[t] += w[t, i] * o_all[(t, i)]
-    out = {"logits": logits, "p": p, "ids": ids, "w": w, "h": h_out, "o": o_out, "y": y}
+    out = {"logits": logits, "p": p, "ids": ids, "w": w, "h": h_out, "o": o_out, "y": y, "copy": use}
     if shared is not None:
         Wg, Wu, Wd = decode_expert(shared, layer.codebook)
         r_ = expert_mlp(Wg, Wu, Wd, x64, swiglu_limit)
@@ -322,11 +351,12 @@ def topk_bruteforce(logits_row: Sequence[float], k: int):
 
 
 def forward_bruteforce(layer, x64: np.ndarray, top_k: int, swiglu_limit: float = 0.0,
-                       shared: Optional[Dict[str, np.ndarray]] = None) -> np.ndarray:
+                       shared: Optional[Dict[str, np.ndarray]] = None,
+                       fp4_copy=None, gate_tau: Optional[float] = None) -> np.ndarray:
     """y [T, H] from the dense all-expert form y[t] = sum_e M[t,e] * MLP_e(x_t) (+ the
     shared expert's MLP with weight 1), where M[t,e] is the renormalised routing weight
-    for selected experts and 0 otherwise.  Scalar Python loops only; meant for the
-    tiny layer."""
+    for selected experts and 0 otherwise, and MLP_e uses expert e's FP4 copy where
+    M[t,e] passes the gate (O10).  Scalar Python loops only; meant for the tiny layer."""
     x = [[float(v) for v in row] for row in np.asarray(x64, dtype=np.float64)]
     T, H = len(x), len(x[0])
     rw = bf16_value(layer.router_w)
@@ -347,7 +377,10 @@ def forward_bruteforce(layer, x64: np.ndarray, top_k: int, swiglu_limit: float =
         sel = topk_bruteforce(logits, top_k)
         psel = sum(p[e] for e in sel)
         M = [p[e] / psel if e in sel else 0.0 for e in range(E)]
-        mlps = [(layer.expert(e), M[e]) for e in range(E)]
+        mlps = []
+        for e in range(E):
+            cp = fp4_copy(e) if (fp4_copy is not None and gate_tau is not None and M[e] > 0.0) else None
+            mlps.append((cp if (cp is not None and M[e] >= gate_tau) else layer.expert(e), M[e]))
         if shared is not None:
             mlps.append((shared, 1.0))
         for ex_arr, m_e in mlps:

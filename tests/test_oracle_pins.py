@@ -450,3 +450,89 @@ def test_shared_expert_matches_scalar_bruteforce(tiny):
     assert np.abs(r["y"] - yb).max() <= 1e-12 * np.abs(yb).max()
     y_routed = oracle.forward(tiny, x, 2, swiglu_limit=L)["y"]
     np.testing.assert_allclose(r["y"] - y_routed, r["o_shared"], rtol=1e-12, atol=1e-14 * np.abs(yb).max())
+
+
+# ---------------------------------------------------------------------------------
+# O10: FP4 delta cache and confidence gate
+# ---------------------------------------------------------------------------------
+
+def _copies(layer, experts):
+    """FP4 copies (the expert stored as MXFP4) for the given experts, None for the rest."""
+    return lambda e: layer.expert_as(e, synth.FMT_MXFP4) if e in experts else None
+
+
+def _tau_between_weights(w, q=0.5):
+    """A gate value at quantile q of the routing weights, moved to the middle of the gap
+    around it, so that no weight lies near it (any rounding of w takes the same side)."""
+    s = np.unique(np.sort(w.reshape(-1)))
+    i = int(np.clip(round(q * (len(s) - 1)), 0, len(s) - 2))
+    assert s[i + 1] - s[i] > 1e-9
+    return 0.5 * (s[i] + s[i + 1])
+
+
+def test_gate_above_one_changes_nothing(tiny):
+    """tau > 1: no renormalised weight reaches it, so every pair keeps its 2-bit expert."""
+    x = oracle.x_value(tiny.x(), "f32")
+    k = tiny.cfg.top_k
+    r0 = oracle.forward(tiny, x, k)
+    r1 = oracle.forward(tiny, x, k, fp4_copy=_copies(tiny, set(range(tiny.cfg.n_experts))), gate_tau=1.01)
+    assert not r1["copy"].any()
+    assert np.array_equal(r0["y"], r1["y"]) and np.array_equal(r0["h"], r1["h"])
+
+
+def test_gate_zero_with_every_copy_is_the_fp4_layer(tiny):
+    """tau = 0 and a copy of every expert: every pair takes its copy, so the step is the
+    one of the layer whose experts are all stored in FP4 (same router, same selection)."""
+    x = oracle.x_value(tiny.x(), "f32")
+    k, E = tiny.cfg.top_k, tiny.cfg.n_experts
+    lay4 = ArrLayer(tiny.codebook, tiny.router_w, [tiny.expert_as(e, synth.FMT_MXFP4) for e in range(E)])
+    r = oracle.forward(tiny, x, k, fp4_copy=_copies(tiny, set(range(E))), gate_tau=0.0)
+    r4 = oracle.forward(lay4, x, k)
+    assert r["copy"].all()
+    assert np.array_equal(r["y"], r4["y"]) and np.array_equal(r["h"], r4["h"])
+
+
+@pytest.mark.parametrize("tau", [0.5, 0.6, 0.75])
+def test_gate_at_one_half_or_more_passes_only_the_first_pair(tiny, tau):
+    """The renormalised weights of a token sum to 1, so with tau >= 0.5 at most one pair
+    passes, and it is the first (largest weight); it passes exactly when w_0 >= tau."""
+    x = oracle.x_value(tiny.x(), "f32")
+    k, E = tiny.cfg.top_k, tiny.cfg.n_experts
+    r = oracle.forward(tiny, x, k, fp4_copy=_copies(tiny, set(range(E))), gate_tau=tau)
+    assert not r["copy"][:, 1:].any()
+    assert np.array_equal(r["copy"][:, 0], r["w"][:, 0] >= tau)
+
+
+def test_copy_changes_only_the_gated_pairs(tiny):
+    """Pairs that do not pass the gate (or whose expert has no copy) give the same h and o
+    as without the delta cache; the gated ones give the copy's MLP (SC1 on the copy)."""
+    x = oracle.x_value(tiny.x(), "f32")
+    k, E = tiny.cfg.top_k, tiny.cfg.n_experts
+    r0 = oracle.forward(tiny, x, k)
+    tau = _tau_between_weights(r0["w"], 0.5)
+    have = set(range(0, E, 2))
+    r = oracle.forward(tiny, x, k, fp4_copy=_copies(tiny, have), gate_tau=tau)
+    gated = r["copy"]
+    assert gated.any() and (~gated).any()
+    assert np.array_equal(gated, (r0["w"] >= tau) & np.isin(r0["ids"], list(have)))
+    assert np.array_equal(r["h"][~gated], r0["h"][~gated]) and np.array_equal(r["o"][~gated], r0["o"][~gated])
+    for t, i in zip(*np.nonzero(gated)):
+        e = int(r["ids"][t, i])
+        one = ArrLayer(tiny.codebook, tiny.router_w[:1].copy(), [tiny.expert_as(e, synth.FMT_MXFP4)])
+        yb = oracle.forward_bruteforce(one, x[t:t + 1], 1)[0]
+        assert np.abs(r["o"][t, i] - yb).max() <= 1e-12 * np.abs(yb).max()
+
+
+def test_gated_forward_matches_scalar_bruteforce(tiny):
+    """Copies for half the experts, tau inside the weight range: the sparse oracle equals
+    the dense scalar brute force, which applies the gate on its own weights."""
+    x = oracle.x_value(tiny.x(), "f32")[:4]
+    k, E = tiny.cfg.top_k, tiny.cfg.n_experts
+    r0 = oracle.forward(tiny, x, k)
+    tau = _tau_between_weights(r0["w"], 0.5)
+    above = r0["ids"][r0["w"] >= tau]
+    cp = _copies(tiny, set(range(E)) - {int(above[0])})  # one gated expert without a copy
+    r = oracle.forward(tiny, x, k, fp4_copy=cp, gate_tau=tau)
+    yb = oracle.forward_bruteforce(tiny, x, k, fp4_copy=cp, gate_tau=tau)
+    assert r["copy"].any() and (~r["copy"]).any()
+    assert np.abs(r["y"] - yb).max() <= 1e-12 * np.abs(yb).max()
