@@ -39,7 +39,7 @@ class Layer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
                 ("pool", ctypes.c_void_p), ("pool_bytes", ctypes.c_uint64), ("slots", ctypes.c_void_p),
-                ("swiglu_limit", ctypes.c_float)]
+                ("swiglu_limit", ctypes.c_float), ("delta_slots", ctypes.c_void_p), ("gate_tau", ctypes.c_float)]
 
 
 class Tier(ctypes.Structure):
@@ -189,7 +189,7 @@ def check(ws: int, stream: int = 0):
 def step_info(layer: Layer, n_tokens: int, ws: int, stream: int = 0):
     """dict(status, info, n_active, n_pairs, experts) of the last step on ws; synchronises."""
     summ = (ctypes.c_int32 * 4)()
-    ex = (ctypes.c_int32 * max(1, layer.n_experts))()
+    ex = (ctypes.c_int32 * max(1, layer.n_experts * (2 if layer.delta_slots else 1)))()
     _ok(_lib.moe_vq_step_info(ctypes.byref(layer), n_tokens, ws, summ, ex, stream), "step_info")
     n = int(summ[2])
     return {"status": int(summ[0]), "info": int(summ[1]), "n_active": n, "n_pairs": int(summ[3]),

@@ -38,12 +38,27 @@ int check_layer(const moe_vq_layer* L) {
     return MOE_VQ_EINVAL;
   if (L->pool_bytes == 0) return MOE_VQ_EINVAL;
   if (!(L->swiglu_limit >= 0.f && L->swiglu_limit <= 3.4e38f)) return MOE_VQ_EINVAL;  // finite, >= 0 (NaN fails)
+  if (L->delta_slots) {  // FP4 delta cache: copies listed as experts E + e
+    if (2 * L->n_experts > MAX_E || ((uintptr_t)L->delta_slots & 7)) return MOE_VQ_EINVAL;
+    if (!(L->gate_tau >= 0.f && L->gate_tau <= 3.4e38f)) return MOE_VQ_EINVAL;
+  }
   return MOE_VQ_OK;
+}
+
+// Experts the worklist can list: E, or 2E with an FP4 delta cache (the copy of e is E + e).
+int virt_experts(const moe_vq_layer* L) { return L->delta_slots ? 2 * L->n_experts : L->n_experts; }
+
+WsLayout layout_of(const moe_vq_layer* L, int T) {
+  return ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, T, virt_experts(L));
+}
+
+uint32_t key_of(const moe_vq_layer* L, int T) {
+  return shape_key(T, virt_experts(L), L->top_k, L->hidden, L->inter);
 }
 
 int check_ws(const moe_vq_layer* L, int T, const void* ws, size_t ws_bytes) {
   if (!ws || ((uintptr_t)ws & 255)) return MOE_VQ_EINVAL;
-  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, T);
+  const WsLayout W = layout_of(L, T);
   if (ws_bytes < W.total) return MOE_VQ_ENOSPACE;
   return MOE_VQ_OK;
 }
@@ -82,8 +97,8 @@ FcArgs make_fc_args(const moe_vq_layer* L, int T, void* ws, const WsLayout& W, b
   a.I = L->inter;
   a.k = L->top_k;
   a.KS = W.KS;
-  a.E = L->n_experts;
-  a.key = shape_key(T, L->n_experts, L->top_k, L->hidden, L->inter);
+  a.E = virt_experts(L);
+  a.key = key_of(L, T);
   a.lim = L->swiglu_limit;
   a.vq2 = slot_layout(MOE_VQ_FMT_VQ2, L->hidden, L->inter);
   a.mx4 = slot_layout(MOE_VQ_FMT_MXFP4, L->hidden, L->inter);
@@ -94,7 +109,7 @@ FcArgs make_fc_args(const moe_vq_layer* L, int T, void* ws, const WsLayout& W, b
 void route_args(const moe_vq_layer* L, const void* x, int x_dtype, int T, int32_t* topk_ids, float* topk_w, void* ws,
                 RouteArgs& ra, WorklistArgs& wa) {
   const int E = L->n_experts, H = L->hidden, I = L->inter, k = L->top_k;
-  const WsLayout W = ws_layout(E, H, I, k, T);
+  const WsLayout W = layout_of(L, T);
   ra = RouteArgs{};
   ra.router_w = static_cast<const uint16_t*>(L->router_w);
   ra.x = x;
@@ -111,8 +126,12 @@ void route_args(const moe_vq_layer* L, const void* x, int x_dtype, int T, int32_
   wa.x_dtype = x_dtype;
   wa.topk_ids = topk_ids;
   wa.slots = L->slots;
+  wa.delta_slots = L->delta_slots;
+  wa.pair_w = at<const float>(ws, W.pair_w);
+  wa.tau = L->gate_tau;
   wa.pool_bytes = L->pool_bytes;
   wa.T = T; wa.E = E; wa.k = k; wa.H = H; wa.I = I;
+  wa.EV = virt_experts(L);
   wa.MT1 = W.MT1;
   wa.MT2 = W.MT2;
   wa.rec1 = at<GroupRec>(ws, W.rec1);
@@ -127,7 +146,7 @@ void route_args(const moe_vq_layer* L, const void* x, int x_dtype, int T, int32_
   wa.grp1 = at<int32_t>(ws, W.grp1);
   wa.grp2 = at<int32_t>(ws, W.grp2);
   wa.pair_list = at<int32_t>(ws, W.pair_list);
-  wa.key = shape_key(T, E, k, H, I);
+  wa.key = key_of(L, T);
 }
 
 // The launches of one call, after its arguments have been checked.
@@ -140,7 +159,7 @@ hipError_t route_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, in
 }
 
 hipError_t fc1_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, void* ws, float* h, hipStream_t stream) {
-  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, T);
+  const WsLayout W = layout_of(L, T);
   FcArgs a = make_fc_args(L, T, ws, W, true);
   a.x_addr = (uint64_t)(uintptr_t)x;
   a.x_dtype = x_dtype;
@@ -151,7 +170,7 @@ hipError_t fc1_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, void
 
 hipError_t fc2_on(const moe_vq_layer* L, const float* h, int T, void* ws, float* y, hipStream_t stream,
                   bool accumulate = false) {
-  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, T);
+  const WsLayout W = layout_of(L, T);
   FcArgs a = make_fc_args(L, T, ws, W, false);
   a.h_in = h;
   a.out = at<float>(ws, W.o_buf);
@@ -245,7 +264,8 @@ int moe_vq_slot_layout(int format, int hidden, int inter, uint64_t offsets[7]) {
 size_t moe_vq_workspace_bytes(const moe_vq_layer* L, int n_tokens) {
   if (!L || !dims_ok(L->hidden, L->inter, L->n_experts, L->top_k)) return 0;
   if (n_tokens < 0 || n_tokens > MAX_T) return 0;
-  return ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens).total;
+  if (L->delta_slots && 2 * L->n_experts > MAX_E) return 0;
+  return layout_of(L, n_tokens).total;
 }
 
 int moe_vq_route_topk(const moe_vq_layer* L, const void* x, int x_dtype, int n_tokens,
@@ -296,7 +316,7 @@ int moe_vq_forward_static(const moe_vq_layer* L, const void* x, int x_dtype, int
   int st = check_forward(L, x, x_dtype, n_tokens, topk_ids, topk_w, h, y);
   if (st || n_tokens == 0) return st;
   if ((uintptr_t)status & 3) return MOE_VQ_EINVAL;
-  if (ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens).total > STATIC_SCRATCH_BYTES)
+  if (layout_of(L, n_tokens).total > STATIC_SCRATCH_BYTES)
     return MOE_VQ_ENOSPACE;
   void* ws = nullptr;
   if ((st = hip_status(static_scratch(&ws)))) return st;
@@ -321,7 +341,7 @@ int moe_vq_shared_expert(const moe_vq_layer* L, const void* x, int x_dtype, int 
   // with the combine adding to y.  The selection goes to the workspace's per-pair
   // arrays' neighbours: routing needs somewhere to write ids and weights, and with k = 1
   // and one expert they carry nothing the caller needs.
-  const WsLayout W = ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, n_tokens);
+  const WsLayout W = layout_of(L, n_tokens);
   int32_t* ids = at<int32_t>(ws, W.o_buf);
   float* w = at<float>(ws, W.o_buf + (size_t)n_tokens * 4);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -340,8 +360,8 @@ int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n
   if (n_tokens == 0) return MOE_VQ_OK;
   if (!x || !y || ((uintptr_t)x & 15) || ((uintptr_t)y & 15)) return MOE_VQ_EINVAL;
   if ((st = check_ws(L, n_tokens, ws, ws_bytes))) return st;
-  const int E = L->n_experts, H = L->hidden, I = L->inter, k = L->top_k, T = n_tokens;
-  const WsLayout W = ws_layout(E, H, I, k, T);
+  const int H = L->hidden, I = L->inter, k = L->top_k, T = n_tokens;
+  const WsLayout W = layout_of(L, T);
   PrefillArgs a{};
   a.pool = L->pool;
   a.codebook = static_cast<const uint16_t*>(L->codebook);
@@ -360,9 +380,9 @@ int moe_vq_prefill_gemm(const moe_vq_layer* L, const void* x, int x_dtype, int n
   a.h = at<uint16_t>(ws, W.h_pre);
   a.o_buf = at<float>(ws, W.o_buf);
   a.y = y;
-  a.T = T; a.H = H; a.I = I; a.k = k; a.E = E;
+  a.T = T; a.H = H; a.I = I; a.k = k; a.E = virt_experts(L);
   a.lim = L->swiglu_limit;
-  a.key = shape_key(T, E, k, H, I);
+  a.key = key_of(L, T);
   a.vq2 = slot_layout(MOE_VQ_FMT_VQ2, H, I);
   a.mx4 = slot_layout(MOE_VQ_FMT_MXFP4, H, I);
   return hip_status(launch_prefill(a, x_dtype, static_cast<hipStream_t>(stream)));
@@ -401,8 +421,9 @@ static int read_step(const moe_vq_layer* L, int n_tokens, const void* ws, int32_
                      void* stream, uint32_t* pinned) {
   if (!L || !dims_ok(L->hidden, L->inter, L->n_experts, L->top_k)) return MOE_VQ_EINVAL;
   if (!ws || !summary || n_tokens < 0 || n_tokens > MAX_T) return MOE_VQ_EINVAL;
-  const int E = L->n_experts;
-  const WsLayout W = ws_layout(E, L->hidden, L->inter, L->top_k, n_tokens);
+  if (L->delta_slots && 2 * L->n_experts > MAX_E) return MOE_VQ_EINVAL;
+  const int E = virt_experts(L);  // (the listed experts include the FP4 copies, E + e)
+  const WsLayout W = layout_of(L, n_tokens);
   static_assert(HDR_WORDS * 4 % 256 == 0, "the expert list must follow the header");
   uint32_t local[HDR_WORDS + MAX_E];
   uint32_t* buf = pinned ? pinned : local;
@@ -511,12 +532,18 @@ int moe_vq_tier_resolve(const moe_vq_layer* L, moe_vq_tier* tier, uint8_t* pool,
     return MOE_VQ_EINVAL;
   if (n_tokens < 0 || n_tokens > MAX_T || !tier->slot_mirror || !tier->dev_slot_offsets || !tier->host_pool)
     return MOE_VQ_EINVAL;
-  const int E = L->n_experts;
+  const int E = L->n_experts, EV = virt_experts(L);
   int32_t summary[4];
   int32_t active[MAX_E];
-  int r = read_step(L, n_tokens, ws, summary, active, stream, tier->readback);  // (synchronises stream)
+  // (the pinned read-back buffer has room for E listed experts: with an FP4 delta cache,
+  // which can list 2E, the read goes through the stack instead)
+  int r = read_step(L, n_tokens, ws, summary, active, stream,
+                    EV == E ? tier->readback : nullptr);  // (synchronises stream)
   if (r) return r;
-  const int n_active = summary[2] < 0 ? 0 : (summary[2] > E ? E : summary[2]);
+  const int n_listed = summary[2] < 0 ? 0 : (summary[2] > EV ? EV : summary[2]);
+  int n_active = 0;  // the tier manages slots[] only: FP4 copies (E + e) are left out
+  for (int i = 0; i < n_listed; ++i)
+    if (active[i] >= 0 && active[i] < E) active[n_active++] = active[i];
   tier->step += 1;
   for (int s = 0; s < tier->n_dev_slots; ++s) {
     const int e = tier->dev_slot_expert[s];

@@ -173,6 +173,7 @@ int moe_vq_cpu_experts(const moe_vq_layer* layer, const uint8_t* host_pool, uint
   if (n_tokens < 0 || n_tokens > 65536 || (x_dtype != MOE_VQ_F32 && x_dtype != MOE_VQ_BF16)) return MOE_VQ_EINVAL;
   const float lim = layer->swiglu_limit;
   if (!(lim >= 0.f && lim <= 3.4e38f)) return MOE_VQ_EINVAL;  // finite, >= 0 (NaN fails)
+  if (layer->delta_slots) return MOE_VQ_EUNSUPPORTED;  // the FP4 delta cache is device-side only
   if (n_tokens == 0) return MOE_VQ_OK;
   if (!host_pool || !host_slots || !codebook || !x || !topk_ids || !topk_w || !compute || !y) return MOE_VQ_EINVAL;
   if (n_threads < 1 || n_threads > CPU_MAX_THREADS) return MOE_VQ_EINVAL;

@@ -157,7 +157,8 @@ __host__ __device__ inline int pf_max_mtiles(int T, int k, int E) {
   return (int)(P / PF_BM + act);
 }
 
-// Workspace layout for (E, H, I, k, T).
+// Workspace layout for (E, H, I, k, T).  EV: the experts the worklist can list (E, or 2E
+// with an FP4 delta cache, whose copies are listed as experts E + e).
 struct WsLayout {
   size_t hdr, logits, x_h, x_sc, act_expert, act_start, act_off, act_fmt, grp1, grp2, rec1, rec2,
       pair_list, pair_w, o_buf, x16, x16_e, mt_pre, hmax, h_pre, total;
@@ -165,8 +166,9 @@ struct WsLayout {
   int MT1, MT2, G1, G2;
 };
 
-inline WsLayout ws_layout(int E, int H, int I, int k, int T) {
+inline WsLayout ws_layout(int E, int H, int I, int k, int T, int EV = 0) {
   WsLayout L{};
+  if (EV < E) EV = E;
   size_t P = (size_t)T * k;
   L.KS = n_slices(H);
   size_t off = 0;
@@ -174,19 +176,19 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int T) {
   L.hdr = take(HDR_WORDS * 4);
   // the distinct experts follow the header directly (HDR_WORDS * 4 is 256 bytes), so the
   // host reads both back in one copy
-  L.act_expert = take((size_t)E * 4);
+  L.act_expert = take((size_t)EV * 4);
   L.logits = take((size_t)((L.KS + 3) & ~3) * T * E * 4);  // [T][E][KS rounded to 4]
   L.x_h = take((size_t)T * H * 2);
   L.x_sc = take((size_t)T * L.KS * 4);
-  L.act_start = take((size_t)(E + 1) * 4);
-  L.act_off = take((size_t)E * 8);
-  L.act_fmt = take((size_t)E * 4);
-  L.grp1 = take((size_t)(E + 1) * 4);
-  L.grp2 = take((size_t)(E + 1) * 4);
+  L.act_start = take((size_t)(EV + 1) * 4);
+  L.act_off = take((size_t)EV * 8);
+  L.act_fmt = take((size_t)EV * 4);
+  L.grp1 = take((size_t)(EV + 1) * 4);
+  L.grp2 = take((size_t)(EV + 1) * 4);
   L.MT1 = fc_group_tokens(T, H, true);
   L.MT2 = fc_group_tokens(T, I, false);
-  L.G1 = fc_max_groups(T, k, E, L.MT1);
-  L.G2 = fc_max_groups(T, k, E, L.MT2);
+  L.G1 = fc_max_groups(T, k, EV, L.MT1);
+  L.G2 = fc_max_groups(T, k, EV, L.MT2);
   L.rec1 = take((size_t)L.G1 * sizeof(GroupRec));
   L.rec2 = take((size_t)L.G2 * sizeof(GroupRec));
   L.pair_list = take(P * 4);
@@ -196,7 +198,7 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int T) {
   // prefix over the active experts, the per-pair max |h| and h itself
   L.x16 = take((size_t)T * H * 2);
   L.x16_e = take((size_t)T * 4);
-  L.mt_pre = take((size_t)(E + 1) * 4);
+  L.mt_pre = take((size_t)(EV + 1) * 4);
   L.hmax = take(P * 4);
   L.h_pre = take(P * I * 2);
   L.total = off;
@@ -223,8 +225,12 @@ struct WorklistArgs {
   int x_dtype;
   const int32_t* topk_ids;
   const moe_vq_slot* slots;
+  const moe_vq_slot* delta_slots;  // FP4 copies, or null (no delta cache)
+  const float* pair_w;             // [T*k] routing weights (the gate reads them)
+  float tau;                       // confidence gate of the delta cache
   uint64_t pool_bytes;
   int T, E, k, H, I, MT1, MT2;
+  int EV;                          // experts the worklist can list: E, or 2E with copies
   uint32_t* hdr;
   int32_t* act_expert;
   int32_t* act_start;

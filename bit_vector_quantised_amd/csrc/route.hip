@@ -174,11 +174,17 @@ constexpr int PL_LDS = 2048;  // pair lists up to this length are also kept in L
 // Single workgroup: (optionally the top-k of every token, one wave per token), then
 // group the routed pairs by expert (stable: ascending pair index p = t*k + i within an
 // expert), list the distinct experts in ascending id with their slot lookups, write
-// the FC token-group records, and validate every selected slot.
+// the FC token-group records, and validate every selected slot.  With an FP4 delta
+// cache (a.EV = 2E) a pair whose weight passes the confidence gate, and whose expert has
+// a copy, is listed under the copy, expert E + e, whose slot is delta_slots[e]
+// (vLLM-Moet README, "2-bit experts on vLLM v0.24.0": a delta cache and a confidence
+// gate bring FP4 back where it matters).
 template <bool FUSED, int NPL>
 __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistArgs a) {
   __shared__ int cnt[16 * MAX_E];
   __shared__ int ids_lds[FUSED ? FUSED_TOPK_MAX_T * MAX_K : 1];
+  __shared__ float w_lds[FUSED ? FUSED_TOPK_MAX_T * MAX_K : 1];
+  __shared__ uint8_t has_copy[MAX_E / 2];
   __shared__ int4 wave_tot[16];
   __shared__ int4 s_total;
   __shared__ int s_bad_expert;
@@ -191,40 +197,48 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   // all four scalar-cache lines of the arguments read at the start, together
   asm volatile("" ::"s"(ra.logits), "s"(a.slots), "s"(a.hdr), "s"(a.rec1));
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int E = a.E, T = a.T, k = a.k;
-  // the slot of expert tid is read first, so that its latency overlaps the top-k
+  const int E = a.E, EV = a.EV, T = a.T, k = a.k;
+  // the slot of (listed) expert tid is read first, so that its latency overlaps the top-k
   moe_vq_slot sl{};
-  if (tid < E) sl = a.slots[tid];
+  if (tid < EV) sl = tid < E ? a.slots[tid] : a.delta_slots[tid - E];
   // counting waves: wave w takes tokens [w*C, (w+1)*C), with as many waves as tokens
   // (up to 16), so that the per-expert totals sum over no more waves than needed
   const int NWC = T < 16 ? (T > 1 ? T : 1) : 16;
   const int C = (T + NWC - 1) / NWC;
-  for (int i = tid; i < NWC * E; i += 1024) cnt[i] = 0;
+  for (int i = tid; i < NWC * EV; i += 1024) cnt[i] = 0;
   if (tid == 0) { s_bad_expert = 0x7FFFFFFF; s_bad_id = 0; }
+  if (EV > E && tid >= E && tid < EV) has_copy[tid - E] = sl.format != MOE_VQ_FMT_ABSENT;
   if (FUSED) {
     for (int t = wave; t < T; t += 16) {
       int id = 0;
-      topk_token<NPL>(ra, t, lane, &id);
-      if (lane < k) ids_lds[t * k + lane] = id;
+      float w = 0.f;
+      topk_token<NPL>(ra, t, lane, &id, &w);
+      if (lane < k) { ids_lds[t * k + lane] = id; w_lds[t * k + lane] = w; }
     }
   }
   __syncthreads();
   auto id_of = [&](int p) -> int { return FUSED ? ids_lds[p] : a.topk_ids[p]; };
+  // the expert pair p (of expert e) is listed under: the FP4 copy E + e when the cache
+  // holds one and the pair's routing weight reaches the gate
+  auto listed = [&](int p, int e) -> int {
+    if (EV == E || !has_copy[e]) return e;
+    return (FUSED ? w_lds[p] : a.pair_w[p]) >= a.tau ? E + e : e;
+  };
   const int tb = min(T, wave * C), te = min(T, tb + C);
   for (int p = tb * k + lane; p < te * k; p += 64) {
     const int e = id_of(p);
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave * E + e], 1);
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave * EV + listed(p, e)], 1);
     else s_bad_id = 1;
   }
   __syncthreads();
   int tot = 0;
-  if (tid < E)
-    for (int w = 0; w < NWC; ++w) tot += cnt[w * E + tid];
+  if (tid < EV)
+    for (int w = 0; w < NWC; ++w) tot += cnt[w * EV + tid];
   const int g1 = (tot + a.MT1 - 1) / a.MT1;
   const int g2 = (tot + a.MT2 - 1) / a.MT2;
   const int4 sc = block_scan_excl4(make_int4(tot, tot > 0 ? 1 : 0, g1, g2), wave_tot, &s_total);
   const int start = sc.x, rank = sc.y, gs1 = sc.z, gs2 = sc.w;
-  if (tid < E && tot > 0) {
+  if (tid < EV && tot > 0) {
     uint32_t fmt = sl.format;
     const uint64_t off = sl.byte_offset;
     uint64_t need = 0;
@@ -250,11 +264,11 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
     a.grp2[n_active] = s_total.w;
   }
   // per-wave bases: cnt[w][e] <- start[e] + sum_{w' < w} cnt[w'][e]
-  if (tid < E) {
+  if (tid < EV) {
     int run = start;
     for (int w = 0; w < NWC; ++w) {
-      const int c = cnt[w * E + tid];
-      cnt[w * E + tid] = run;
+      const int c = cnt[w * EV + tid];
+      cnt[w * EV + tid] = run;
       run += c;
     }
   }
@@ -266,7 +280,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
       const int p = t * k + lane;
       const int e = id_of(p);
       if ((unsigned)e < (unsigned)E) {
-        const int pos = atomicAdd(&cnt[wave * E + e], 1);
+        const int pos = atomicAdd(&cnt[wave * EV + listed(p, e)], 1);
         a.pair_list[pos] = p;
         pl_lds[pos < PL_LDS ? pos : 0] = p;
       }

@@ -96,8 +96,10 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
 // top-k, the k experts ordered by id, their slots checked, and -- with write -- the same
 // worklist as the many-token worklist kernel (experts ascending, one pair and one group of
 // each list per expert) and the header.  Lane i < k returns its pick: the expert of pair i
-// (pair index p = i), its rank among the k experts, its slot offset and format (absent
-// when the slot is missing, misaligned or outside the pool).
+// (pair index p = i; E + e for the FP4 copy of e when the delta cache holds one and the
+// pair's weight reaches the confidence gate), its rank among the k listed experts, its
+// slot offset and format (absent when the slot is missing, misaligned or outside the
+// pool).
 struct OneTokenPick {
   int id, rank;
   uint64_t off;
@@ -117,11 +119,9 @@ __device__ __forceinline__ OneTokenPick one_token_pick(const RouteArgs& ra, cons
     pre[i] = e < a.E ? a.slots[e] : moe_vq_slot{};
   }
   int id = 0;
-  if (write) topk_token<NPL, true>(ra, 0, lane, &id);
-  else topk_token<NPL, false>(ra, 0, lane, &id);
-  // rank of this lane's expert among the k (distinct) experts
-  int rank = 0;
-  for (int j = 0; j < k; ++j) rank += __shfl(id, j) < id ? 1 : 0;
+  float w = 0.f;
+  if (write) topk_token<NPL, true>(ra, 0, lane, &id, &w);
+  else topk_token<NPL, false>(ra, 0, lane, &id, &w);
   moe_vq_slot sl{};
   {
     const int src = id & 63, hi = id >> 6;  // (every lane takes part in the shuffles)
@@ -136,6 +136,17 @@ __device__ __forceinline__ OneTokenPick one_token_pick(const RouteArgs& ra, cons
       }
     }
   }
+  // FP4 delta cache: the pair takes its expert's copy (listed as E + e) when the cache
+  // holds one and the pair's weight reaches the confidence gate
+  int v = id;
+  if (a.EV > a.E) {
+    moe_vq_slot d{};
+    if (lane < k && w >= a.tau) d = a.delta_slots[id];
+    if (d.format != MOE_VQ_FMT_ABSENT) { v = a.E + id; sl = d; }
+  }
+  // rank of this lane's listed expert among the k (distinct) ones
+  int rank = 0;
+  for (int j = 0; j < k; ++j) rank += __shfl(v, j) < v ? 1 : 0;
   uint32_t fmt = sl.format;
   const uint64_t off = sl.byte_offset;
   uint64_t need = 0;
@@ -143,12 +154,12 @@ __device__ __forceinline__ OneTokenPick one_token_pick(const RouteArgs& ra, cons
   const bool ok = need != 0 && (off & 255) == 0 && off <= a.pool_bytes && need <= a.pool_bytes - off;
   if (!ok) fmt = MOE_VQ_FMT_ABSENT;
   if (write) {
-    int bad = (lane < k && !ok) ? id : 0x7FFFFFFF;
+    int bad = (lane < k && !ok) ? v : 0x7FFFFFFF;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) bad = min(bad, __shfl_xor(bad, d));
     if (lane < k) {
       a.pair_list[rank] = lane;
-      a.act_expert[rank] = id;
+      a.act_expert[rank] = v;
       a.act_start[rank] = rank;
       a.act_off[rank] = off;
       a.act_fmt[rank] = fmt;
@@ -159,7 +170,7 @@ __device__ __forceinline__ OneTokenPick one_token_pick(const RouteArgs& ra, cons
       r.p0 = rank;
       r.mcount = 1;
       r.fmt = fmt;
-      r.expert = id;
+      r.expert = v;
 #pragma unroll
       for (int j = 0; j < MAX_MT; ++j) r.pair[j] = lane;
 #pragma unroll
@@ -186,7 +197,7 @@ __device__ __forceinline__ OneTokenPick one_token_pick(const RouteArgs& ra, cons
       a.hdr[HDR_X_DTYPE] = (uint32_t)a.x_dtype;
     }
   }
-  return OneTokenPick{id, rank, off, fmt};
+  return OneTokenPick{v, rank, off, fmt};
 }
 
 }  // namespace mvq

@@ -35,16 +35,28 @@ def pack_slot(expert: Dict[str, np.ndarray], hidden: int, inter: int, fmt: Optio
     return buf
 
 
+def _slot_table(offsets: np.ndarray, formats: Sequence[int]) -> np.ndarray:
+    slots = np.zeros(len(offsets), dtype=[("byte_offset", "<u8"), ("format", "<u4"), ("reserved", "<u4")])
+    slots["byte_offset"] = offsets
+    slots["format"] = np.asarray(formats, dtype=np.uint32)
+    return slots
+
+
 class DeviceLayer:
     """Slot pool + slot table + router weights + codebook in device memory.
 
     experts(e) returns expert e's storage arrays (see synth); formats[e] gives its
-    format, MOE_VQ_FMT_ABSENT leaving the slot empty (not resident).
+    format, MOE_VQ_FMT_ABSENT leaving the slot empty (not resident).  With copies (a
+    function e -> storage arrays or None), the experts it returns arrays for also get an
+    FP4 copy in the FP4 delta cache (the layer's delta_slots, placed after the experts in
+    the same pool), used by the routed pairs whose weight reaches gate_tau.
     """
 
     def __init__(self, hidden: int, inter: int, n_experts: int, top_k: int, codebook: np.ndarray,
                  router_w_bits: np.ndarray, experts: Callable[[int], Dict[str, np.ndarray]],
-                 formats: Sequence[int], device: str = "cuda", swiglu_limit: float = 0.0):
+                 formats: Sequence[int], device: str = "cuda", swiglu_limit: float = 0.0,
+                 copies: Optional[Callable[[int], Optional[Dict[str, np.ndarray]]]] = None,
+                 gate_tau: float = 0.0):
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.device = torch.device(device)
         offsets = np.zeros(n_experts, dtype=np.uint64)
@@ -55,6 +67,13 @@ class DeviceLayer:
                 continue
             offsets[e] = total
             total += _lib.expert_bytes(f, hidden, inter)
+        copy_arrays = [copies(e) for e in range(n_experts)] if copies is not None else [None] * n_experts
+        copy_formats = [int(a["format"]) if a is not None else _lib.FMT_ABSENT for a in copy_arrays]
+        copy_offsets = np.zeros(n_experts, dtype=np.uint64)
+        for e in range(n_experts):
+            if copy_arrays[e] is not None:
+                copy_offsets[e] = total
+                total += _lib.expert_bytes(copy_formats[e], hidden, inter)
         self.pool_bytes = max(total, 256)
         self.pool = torch.empty(self.pool_bytes, dtype=torch.uint8, device=self.device)
         for e in range(n_experts):
@@ -64,31 +83,43 @@ class DeviceLayer:
             buf = pack_slot(experts(e), hidden, inter, f)
             o = int(offsets[e])
             self.pool[o:o + buf.size].copy_(torch.from_numpy(buf))
-        slots = np.zeros(n_experts, dtype=[("byte_offset", "<u8"), ("format", "<u4"), ("reserved", "<u4")])
-        slots["byte_offset"] = offsets
-        slots["format"] = np.asarray(formats, dtype=np.uint32)
+        for e in range(n_experts):
+            if copy_arrays[e] is not None:
+                buf = pack_slot(copy_arrays[e], hidden, inter)
+                o = int(copy_offsets[e])
+                self.pool[o:o + buf.size].copy_(torch.from_numpy(buf))
         self.slot_offsets = offsets
         self.formats = np.asarray(formats, dtype=np.int32)
-        self.slots = torch.from_numpy(slots.view(np.uint8).copy()).to(self.device)
+        self.slots = torch.from_numpy(_slot_table(offsets, formats).view(np.uint8).copy()).to(self.device)
+        self.copy_formats = np.asarray(copy_formats, dtype=np.int32)
+        self.delta_slots = None
+        if copies is not None:
+            self.delta_slots = torch.from_numpy(
+                _slot_table(copy_offsets, copy_formats).view(np.uint8).copy()).to(self.device)
         self.router_w = torch.from_numpy(np.ascontiguousarray(router_w_bits).view(np.int16)).to(self.device)
         self.codebook = torch.from_numpy(np.ascontiguousarray(codebook).view(np.int16)).to(self.device)
         self.c = _lib.Layer(hidden, inter, n_experts, top_k, self.router_w.data_ptr(), self.codebook.data_ptr(),
-                            self.pool.data_ptr(), self.pool_bytes, self.slots.data_ptr(), float(swiglu_limit))
+                            self.pool.data_ptr(), self.pool_bytes, self.slots.data_ptr(), float(swiglu_limit),
+                            self.delta_slots.data_ptr() if self.delta_slots is not None else None,
+                            float(gate_tau))
 
     @classmethod
     def from_synth(cls, syn, device: str = "cuda", formats: Optional[Sequence[int]] = None,
-                   swiglu_limit: float = 0.0):
+                   swiglu_limit: float = 0.0, fp4_copies: Optional[Sequence[int]] = None,
+                   gate_tau: float = 0.0):
+        """fp4_copies: the experts that get an FP4 (MXFP4) copy in the delta cache."""
         cfg = syn.cfg
         fm = syn.formats if formats is None else formats
+        copies = None
+        if fp4_copies is not None:
+            have = set(int(e) for e in fp4_copies)
+            copies = lambda e: syn.expert_as(e, _lib.FMT_MXFP4) if e in have else None  # noqa: E731
         return cls(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, syn.codebook, syn.router_w,
-                   lambda e: syn.expert_as(e, fm[e]), fm, device, swiglu_limit)
+                   lambda e: syn.expert_as(e, fm[e]), fm, device, swiglu_limit, copies, gate_tau)
 
     def set_slots(self, offsets: np.ndarray, formats: Sequence[int]) -> None:
         """Rewrite the slot table (e.g. to mark experts absent)."""
-        slots = np.zeros(self.n_experts, dtype=[("byte_offset", "<u8"), ("format", "<u4"), ("reserved", "<u4")])
-        slots["byte_offset"] = offsets
-        slots["format"] = np.asarray(formats, dtype=np.uint32)
-        self.slots.copy_(torch.from_numpy(slots.view(np.uint8).copy()))
+        self.slots.copy_(torch.from_numpy(_slot_table(offsets, formats).view(np.uint8).copy()))
 
 
 class SharedExpert:

@@ -100,6 +100,8 @@ typedef struct moe_vq_layer {
   uint64_t pool_bytes;         /* size of the pool in bytes                 */
   const moe_vq_slot *slots;    /* [E] expert id -> slot                     */
   float swiglu_limit;          /* SwiGLU clamp L (0: none), see below       */
+  const moe_vq_slot *delta_slots; /* [E] FP4 delta cache, or NULL; see below */
+  float gate_tau;              /* confidence gate of the delta cache        */
 } moe_vq_layer;
 /* swiglu_limit: with L > 0 every expert's FC1 output is h = silu(min(g, L)) * clamp(u,
  * -L, L) instead of silu(g) * u, on every path (decode, prefill, the host miss path).
@@ -107,7 +109,22 @@ typedef struct moe_vq_layer {
  * checkpoint has a SwiGLU clamp that a port must not omit, but gives neither its form
  * nor its constant; this form (gate capped above, up clamped on both sides) is the one
  * read here.  L must be finite and >= 0 (MOE_VQ_EINVAL otherwise).  Zero-initialising
- * the struct leaves the clamp off. */
+ * the struct leaves the clamp off.
+ *
+ * delta_slots, gate_tau: the FP4 delta cache and its confidence gate (vLLM-Moet README,
+ * "2-bit experts on vLLM v0.24.0", first bullet: a delta cache and a confidence gate
+ * bring FP4 back where it matters; "Benchmark results", row glm-5.2-nvfp4: the gate at
+ * tau = 0.60).  The pages do not describe the mechanism; the reading here: delta_slots[e]
+ * is the slot (in the same pool) of expert e's copy in FP4 (normally MXFP4; format
+ * MOE_VQ_FMT_ABSENT: no copy), and a routed pair whose renormalised weight is >= gate_tau
+ * and whose expert has a copy is computed from the copy instead of slots[e], on every
+ * path (decode and prefill).  Its weight in the combine is unchanged.  With gate_tau >=
+ * 0.5 at most one pair of a token passes (its first).  In the workspace, the step's
+ * distinct experts (moe_vq_step_info) then count the copies as experts E + e, and a copy
+ * whose slot is bad is reported as expert E + e.  NULL (zero-initialised) leaves the cache
+ * off.  With delta_slots set, n_experts must be <= 512 and gate_tau finite and >= 0
+ * (MOE_VQ_EINVAL otherwise); the host miss path (moe_vq_cpu_experts) does not take such a
+ * layer (MOE_VQ_EUNSUPPORTED), and the tier (moe_vq_tier_resolve) manages slots[] only. */
 
 /* [host] Bytes of one expert slot of the given format, 0 if an argument is invalid. */
 size_t moe_vq_expert_bytes(int format, int hidden, int inter);
@@ -248,7 +265,8 @@ int moe_vq_check(const void *ws, void *stream, int32_t *info);
  * summary[0] = device status, summary[1] = offending expert or -1, summary[2] = number
  * of distinct selected experts (n_active), summary[3] = routed pairs placed.  If
  * experts is not NULL it receives the n_active distinct expert ids in ascending order
- * (room for n_experts entries).  layer and n_tokens must match the route call. */
+ * (room for n_experts entries; 2 n_experts with an FP4 delta cache, whose copies are
+ * listed as E + e).  layer and n_tokens must match the route call. */
 int moe_vq_step_info(const moe_vq_layer *layer, int n_tokens, const void *ws, int32_t summary[4],
                      int32_t *experts, void *stream);
 

@@ -53,9 +53,10 @@ def rel_err_rows(a: np.ndarray, ref: np.ndarray) -> np.ndarray:
 
 
 def compare(syn, x_np: np.ndarray, x_dtype: str, g: dict, top_k: int, tokens=None, check_h=True,
-            swiglu_limit=0.0, shared=None):
+            swiglu_limit=0.0, shared=None, fp4_copy=None, gate_tau=None):
     """Compare one GPU step with the oracle on the given tokens (all by default); with
-    swiglu_limit / shared, against the oracle's clamped layer / with its shared expert."""
+    swiglu_limit / shared / fp4_copy and gate_tau, against the oracle's clamped layer /
+    with its shared expert / with its FP4 delta cache."""
     x64 = oracle.x_value(x_np, x_dtype)
     T = x64.shape[0]
     tokens = list(range(T)) if tokens is None else list(tokens)
@@ -65,7 +66,8 @@ def compare(syn, x_np: np.ndarray, x_dtype: str, g: dict, top_k: int, tokens=Non
     assert oracle.selection_is_valid(g["ids"], logits, delta, top_k), "GPU selection is not a valid top-k"
     n_diff = int((g["ids"] != ref_ids).any(axis=1).sum())
     sel = g["ids"][tokens]
-    r = oracle.forward(syn, x64[tokens], top_k, forced_selection=sel, swiglu_limit=swiglu_limit, shared=shared)
+    r = oracle.forward(syn, x64[tokens], top_k, forced_selection=sel, swiglu_limit=swiglu_limit, shared=shared,
+                       fp4_copy=fp4_copy, gate_tau=gate_tau)
     werr = np.abs(g["w"][tokens] - r["w"]).max()
     assert werr <= W_TOL, f"routing weights off by {werr}"
     assert np.all(np.abs(g["w"].sum(axis=1) - 1.0) <= 4 * top_k * 2.0 ** -24)

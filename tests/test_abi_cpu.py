@@ -236,3 +236,36 @@ def test_swiglu_limit_and_shared_expert_arguments():
     assert raw.moe_vq_shared_expert(P(S), X, _lib.F32, 0, WS, ws_s, H_, Y, None) == _lib.OK
     S.swiglu_limit = float("nan")
     assert raw.moe_vq_shared_expert(P(S), X, _lib.F32, 4, WS, ws_s, H_, Y, None) == _lib.EINVAL
+
+
+def test_delta_cache_arguments():
+    """FP4 delta cache: its copies are listed as experts E + e, so the workspace grows;
+    more than 512 experts, a negative or NaN gate, or the host miss path are refused."""
+    raw = _lib.raw()
+    P = ctypes.byref
+    X, IDS, W, WS = 0x40000, 0x50000, 0x60000, 0x700000
+    L = fake_layer(E=128)
+    D = fake_layer(E=128)
+    D.delta_slots, D.gate_tau = 0x38000, 0.6
+    assert _lib.workspace_bytes(D, 64) > _lib.workspace_bytes(L, 64)
+    ws_d = _lib.workspace_bytes(D, 4)
+    assert ws_d > _lib.workspace_bytes(L, 4)
+    assert raw.moe_vq_route_topk(P(D), X, _lib.F32, 0, IDS, W, WS, ws_d, None) == _lib.OK
+    # the layer without the cache needs less: with the cache the smaller size is refused
+    assert raw.moe_vq_route_topk(P(D), X, _lib.F32, 4, IDS, W, WS, _lib.workspace_bytes(L, 4), None) \
+        == _lib.ENOSPACE
+    for tau in (-0.1, float("nan"), float("inf")):
+        bad = fake_layer()
+        bad.delta_slots, bad.gate_tau = 0x38000, tau
+        assert raw.moe_vq_route_topk(P(bad), X, _lib.F32, 0, IDS, W, WS, ws_d, None) == _lib.EINVAL
+    big = fake_layer(E=513, k=2)
+    big.delta_slots, big.gate_tau = 0x38000, 0.6
+    assert _lib.workspace_bytes(big, 4) == 0
+    assert raw.moe_vq_route_topk(P(big), X, _lib.F32, 0, IDS, W, WS, 1 << 30, None) == _lib.EINVAL
+    misaligned = fake_layer()
+    misaligned.delta_slots, misaligned.gate_tau = 0x38004, 0.6
+    assert raw.moe_vq_route_topk(P(misaligned), X, _lib.F32, 0, IDS, W, WS, ws_d, None) == _lib.EINVAL
+    Y, CMP, HP, CB = 0x90000, 0xA0000, 0xB0000, 0xD0000
+    HS = (_lib.Slot * 128)()
+    assert raw.moe_vq_cpu_experts(P(D), HP, 1 << 20, HS, CB, X, _lib.F32, 4, IDS, W, CMP, Y, 1) \
+        == _lib.EUNSUPPORTED
