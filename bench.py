@@ -53,9 +53,25 @@ WORKLOADS = {
     "b32": "decode batch 32: H=7168 I=2048 E=256 top-8, VQ2, router logits with Zipf(1.1) expert popularity",
     "b8mx": "decode batch 8: 52 most-routed experts MXFP4, 204 VQ2, Zipf(1.1) routing",
     "p4096": "prefill chunk of 4096 tokens: H=7168 I=2048 E=256 top-8, VQ2, grouped fp16 MFMA GEMMs",
+    "b1d": "decode batch 1 as b1, with an FP4 (MXFP4) copy of every expert in the delta cache and the "
+           "confidence gate at 0.60",
+    "b32d": "decode batch 32 as b32, with an FP4 (MXFP4) copy of every expert in the delta cache and the "
+            "confidence gate at 0.60",
 }
 PREFILL = {"p4096"}
+DELTA = {"b1d": "b1", "b32d": "b32"}  # workload -> the preset it adds the FP4 delta cache to
+GATE_TAU = 0.60
+
+
+def preset(config):
+    import synth
+    return synth.PRESETS[DELTA.get(config, config)]
 MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def listed_format(dev, e):
+    """Format of a listed expert: e < E the expert itself, E + e its FP4 copy."""
+    return int(dev.formats[e]) if e < dev.n_experts else int(dev.copy_formats[e - dev.n_experts])
 
 
 def expert_stream_bytes(dev, experts):
@@ -63,7 +79,7 @@ def expert_stream_bytes(dev, experts):
     H, I = dev.hidden, dev.inter
     tot = 0
     for e in experts:
-        f = int(dev.formats[e])
+        f = listed_format(dev, e)
         if f == 1:
             tot += 3 * H * I // 4 + 3 * (H * I // 128) * 2
         else:
@@ -75,7 +91,7 @@ def fc1_exact_bytes(dev, experts):
     H, I = dev.hidden, dev.inter
     tot = 0
     for e in experts:
-        f = int(dev.formats[e])
+        f = listed_format(dev, e)
         tot += (2 * I * H // 4 + 2 * (I * H // 128) * 2) if f == 1 else (2 * I * H // 2 + 2 * (I * H // 32))
     return tot
 
@@ -263,11 +279,15 @@ def measure(args, config, with_events=True):
     from bit_vector_quantised_amd import _lib
     from bit_vector_quantised_amd.layer import DeviceLayer, Step
 
-    cfg = synth.PRESETS[config]
+    cfg = preset(config)
     T, k = cfg.n_tokens, cfg.top_k
+    delta = config in DELTA
     print(f"[bench] building {config} layer ({cfg.n_experts} experts)", file=sys.stderr, flush=True)
     syn_dev = synth.SynthLayer(cfg, cache=False)
-    dev = DeviceLayer.from_synth(syn_dev)
+    if delta:  # every expert also stored as MXFP4 in the delta cache
+        dev = DeviceLayer.from_synth(syn_dev, fp4_copies=range(cfg.n_experts), gate_tau=GATE_TAU)
+    else:
+        dev = DeviceLayer.from_synth(syn_dev)
     prefill = config in PREFILL
     n_pool = 256 if T == 1 else (max(8, 256 // T) * T if T <= 256 else 2 * T)
     x_pool_np = synth.SynthLayer(cfg, cache=False).x(n=n_pool, stream=7)
@@ -307,13 +327,16 @@ def measure(args, config, with_events=True):
         raise RuntimeError(f"step status {st} ({_lib.strerror(st)}), expert {info}")
 
     # distinct experts per step (for the algorithmic bytes), read outside the timed region
-    uniq, fc1_bytes, step_bytes = [], [], []
+    uniq, fc1_bytes, step_bytes, gated, copies = [], [], [], [], []
     for i in range(n_batches):
         run_step(i)
         inf = step.info(T)
         uniq.append(inf["n_active"])
         fc1_bytes.append(fc1_exact_bytes(dev, inf["experts"]))
         step_bytes.append(expert_stream_bytes(dev, inf["experts"]))
+        if delta:  # (every expert has a copy: a pair is gated when its weight reaches the gate)
+            gated.append(int((step.w[:T] >= GATE_TAU).sum().item()))
+            copies.append(sum(1 for e in inf["experts"] if e >= cfg.n_experts))
     torch.cuda.synchronize()
 
     # throughput: K steps, nothing but the step on the stream
@@ -330,6 +353,10 @@ def measure(args, config, with_events=True):
     out = {"value": args.steps * T / dt, "unit": "tokens/s", "ms_per_step": dt * 1e3 / args.steps,
            "workload": WORKLOADS[config], "tokens_per_step": T,
            "unique_experts_per_step": float(np.mean([uniq[b] for b in bidx]))}
+    if delta:
+        out["delta"] = {"gate_tau": GATE_TAU, "fp4_copies": cfg.n_experts,
+                        "gated_pairs_per_step": float(np.mean([gated[b] for b in bidx])),
+                        "copies_listed_per_step": float(np.mean([copies[b] for b in bidx]))}
     if not with_events:
         return out, dev, syn_dev, x_pool_np
 
@@ -433,7 +460,7 @@ def main():
     if res is None:  # (the host-RAM tier mode printed its own line)
         return
     main_block, dev, syn_dev, x_pool_np = res
-    cfg = synth.PRESETS[args.config]
+    cfg = preset(args.config)
     out = {
         "metric": "MoE-VQ layer tokens/s and code-stream HBM GB/s (% peak), batch 1 & 32",
         "value": main_block["value"],
@@ -454,10 +481,10 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": main_block["roofline"],
     }
-    for key in ("code_stream", "prefill"):
+    for key in ("code_stream", "prefill", "delta"):
         if key in main_block:
             out[key] = main_block[key]
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.config not in DELTA:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         syn_or = synth.SynthLayer(cfg)
         out["cpu_baseline"] = cpu_baseline(syn_or, x_pool_np, cfg.top_k, args.cpu_budget,

@@ -147,6 +147,23 @@ void route_args(const moe_vq_layer* L, const void* x, int x_dtype, int T, int32_
   wa.grp2 = at<int32_t>(ws, W.grp2);
   wa.pair_list = at<int32_t>(ws, W.pair_list);
   wa.key = key_of(L, T);
+  // the matrix-core FC launches' grids, for the worklist's split of their tiles by cost
+  // (the FC launches compute the same grids; a kernel checks it before using the split)
+  wa.part1 = at<int32_t>(ws, W.part1);
+  wa.part2 = at<int32_t>(ws, W.part2);
+  const int n_cu = device_cu_count();
+  if (W.MT1 == MF_MT && mf_supported(H, true)) {
+    const int rows = mf_tile_rows(H / 1024, true);
+    wa.rb1 = (I + rows - 1) / rows;
+    wa.grid1 = mf_grid(n_cu, W.G1, I, rows);
+  }
+  if (W.MT2 == MF_MT && mf_supported(I, false)) {
+    const int rows = mf_tile_rows(I / 1024, false);
+    wa.rb2 = (H + rows - 1) / rows;
+    wa.grid2 = mf_grid(n_cu, W.G2, H, rows);
+  }
+  if (wa.grid1 > MAX_PART) wa.grid1 = 0;
+  if (wa.grid2 > MAX_PART) wa.grid2 = 0;
 }
 
 // The launches of one call, after its arguments have been checked.
@@ -165,6 +182,7 @@ hipError_t fc1_on(const moe_vq_layer* L, const void* x, int x_dtype, int T, void
   a.x_dtype = x_dtype;
   a.out = h;
   a.max_groups = W.G1;
+  a.part = at<const int32_t>(ws, W.part1);
   return launch_fc1(a, W.MT1, W.G1, device_cu_count(), stream);
 }
 
@@ -177,6 +195,7 @@ hipError_t fc2_on(const moe_vq_layer* L, const float* h, int T, void* ws, float*
   a.y = y;
   a.accumulate = accumulate ? 1 : 0;
   a.max_groups = W.G2;
+  a.part = at<const int32_t>(ws, W.part2);
   return launch_fc2(a, W.MT2, W.G2, device_cu_count(), stream);
 }
 

@@ -78,6 +78,7 @@ struct MfGeom {
   static constexpr int NB_CAP = W == 8 ? (FC1 ? 4 : 8) : 8 / NM;
   static constexpr int NB = NB_RULE < NB_CAP ? NB_RULE : NB_CAP;
   static constexpr int ROWS = 16 * NB;
+  static_assert(ROWS == mf_tile_rows(CPL, FC1), "the worklist's tile split assumes this tile height");
   static constexpr int QS = ROWS + 1;  // LDS stride of one token's partial sums
   static constexpr int RED = W * NM * MF_MT * QS;  // floats per reduction buffer
   static constexpr int NBUF = (size_t)TAB_BYTES + 2 * (size_t)RED * 4 <= (size_t)150 * 1024 ? 2 : 1;
@@ -185,10 +186,15 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   // The kernel arguments span five scalar-cache lines: the activation and output
   // pointers', the MXFP4 offsets' and the grid size's are read here with the header.
   asm volatile("" ::"s"(FC1 ? a.x_h : (const uint16_t*)a.h_in), "s"(a.mx4.s_down), "s"(gridDim.x));
+  // The workgroup's tiles: the worklist's split by cost when it was made for this grid
+  // (read together with the header), else an equal share of the tile count.
+  int pb = 0, pe = 0;
+  if (a.part) { pb = a.part[blockIdx.x]; pe = a.part[blockIdx.x + 1]; }
   if (!ws_ok(a, FC1, MF_MT)) return;
   const int n_tiles = (int)a.hdr[FC1 ? HDR_GROUPS1 : HDR_GROUPS2] * RB;
-  const int t_begin = (int)(((long)blockIdx.x * n_tiles) / gridDim.x);
-  const int t_end = (int)(((long)(blockIdx.x + 1) * n_tiles) / gridDim.x);
+  const bool split = a.part && a.hdr[FC1 ? HDR_PGRID1 : HDR_PGRID2] == gridDim.x;
+  const int t_begin = split ? pb : (int)(((long)blockIdx.x * n_tiles) / gridDim.x);
+  const int t_end = split ? min(pe, n_tiles) : (int)(((long)(blockIdx.x + 1) * n_tiles) / gridDim.x);
   if (t_begin >= t_end) return;
 
   // ---- activations of the current token group, in registers
@@ -776,16 +782,15 @@ hipError_t launch_mfma(const FcArgs& a, int K, int MT, int max_groups, int n_cu,
   if (MT != MF_MT || !mf_supported(K, FC1)) return hipSuccess;
   const int cpl = K / 1024;
   const int nrows = FC1 ? a.I : a.H;
-  const int per_cu = 1;  // a workgroup fills the CU's registers
+  // (one workgroup per CU: a workgroup fills the CU's registers)
 #define MVQ_MFMA_CASE(C)                                                                     \
   if (cpl == C) {                                                                            \
-    constexpr int ROWS = MfGeom<C, FC1>::ROWS;                                               \
-    const long tiles = (long)max_groups * ((nrows + ROWS - 1) / ROWS);                      \
-    long grid = (long)n_cu * per_cu;                                                         \
-    if (tiles < grid) grid = tiles;                                                          \
+    const int grid = mf_grid(n_cu, max_groups, nrows, MfGeom<C, FC1>::ROWS);                 \
     *done = true;                                                                            \
     if (grid <= 0) return hipSuccess;                                                        \
-    launch_fc_kernel(fc_mfma_kernel<C, FC1>, (unsigned)grid, MfGeom<C, FC1>::THREADS, 0, st, a); \
+    FcArgs b = a;                                                                            \
+    if (grid > MAX_PART) b.part = nullptr; /* (the split table's size) */                    \
+    launch_fc_kernel(fc_mfma_kernel<C, FC1>, (unsigned)grid, MfGeom<C, FC1>::THREADS, 0, st, b); \
     return hipGetLastError();                                                                \
   }
   MVQ_MFMA_CASE(1) MVQ_MFMA_CASE(2)

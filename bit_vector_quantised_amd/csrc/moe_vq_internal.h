@@ -45,6 +45,8 @@ enum HdrField {
   HDR_X_LO = 10,      // address of the activations the step was routed with (low, high
   HDR_X_HI = 11,      // word) and their dtype: FC1 and prefill read the staged copy of x
   HDR_X_DTYPE = 12,   // and refuse a call made with other activations
+  HDR_PGRID1 = 13,    // grid the FC1 tile split was made for (0: no split)
+  HDR_PGRID2 = 14,    // the same for FC2
   HDR_WORDS = 64
 };
 
@@ -94,6 +96,33 @@ constexpr int MF_MT = 16;  // token group of the matrix-core FC kernel (its A op
 // whole quarter of K in registers, which caps K at 2048 there).
 __host__ __device__ inline bool mf_supported(int K, bool fc1) {
   return K == 1024 || K == 2048 || (fc1 && K == 7168);
+}
+
+// Rows of one tile of the matrix-core FC kernel at K = 1024 cpl: 16-row blocks, as many
+// as keep several KB of codes in flight per wave within the registers of eight waves
+// (FC1 at most 4, FC2 at most 8; at K = 7168 FC1 takes one block).
+__host__ __device__ constexpr int mf_tile_rows(int cpl, bool fc1) {
+  const int rule = cpl >= 4 ? (fc1 ? 1 : 2) : (fc1 ? 8 / cpl : 16 / cpl);
+  const int cap = fc1 ? 4 : 8;
+  return 16 * (rule < cap ? rule : cap);
+}
+
+// Workgroups of a matrix-core FC launch: one per compute unit, at most one per tile.
+__host__ __device__ inline int mf_grid(int n_cu, int max_groups, int nrows, int rows) {
+  const long tiles = (long)max_groups * ((nrows + rows - 1) / rows);
+  return (int)(tiles < n_cu ? tiles : n_cu);
+}
+
+// The worklist splits the matrix-core FC kernels' tiles over their workgroups by cost
+// rather than by count (table of MAX_PART + 1 tile boundaries per kernel): a tile of an
+// MXFP4 group reads twice the bytes of a VQ2 one and, starting with nothing in flight,
+// takes longer still, so equal tile counts left the workgroups holding MXFP4 tiles
+// running about twice as long as the rest.  The cost ratio 5 : 2 was the fastest of 1.5
+// to 4 for both a mixed-format batch and FP4 delta-cache copies.
+constexpr int MAX_PART = 1024;
+constexpr int PART_COST_VQ2 = 2, PART_COST_MX4 = 5, PART_COST_ABSENT = 1;
+__host__ __device__ inline int part_cost(uint32_t fmt) {
+  return fmt == MOE_VQ_FMT_VQ2 ? PART_COST_VQ2 : (fmt == MOE_VQ_FMT_MXFP4 ? PART_COST_MX4 : PART_COST_ABSENT);
 }
 
 // One token group of one expert, as the FC kernels consume it: a tile is (group, block
@@ -161,7 +190,7 @@ __host__ __device__ inline int pf_max_mtiles(int T, int k, int E) {
 // with an FP4 delta cache, whose copies are listed as experts E + e).
 struct WsLayout {
   size_t hdr, logits, x_h, x_sc, act_expert, act_start, act_off, act_fmt, grp1, grp2, rec1, rec2,
-      pair_list, pair_w, o_buf, x16, x16_e, mt_pre, hmax, h_pre, total;
+      part1, part2, pair_list, pair_w, o_buf, x16, x16_e, mt_pre, hmax, h_pre, total;
   int KS;  // number of activation slices of H
   int MT1, MT2, G1, G2;
 };
@@ -191,6 +220,8 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int T, int EV = 0) {
   L.G2 = fc_max_groups(T, k, EV, L.MT2);
   L.rec1 = take((size_t)L.G1 * sizeof(GroupRec));
   L.rec2 = take((size_t)L.G2 * sizeof(GroupRec));
+  L.part1 = take((size_t)(MAX_PART + 1) * 4);
+  L.part2 = take((size_t)(MAX_PART + 1) * 4);
   L.pair_list = take(P * 4);
   L.pair_w = take(P * 4);
   L.o_buf = take(P * H * 4);
@@ -231,6 +262,10 @@ struct WorklistArgs {
   uint64_t pool_bytes;
   int T, E, k, H, I, MT1, MT2;
   int EV;                          // experts the worklist can list: E, or 2E with copies
+  int32_t* part1;                  // FC1 / FC2 tile split by cost (MAX_PART + 1 entries)
+  int32_t* part2;
+  int grid1, grid2;                // the matrix-core launches' grids (0: no split)
+  int rb1, rb2;                    // their row blocks per token group
   uint32_t* hdr;
   int32_t* act_expert;
   int32_t* act_start;
@@ -268,6 +303,7 @@ struct FcArgs {
   int x_dtype;
   float lim;                 // FC1: SwiGLU clamp (0: none)
   int accumulate;            // FC2: add to y instead of overwriting it
+  const int32_t* part;       // matrix-core kernel: the worklist's tile split, or null
   SlotLayout vq2, mx4;
 };
 

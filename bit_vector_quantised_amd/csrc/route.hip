@@ -178,7 +178,10 @@ constexpr int PL_LDS = 2048;  // pair lists up to this length are also kept in L
 // cache (a.EV = 2E) a pair whose weight passes the confidence gate, and whose expert has
 // a copy, is listed under the copy, expert E + e, whose slot is delta_slots[e]
 // (vLLM-Moet README, "2-bit experts on vLLM v0.24.0": a delta cache and a confidence
-// gate bring FP4 back where it matters).
+// gate bring FP4 back where it matters).  Each copy is listed right after its expert
+// (thread / counter index 2e + 1, the expert itself 2e), so that the FC kernels, which
+// hand each workgroup a contiguous run of tiles in listing order, spread the copies'
+// heavier tiles over the grid instead of giving them all to the last workgroups.
 template <bool FUSED, int NPL>
 __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistArgs a) {
   __shared__ int cnt[16 * MAX_E];
@@ -194,20 +197,26 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   __shared__ int r_start[MAX_E], r_tot[MAX_E], r_gs1[MAX_E], r_gs2[MAX_E], r_expert[MAX_E];
   __shared__ uint32_t r_fmt[MAX_E];
   __shared__ uint64_t r_off[MAX_E];
+  __shared__ int r_wc1[MAX_E], r_wc2[MAX_E];  // tile-cost prefixes (the matrix-core split)
+  __shared__ int4 s_cost;
   // all four scalar-cache lines of the arguments read at the start, together
   asm volatile("" ::"s"(ra.logits), "s"(a.slots), "s"(a.hdr), "s"(a.rec1));
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int E = a.E, EV = a.EV, T = a.T, k = a.k;
+  const bool dc = EV > E;  // delta cache: index 2e is expert e, 2e + 1 its copy
+  const int my_e = dc ? tid >> 1 : tid;
+  const bool my_copy = dc && (tid & 1);
+  const int my_id = my_copy ? E + my_e : my_e;  // the id the worklist reports
   // the slot of (listed) expert tid is read first, so that its latency overlaps the top-k
   moe_vq_slot sl{};
-  if (tid < EV) sl = tid < E ? a.slots[tid] : a.delta_slots[tid - E];
+  if (tid < EV) sl = my_copy ? a.delta_slots[my_e] : a.slots[my_e];
   // counting waves: wave w takes tokens [w*C, (w+1)*C), with as many waves as tokens
   // (up to 16), so that the per-expert totals sum over no more waves than needed
   const int NWC = T < 16 ? (T > 1 ? T : 1) : 16;
   const int C = (T + NWC - 1) / NWC;
   for (int i = tid; i < NWC * EV; i += 1024) cnt[i] = 0;
   if (tid == 0) { s_bad_expert = 0x7FFFFFFF; s_bad_id = 0; }
-  if (EV > E && tid >= E && tid < EV) has_copy[tid - E] = sl.format != MOE_VQ_FMT_ABSENT;
+  if (my_copy && tid < EV) has_copy[my_e] = sl.format != MOE_VQ_FMT_ABSENT;
   if (FUSED) {
     for (int t = wave; t < T; t += 16) {
       int id = 0;
@@ -218,11 +227,13 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   }
   __syncthreads();
   auto id_of = [&](int p) -> int { return FUSED ? ids_lds[p] : a.topk_ids[p]; };
-  // the expert pair p (of expert e) is listed under: the FP4 copy E + e when the cache
-  // holds one and the pair's routing weight reaches the gate
+  // the counter index of the expert pair p (of expert e) is listed under: with the
+  // cache, 2e + 1 (the copy) when the cache holds one and the pair's routing weight
+  // reaches the gate, else 2e
   auto listed = [&](int p, int e) -> int {
-    if (EV == E || !has_copy[e]) return e;
-    return (FUSED ? w_lds[p] : a.pair_w[p]) >= a.tau ? E + e : e;
+    if (!dc) return e;
+    if (!has_copy[e]) return 2 * e;
+    return (FUSED ? w_lds[p] : a.pair_w[p]) >= a.tau ? 2 * e + 1 : 2 * e;
   };
   const int tb = min(T, wave * C), te = min(T, tb + C);
   for (int p = tb * k + lane; p < te * k; p += 64) {
@@ -238,6 +249,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   const int g2 = (tot + a.MT2 - 1) / a.MT2;
   const int4 sc = block_scan_excl4(make_int4(tot, tot > 0 ? 1 : 0, g1, g2), wave_tot, &s_total);
   const int start = sc.x, rank = sc.y, gs1 = sc.z, gs2 = sc.w;
+  uint32_t my_fmt = MOE_VQ_FMT_ABSENT;
   if (tid < EV && tot > 0) {
     uint32_t fmt = sl.format;
     const uint64_t off = sl.byte_offset;
@@ -246,16 +258,17 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
     const bool ok = need != 0 && (off & 255) == 0 && off <= a.pool_bytes && need <= a.pool_bytes - off;
     if (!ok) {
       fmt = MOE_VQ_FMT_ABSENT;
-      atomicMin(&s_bad_expert, tid);
+      atomicMin(&s_bad_expert, my_id);
     }
-    a.act_expert[rank] = tid;
+    a.act_expert[rank] = my_id;
     a.act_start[rank] = start;
     a.act_off[rank] = off;
     a.act_fmt[rank] = fmt;
     a.grp1[rank] = gs1;
     a.grp2[rank] = gs2;
     r_start[rank] = start; r_tot[rank] = tot; r_gs1[rank] = gs1; r_gs2[rank] = gs2;
-    r_expert[rank] = tid; r_fmt[rank] = fmt; r_off[rank] = off;
+    r_expert[rank] = my_id; r_fmt[rank] = fmt; r_off[rank] = off;
+    my_fmt = fmt;
   }
   if (tid == 0) {
     const int n_active = s_total.y;
@@ -318,6 +331,35 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
     for (int j = 0; j < 4; ++j) r.pad[j] = 0;
     (one ? a.rec1 : a.rec2)[g] = r;
   }
+  // The matrix-core FC kernels' tiles split over their grids by cost: boundary b of a
+  // grid of n is the tile where the cost prefix reaches b / n of the total (each listed
+  // expert's tiles cost part_cost(format) apiece, in listing order).
+  {
+    const int wt = (tid < EV && tot > 0) ? part_cost(my_fmt) : 0;
+    const int4 cs = block_scan_excl4(make_int4(g1 * a.rb1 * wt, g2 * a.rb2 * wt, 0, 0), wave_tot, &s_cost);
+    if (tid < EV && tot > 0) { r_wc1[rank] = cs.x; r_wc2[rank] = cs.y; }
+    __syncthreads();
+    auto split = [&](int grid, int rb, const int* wc, const int* gs, int G, int C, int32_t* out) {
+      for (int b = tid; b <= grid; b += 1024) {
+        const long target = (long)b * C / grid;
+        int tile = 0;
+        if (n_act > 0) {
+          int lo = 0, hi = n_act - 1;  // the last listed expert whose prefix is <= target
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (wc[mid] <= target) lo = mid; else hi = mid - 1;
+          }
+          const int w = part_cost(r_fmt[lo]);
+          const int nt = ((lo + 1 < n_act ? gs[lo + 1] : G) - gs[lo]) * rb;
+          const int in = (int)((target - wc[lo] + w - 1) / w);
+          tile = gs[lo] * rb + (in < nt ? in : nt);
+        }
+        out[b] = tile;
+      }
+    };
+    if (a.grid1 > 0) split(a.grid1, a.rb1, r_wc1, r_gs1, G1n, s_cost.x, a.part1);
+    if (a.grid2 > 0) split(a.grid2, a.rb2, r_wc2, r_gs2, G2n, s_cost.y, a.part2);
+  }
   if (tid == 0) {
     uint32_t status = MOE_VQ_OK;
     int info = -1;
@@ -336,6 +378,8 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
     a.hdr[HDR_X_LO] = (uint32_t)(uintptr_t)a.x;
     a.hdr[HDR_X_HI] = (uint32_t)((uint64_t)(uintptr_t)a.x >> 32);
     a.hdr[HDR_X_DTYPE] = (uint32_t)a.x_dtype;
+    a.hdr[HDR_PGRID1] = (uint32_t)a.grid1;
+    a.hdr[HDR_PGRID2] = (uint32_t)a.grid2;
   }
 }
 

@@ -144,9 +144,11 @@ __device__ __forceinline__ OneTokenPick one_token_pick(const RouteArgs& ra, cons
     if (lane < k && w >= a.tau) d = a.delta_slots[id];
     if (d.format != MOE_VQ_FMT_ABSENT) { v = a.E + id; sl = d; }
   }
-  // rank of this lane's listed expert among the k (distinct) ones
+  // rank of this lane's listed expert among the k (distinct) ones, in the many-token
+  // worklist's order: by expert, each copy right after its expert
+  const int order = a.EV > a.E ? 2 * id + (v != id ? 1 : 0) : id;
   int rank = 0;
-  for (int j = 0; j < k; ++j) rank += __shfl(v, j) < v ? 1 : 0;
+  for (int j = 0; j < k; ++j) rank += __shfl(order, j) < order ? 1 : 0;
   uint32_t fmt = sl.format;
   const uint64_t off = sl.byte_offset;
   uint64_t need = 0;
@@ -195,6 +197,8 @@ __device__ __forceinline__ OneTokenPick one_token_pick(const RouteArgs& ra, cons
       a.hdr[HDR_X_LO] = (uint32_t)(uintptr_t)a.x;
       a.hdr[HDR_X_HI] = (uint32_t)((uint64_t)(uintptr_t)a.x >> 32);
       a.hdr[HDR_X_DTYPE] = (uint32_t)a.x_dtype;
+      a.hdr[HDR_PGRID1] = 0;  // (one-token groups: the matrix-core kernels do not run)
+      a.hdr[HDR_PGRID2] = 0;
     }
   }
   return OneTokenPick{v, rank, off, fmt};

@@ -120,8 +120,8 @@ typedef struct moe_vq_layer {
  * and whose expert has a copy is computed from the copy instead of slots[e], on every
  * path (decode and prefill).  Its weight in the combine is unchanged.  With gate_tau >=
  * 0.5 at most one pair of a token passes (its first).  In the workspace, the step's
- * distinct experts (moe_vq_step_info) then count the copies as experts E + e, and a copy
- * whose slot is bad is reported as expert E + e.  NULL (zero-initialised) leaves the cache
+ * distinct experts (moe_vq_step_info) then count the copies as experts E + e, each listed
+ * right after expert e, and a copy whose slot is bad is reported as expert E + e.  NULL (zero-initialised) leaves the cache
  * off.  With delta_slots set, n_experts must be <= 512 and gate_tau finite and >= 0
  * (MOE_VQ_EINVAL otherwise); the host miss path (moe_vq_cpu_experts) does not take such a
  * layer (MOE_VQ_EUNSUPPORTED), and the tier (moe_vq_tier_resolve) manages slots[] only. */
@@ -264,9 +264,9 @@ int moe_vq_check(const void *ws, void *stream, int32_t *info);
 /* Synchronise stream and copy the routing summary of the last step on ws to the host:
  * summary[0] = device status, summary[1] = offending expert or -1, summary[2] = number
  * of distinct selected experts (n_active), summary[3] = routed pairs placed.  If
- * experts is not NULL it receives the n_active distinct expert ids in ascending order
- * (room for n_experts entries; 2 n_experts with an FP4 delta cache, whose copies are
- * listed as E + e).  layer and n_tokens must match the route call. */
+ * experts is not NULL it receives the n_active distinct expert ids in ascending order of
+ * expert (room for n_experts entries; 2 n_experts with an FP4 delta cache, whose copies
+ * are listed as E + e, each right after expert e).  layer and n_tokens must match the route call. */
 int moe_vq_step_info(const moe_vq_layer *layer, int n_tokens, const void *ws, int32_t summary[4],
                      int32_t *experts, void *stream);
 
