@@ -190,6 +190,15 @@ __device__ __forceinline__ half8_t pf_decode(const uint2* tab, const PfCodes& c,
   return b;
 }
 
+// f(integral_constant<int, I>) for I = B .. N - 1, in order.
+template <int B, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < N) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, N>(f);
+  }
+}
+
 template <bool FC1>
 struct PfTile {
   int p_lo, mcnt, nt;
@@ -337,6 +346,54 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
       a_load(g + 2, a_ahead);
     }
     const _Float16* Ab = As[g & 1];
+    if constexpr (FMT == MOE_VQ_FMT_VQ2) {
+      // The group's B fragments j = (S, m, nb) in order.  Fragment j's two table lookups
+      // are issued LA fragments ahead of its products, and step S + 1's A fragments two
+      // fragments before the step starts, so that the LDS round trips run under earlier
+      // fragments' MFMAs (scheduling barriers keep that order).
+      constexpr int NF = NM * NB, J = 4 * NF, LA = 2;
+      uint2 lk[J + LA][2];
+      half8_t af[2][4];
+      auto issue = [&](auto J_) __attribute__((always_inline)) {
+        constexpr int j = decltype(J_)::value;
+        if constexpr (j < J) {
+          constexpr int S = j / NF, m = (j % NF) / NB, nb = j % NB;
+          const uint32_t wd = S < 2 ? cur[m][nb].q.x : cur[m][nb].q.y;
+          lk[j][0] = tab_lookup(tab, tab_addr<(2 * S) & 3>(wd, laneoff) >> 1);
+          lk[j][1] = tab_lookup(tab, tab_addr<(2 * S + 1) & 3>(wd, laneoff) >> 1);
+        }
+      };
+      auto a_frag = [&](auto S_) __attribute__((always_inline)) {
+        constexpr int S = decltype(S_)::value;
+        if constexpr (S < 4) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            af[S & 1][mb] = *reinterpret_cast<const half8_t*>(&Ab[(mb * 16 + i16) * PF_AROW + 32 * kq + 8 * S]);
+        }
+      };
+      a_frag(std::integral_constant<int, 0>{});
+      static_for<0, LA>(issue);
+      static_for<0, J>([&](auto J_) __attribute__((always_inline)) {
+        constexpr int j = decltype(J_)::value;
+        constexpr int S = j / NF, f = j % NF, m = f / NB, nb = f % NB;
+        issue(std::integral_constant<int, j + LA>{});
+        if constexpr (f == (NF > 2 ? NF - 2 : 0)) a_frag(std::integral_constant<int, S + 1>{});
+        const half2_t sc = __builtin_bit_cast(half2_t, (cur[m][nb].s & 0xFFFFu) * 0x10001u);
+        const uint2 e0 = lk[j][0], e1 = lk[j][1];
+        const half2_t p0 = __builtin_bit_cast(half2_t, e0.x) * sc, p1 = __builtin_bit_cast(half2_t, e0.y) * sc;
+        const half2_t p2 = __builtin_bit_cast(half2_t, e1.x) * sc, p3 = __builtin_bit_cast(half2_t, e1.y) * sc;
+        half8_t bf;
+        bf[0] = p0[0]; bf[1] = p0[1]; bf[2] = p1[0]; bf[3] = p1[1];
+        bf[4] = p2[0]; bf[5] = p2[1]; bf[6] = p3[0]; bf[7] = p3[1];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[S & 1][mb], bf, acc[m][nb][mb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if (g + 1 < NG) a_store((g + 1) & 1, a_next);
+      __syncthreads();
+      return;
+    }
     auto step = [&](auto S_) __attribute__((always_inline)) {
       constexpr int S = decltype(S_)::value;
       half8_t af[4];
