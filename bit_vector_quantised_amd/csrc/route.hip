@@ -333,15 +333,23 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
   }
   // The matrix-core FC kernels' tiles split over their grids by cost: boundary b of a
   // grid of n is the tile where the cost prefix reaches b / n of the total (each listed
-  // expert's tiles cost part_cost(format) apiece, in listing order).
-  {
-    const int wt = (tid < EV && tot > 0) ? part_cost(my_fmt) : 0;
+  // expert's tiles cost part_cost(format) apiece, in listing order).  Only a step that
+  // lists both formats needs it: with one format equal costs are equal counts, which the
+  // kernels take by themselves when the header records no split.
+  const bool listed_here = tid < EV && tot > 0;
+  const bool mixed = __syncthreads_or(listed_here && my_fmt == MOE_VQ_FMT_MXFP4) &&
+                     __syncthreads_or(listed_here && my_fmt == MOE_VQ_FMT_VQ2);
+  const int pgrid1 = mixed ? a.grid1 : 0, pgrid2 = mixed ? a.grid2 : 0;
+  if (mixed && (pgrid1 > 0 || pgrid2 > 0)) {
+    const int wt = listed_here ? part_cost(my_fmt) : 0;
     const int4 cs = block_scan_excl4(make_int4(g1 * a.rb1 * wt, g2 * a.rb2 * wt, 0, 0), wave_tot, &s_cost);
     if (tid < EV && tot > 0) { r_wc1[rank] = cs.x; r_wc2[rank] = cs.y; }
     __syncthreads();
     auto split = [&](int grid, int rb, const int* wc, const int* gs, int G, int C, int32_t* out) {
       for (int b = tid; b <= grid; b += 1024) {
-        const long target = (long)b * C / grid;
+        // floor(b C / grid): exact in double (b C < 2^53, and a quotient that is not an
+        // integer lies at least 1 / grid from one)
+        const int target = (int)floor((double)b * (double)C / (double)grid);
         int tile = 0;
         if (n_act > 0) {
           int lo = 0, hi = n_act - 1;  // the last listed expert whose prefix is <= target
@@ -351,14 +359,14 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
           }
           const int w = part_cost(r_fmt[lo]);
           const int nt = ((lo + 1 < n_act ? gs[lo + 1] : G) - gs[lo]) * rb;
-          const int in = (int)((target - wc[lo] + w - 1) / w);
+          const int in = (target - wc[lo] + w - 1) / w;
           tile = gs[lo] * rb + (in < nt ? in : nt);
         }
         out[b] = tile;
       }
     };
-    if (a.grid1 > 0) split(a.grid1, a.rb1, r_wc1, r_gs1, G1n, s_cost.x, a.part1);
-    if (a.grid2 > 0) split(a.grid2, a.rb2, r_wc2, r_gs2, G2n, s_cost.y, a.part2);
+    if (pgrid1 > 0) split(pgrid1, a.rb1, r_wc1, r_gs1, G1n, s_cost.x, a.part1);
+    if (pgrid2 > 0) split(pgrid2, a.rb2, r_wc2, r_gs2, G2n, s_cost.y, a.part2);
   }
   if (tid == 0) {
     uint32_t status = MOE_VQ_OK;
@@ -378,8 +386,8 @@ __global__ __launch_bounds__(1024) void worklist_kernel(RouteArgs ra, WorklistAr
     a.hdr[HDR_X_LO] = (uint32_t)(uintptr_t)a.x;
     a.hdr[HDR_X_HI] = (uint32_t)((uint64_t)(uintptr_t)a.x >> 32);
     a.hdr[HDR_X_DTYPE] = (uint32_t)a.x_dtype;
-    a.hdr[HDR_PGRID1] = (uint32_t)a.grid1;
-    a.hdr[HDR_PGRID2] = (uint32_t)a.grid2;
+    a.hdr[HDR_PGRID1] = (uint32_t)pgrid1;
+    a.hdr[HDR_PGRID2] = (uint32_t)pgrid2;
   }
 }
 
