@@ -204,7 +204,7 @@ int moe_vq_forward(const moe_vq_layer *layer, const void *x, int x_dtype, int n_
  * serialised by the caller.  Nothing in the array needs clearing between calls (every
  * word a step reads is written earlier in the same step).  Errors: as moe_vq_forward, and
  * MOE_VQ_ENOSPACE when the step's workspace (moe_vq_workspace_bytes for n_tokens) exceeds
- * 16 MiB, about 56 tokens at H = 7168, I = 2048, 256 experts, top-8. */
+ * 16 MiB: 55 tokens at H = 7168, I = 2048, 256 experts, top-8. */
 int moe_vq_forward_static(const moe_vq_layer *layer, const void *x, int x_dtype, int n_tokens,
                           int32_t *topk_ids, float *topk_w, float *h, float *y, int32_t *status,
                           void *stream);

@@ -269,3 +269,10 @@ def test_delta_cache_arguments():
     HS = (_lib.Slot * 128)()
     assert raw.moe_vq_cpu_experts(P(D), HP, 1 << 20, HS, CB, X, _lib.F32, 4, IDS, W, CMP, Y, 1) \
         == _lib.EUNSUPPORTED
+
+
+def test_static_workspace_capacity_matches_its_documentation():
+    """moe_vq_forward_static's 16 MiB array holds the workspace of 55 tokens at the full
+    shape (H = 7168, I = 2048, 256 experts, top-8), as include/moe_vq.h states."""
+    full = _lib.Layer(7168, 2048, 256, 8, 0x10000, 0x20000, 0x100000, 1 << 30, 0x30000)
+    assert _lib.workspace_bytes(full, 55) <= 16 << 20 < _lib.workspace_bytes(full, 56)
