@@ -1,4 +1,4 @@
-"""The CPU miss path on the GPU machine: a tiered layer whose device slots hold some of the
+"""The CPU miss path on the GPU: a tiered layer whose device slots hold some of the
 experts; each step's other selected experts are computed on the host cores from the host
 pool while the GPU runs the resident ones, and y is their sum.  Every step is compared with
 the fp64 oracle (the parity rules) and with the layer whose experts are all resident."""
