@@ -449,15 +449,23 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a
   if (jx >= per) return;
   const int L = (blockIdx.x & 7) * per + jx;
   if (L >= n_valid) return;
-  const int mt = L / NT;
-  // active expert of this token tile: the last rank whose tile prefix is <= mt
+  // active expert of this logical tile: the last rank whose tiles start at or before it
+  // (an expert's tiles are the logical tiles mt_pre[e] * NT .. mt_pre[e + 1] * NT - 1)
   int lo = 0, hi = n_act - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.mt_pre[mid] <= mt) lo = mid; else hi = mid - 1;
+  {
+    const int mtl = L / NT;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.mt_pre[mid] <= mtl) lo = mid; else hi = mid - 1;
+    }
   }
+  // within the expert, row tile major: its token tiles that share one row tile's codes
+  // run next to each other
+  const int ce = a.mt_pre[lo + 1] - a.mt_pre[lo];
+  const int li = L - a.mt_pre[lo] * NT;
+  const int mt = a.mt_pre[lo] + li % ce;
   PfTile<FC1> tl;
-  tl.nt = L % NT;
+  tl.nt = li / ce;
   tl.p_lo = a.act_start[lo] + (mt - a.mt_pre[lo]) * PF_BM;
   tl.mcnt = min(PF_BM, a.act_start[lo + 1] - tl.p_lo);
   tl.fmt = a.act_fmt[lo];
