@@ -501,19 +501,14 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
   auto compute_vq = [&](bool refill, const RecS& rn, int rbn, const RecS& rcur, int rbc)
                         __attribute__((always_inline)) {
     const MfAddr dn = refill ? vq_addr(rn, rbn) : vq_addr(rcur, rbc);
-    if (FC1 && MF_WAVES > 4) {
-      // two waves per SIMD interleave by themselves: no registers for a pipeline
+    // (FC1 at K = 7168 has the 17 registers this takes: B32 FC1 201.7 -> 199.1 us)
+    UDec cur = decode(0, dn);
 #pragma unroll
-      for (int u = 0; u < NU; ++u) unit_mma(u, decode(u, dn));
-    } else {
-      UDec cur = decode(0, dn);
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        UDec nxt;
-        if (u + 1 < NU) nxt = decode(u + 1, dn);
-        unit_mma(u, cur);
-        if (u + 1 < NU) cur = nxt;
-      }
+    for (int u = 0; u < NU; ++u) {
+      UDec nxt;
+      if (u + 1 < NU) nxt = decode(u + 1, dn);
+      unit_mma(u, cur);
+      if (u + 1 < NU) cur = nxt;
     }
   };
 
