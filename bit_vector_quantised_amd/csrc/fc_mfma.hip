@@ -514,12 +514,12 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 
   // MXFP4 tile (not in the ring): the groups of the wave's part of K load in passes of up
   // to MXG groups.  Each lane reads the 32 weights of its k-part p(q) of a group.
+  // e: the four E8M0 bytes of this row's group (one dword); the lane's block is byte pq
   auto mx_unit = [&](int gi, const uint4& q, uint32_t e, int m, int nb) __attribute__((always_inline)) {
-    // e_max over the four blocks of this row's group (lanes i16, i16 + 16, + 32, + 48)
-    int em = (int)(e & 0xFFu);
-    em = max(em, __shfl_xor(em, 16));
-    em = max(em, __shfl_xor(em, 32));
-    const float es = ldexp2(1.0f, (int)(e & 0xFFu) - em);  // 2^(e - e_max), in (0, 1]
+    // e_max over the four blocks of this row's group, which the lanes i16, i16 + 16, + 32
+    // and + 48 hold: all four bytes are in every lane's dword
+    const int em = (int)max(max(e & 0xFFu, (e >> 8) & 0xFFu), max((e >> 16) & 0xFFu, e >> 24));
+    const float es = ldexp2(1.0f, (int)((e >> (8 * pq)) & 0xFFu) - em);  // 2^(e - e_max), in (0, 1]
     half8_t bfr[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -554,7 +554,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
             for (int nb = 0; nb < NB; ++nb) {
               const uint32_t g = (uint32_t)gid(gi);
               mx[b][j][m][nb].q = *reinterpret_cast<const uint4*>(d.qb[m] + (uint32_t)(d.qo[nb] - d.dq0 + g * 64));
-              mx[b][j][m][nb].e = d.sb[m][(uint32_t)(d.so[nb] - d.ds0 + g * 4 + pq)];
+              mx[b][j][m][nb].e = *reinterpret_cast<const uint32_t*>(d.sb[m] + (uint32_t)(d.so[nb] - d.ds0 + g * 4));
             }
       }
     };
