@@ -28,6 +28,10 @@ its algorithmic code+scale bytes per launch over the mean duration those events 
 without the dispatch that events recorded on the stream around the launch would add.
 Prefill is timed by events on the stream around the whole call.
 
+`read_probe` is the rate of a plain streaming read of 1 GiB on the same device
+(moe_vq_read_probe, timed like the FC kernels); `code_stream.frac_of_read_probe` sets
+the code stream against it, beside the fraction of the published 8 TB/s.
+
 `roofline.traffic` is the FC1 kernel's HBM traffic per launch as the hardware
 counters saw it: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc
 run each) scaled by what the same counters read for a plain device copy of known
@@ -266,6 +270,31 @@ def bench_tier(args, cfg, syn, x_pool, n_batches):
 
 
 SCRUB_BYTES = 512 << 20
+READ_PROBE_BYTES = 1 << 30
+
+
+def read_peak(reps=10):
+    """The HBM read rate of a plain streaming read (moe_vq_read_probe) of 1 GiB, four
+    times the memory-side cache: median over reps runs, each timed by events its own
+    launch records.  GB/s."""
+    import torch
+    from bit_vector_quantised_amd import _lib
+    buf = torch.zeros(READ_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:  # (a torch event holds a HIP event only once it has been recorded)
+        a.record(stream)
+        b.record(stream)
+    for _ in range(3):
+        _lib.read_probe(buf.data_ptr(), READ_PROBE_BYTES, sink.data_ptr(), stream.cuda_stream)
+    for a, b in evs:
+        _lib.time_next_kernel(a.cuda_event, b.cuda_event)
+        _lib.read_probe(buf.data_ptr(), READ_PROBE_BYTES, sink.data_ptr(), stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    del buf
+    return READ_PROBE_BYTES / (ms[len(ms) // 2] * 1e-3) / 1e9
 
 
 def measure(args, config, with_events=True):
@@ -456,6 +485,7 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    peak_read = read_peak() if not args.tier_slots and args.config not in PREFILL else None
     res = measure(args, args.config)
     if res is None:  # (the host-RAM tier mode printed its own line)
         return
@@ -484,6 +514,11 @@ def main():
     for key in ("code_stream", "prefill", "delta"):
         if key in main_block:
             out[key] = main_block[key]
+    if peak_read:
+        # the code stream against a plain read of the same device (beside the published peak)
+        out["read_probe"] = {"GBps": peak_read, "bytes": READ_PROBE_BYTES, "kernel": "moe_vq_read_probe",
+                             "frac_of_peak": peak_read / HBM_PEAK_GBPS}
+        out["code_stream"]["frac_of_read_probe"] = out["code_stream"]["GBps"] / peak_read
     if not args.no_cpu_baseline and args.config not in DELTA:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         syn_or = synth.SynthLayer(cfg)
@@ -498,6 +533,8 @@ def main():
         b32, dev32, _, _ = measure(args, "b32")
         out["b32"] = {k: b32[k] for k in ("value", "unit", "ms_per_step", "workload", "tokens_per_step",
                                            "unique_experts_per_step", "roofline", "code_stream")}
+        if peak_read:
+            out["b32"]["code_stream"]["frac_of_read_probe"] = b32["code_stream"]["GBps"] / peak_read
         del dev32
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)

@@ -21,7 +21,7 @@ MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 EXPORTS = ("moe_vq_expert_bytes", "moe_vq_slot_layout", "moe_vq_workspace_bytes", "moe_vq_route_topk",
            "moe_vq_fc1_silu", "moe_vq_fc2_combine", "moe_vq_forward", "moe_vq_forward_static", "moe_vq_shared_expert", "moe_vq_prefill_gemm", "moe_vq_decode_expert",
            "moe_vq_check", "moe_vq_step_info", "moe_vq_tier_init", "moe_vq_tier_plan", "moe_vq_tier_resolve", "moe_vq_cpu_experts",
-           "moe_vq_time_next_kernel", "moe_vq_last_hip_error", "moe_vq_strerror")
+           "moe_vq_time_next_kernel", "moe_vq_read_probe", "moe_vq_last_hip_error", "moe_vq_strerror")
 
 
 class MoeVqError(RuntimeError):
@@ -86,6 +86,7 @@ def _load():
         "moe_vq_cpu_experts": (i32, [LP, vp, ctypes.c_uint64, ctypes.POINTER(Slot), vp, vp, i32, i32, vp, vp, vp,
                                      vp, i32]),
         "moe_vq_time_next_kernel": (i32, [vp, vp]),
+        "moe_vq_read_probe": (i32, [vp, sz, vp, vp]),
         "moe_vq_last_hip_error": (ctypes.c_char_p, []),
         "moe_vq_strerror": (ctypes.c_char_p, [i32]),
     }
@@ -108,6 +109,11 @@ def time_next_kernel(start_event: int, stop_event: int) -> None:
     """The next FC kernel launched from this thread records the two events (raw hipEvent_t
     handles, e.g. torch.cuda.Event(enable_timing=True).cuda_event) at its start and end."""
     _ok(_lib.moe_vq_time_next_kernel(start_event or None, stop_event or None), "time_next_kernel")
+
+
+def read_probe(buf: int, nbytes: int, sink: int, stream: int = 0) -> None:
+    """Enqueue a plain streaming read of nbytes at buf (a measurement of the read rate)."""
+    _ok(_lib.moe_vq_read_probe(buf, nbytes, sink, stream), "read_probe")
 
 
 def last_hip_error() -> str:

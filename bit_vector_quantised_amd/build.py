@@ -27,7 +27,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_vq.so")
-SOURCES = ["api.hip", "route.hip", "fc.hip", "fc_mfma.hip", "fc2_single.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "route.hip", "fc.hip", "fc_mfma.hip", "fc2_single.hip", "decode.hip", "prefill.hip",
+           "probe.hip"]
 CPP_SOURCES = ["cpu_experts.cpp"]  # host code (the expert path on the host cores), built with g++
 ARCH = "gfx950"
 

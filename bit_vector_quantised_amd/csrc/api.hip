@@ -595,6 +595,12 @@ int moe_vq_tier_resolve(const moe_vq_layer* L, moe_vq_tier* tier, uint8_t* pool,
   return hip_status(hipStreamSynchronize(st));
 }
 
+int moe_vq_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || ((uintptr_t)buf & 15) || ((uintptr_t)sink & 3) || bytes < 16 || (bytes & 15))
+    return MOE_VQ_EINVAL;
+  return hip_status(launch_read_probe(buf, bytes, sink, device_cu_count(), static_cast<hipStream_t>(stream)));
+}
+
 int moe_vq_time_next_kernel(void* start_event, void* stop_event) {
   kernel_timing() = KernelTiming{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
   return MOE_VQ_OK;

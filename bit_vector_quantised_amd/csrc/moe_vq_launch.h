@@ -50,6 +50,10 @@ void launch_combine(const float* o_buf, float* y, int T, int H, int k, int accum
 // Prefill: stage x, token tiles, FC1 and FC2 as grouped MFMA GEMMs, combine.
 hipError_t launch_prefill(const PrefillArgs& a, int x_dtype, hipStream_t st);
 
+// Streaming read of bytes (a multiple of 16) at buf; sink[0] is written only in a case
+// that does not occur in practice.
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int n_cu, hipStream_t st);
+
 hipError_t launch_decode_expert(const uint8_t* pool, const moe_vq_slot* slots, uint64_t pool_bytes,
                                 const uint16_t* codebook, int H, int I, int expert, int matrix,
                                 int out_dtype, void* out, int32_t* status_dev, hipStream_t st);

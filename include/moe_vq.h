@@ -273,14 +273,23 @@ int moe_vq_step_info(const moe_vq_layer *layer, int n_tokens, const void *ws, in
 /* Measurement hook for benchmarks (timing the kernels against the pages' throughput
  * figures; Tandem-vLLM 0.2.0 announcement, "Speed").  The next decode FC kernel that a
  * call made on this thread launches -- FC1's in moe_vq_fc1_silu, moe_vq_forward and
- * moe_vq_forward_static, FC2's in moe_vq_fc2_combine; not the combine kernel and not
- * prefill -- is launched with hipExtLaunchKernel so that start_event records the
+ * moe_vq_forward_static, FC2's in moe_vq_fc2_combine, the read of moe_vq_read_probe; not
+ * the combine kernel and not prefill -- is launched with hipExtLaunchKernel so that start_event records the
  * kernel's start and stop_event its end (hipEvent_t, created with timing; either may be
  * NULL).  hipEventElapsedTime of the two is then the kernel's own run time, without the
  * dispatch that an event recorded on the stream before the launch also counts.  The
  * hook is per thread, used by one launch, and stays set until a launch uses it; NULL,
  * NULL clears it.  Returns MOE_VQ_OK. */
 int moe_vq_time_next_kernel(void *start_event, void *stop_event);
+
+/* Measurement hook: a plain streaming read of bytes (a multiple of 16, >= 16) at buf
+ * (16-byte aligned) with 16-byte loads over every compute unit, enqueued on stream, so
+ * that the rate the decode kernels reach can be set against what a read alone reaches on
+ * the same device (the pages measure their kernels against the hardware's limits; vLLM-Moet
+ * README, "What we changed against official vLLM").  sink (device, 4-byte aligned) is
+ * written only in a case that does not occur in practice.  Errors: MOE_VQ_EINVAL for bad
+ * arguments (before any HIP call), MOE_VQ_EHIP if the launch fails. */
+int moe_vq_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 /* ---- Host-RAM expert tier.  Experts can live in a pinned host pool, with the device
  * pool holding only some of them: a GPU cache of the experts in use in front of the rest

@@ -276,3 +276,14 @@ def test_static_workspace_capacity_matches_its_documentation():
     shape (H = 7168, I = 2048, 256 experts, top-8), as include/moe_vq.h states."""
     full = _lib.Layer(7168, 2048, 256, 8, 0x10000, 0x20000, 0x100000, 1 << 30, 0x30000)
     assert _lib.workspace_bytes(full, 55) <= 16 << 20 < _lib.workspace_bytes(full, 56)
+
+
+def test_read_probe_rejects_bad_arguments():
+    raw = _lib.raw()
+    BUF, SINK = 0x100000, 0x200000
+    assert raw.moe_vq_read_probe(None, 1 << 20, SINK, None) == _lib.EINVAL
+    assert raw.moe_vq_read_probe(BUF, 1 << 20, None, None) == _lib.EINVAL
+    assert raw.moe_vq_read_probe(BUF + 8, 1 << 20, SINK, None) == _lib.EINVAL
+    assert raw.moe_vq_read_probe(BUF, (1 << 20) + 8, SINK, None) == _lib.EINVAL
+    assert raw.moe_vq_read_probe(BUF, 0, SINK, None) == _lib.EINVAL
+    assert raw.moe_vq_read_probe(BUF, 1 << 20, SINK + 2, None) == _lib.EINVAL

@@ -53,3 +53,23 @@ def test_timed_launch_matches_plain_launch(T):
     torch.cuda.synchronize()
     assert ev[0].elapsed_time(ev[1]) == fc1_ms and ev[2].elapsed_time(ev[3]) == fc2_ms
     _lib.time_next_kernel(0, 0)
+
+
+def test_read_probe_runs_and_is_timed_by_the_hook():
+    """The streaming read probe reads a buffer (its sink stays untouched for zero data) and
+    its launch records the hook's events; 64 MiB take well under a millisecond."""
+    say("read probe")
+    buf = torch.zeros(16 << 20, dtype=torch.int32, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    _lib.time_next_kernel(a.cuda_event, b.cuda_event)
+    _lib.read_probe(buf.data_ptr(), buf.numel() * 4, sink.data_ptr(), stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    assert 0 < ms < 1.0, ms
+    assert int(sink.item()) == 7
+    say("read probe GB/s", buf.numel() * 4 / (ms * 1e-3) / 1e9)
