@@ -499,13 +499,16 @@ __global__ __launch_bounds__(64) void stage_x_kernel(RouteArgs a) {
 }
 
 // Fewer tokens than the matrix-core router takes (bf16 x): the product split over K as the
-// GEMV router splits it, on the matrix cores.  Workgroup (expert block of 16, slice of
-// 1024 columns); wave w takes 256 columns of the slice for every token block of 16.  Its
+// GEMV router splits it, on the matrix cores.  Workgroup (expert block of RS_EXPERTS,
+// slice of 1024 columns); wave w takes 256 columns of the slice for every token block of
+// 16.  Eight experts per workgroup rather than the matrix op's 16 columns: twice the
+// workgroups (224 for 256 experts and H = 7168), each reading half the weights, so that
+// more compute units share the router's read.  Its
 // loads (weights and x) are all issued before the first matrix op, so a workgroup waits
 // for one memory latency.  The four waves' sums meet in LDS in a fixed order, and the
 // slice's partial logit goes where the GEMV router puts it ([T][E][ksp]).  The workgroups
 // of a slice also stage its x as fp16 for the FC kernels.
-constexpr int RS_EXPERTS = 16;
+constexpr int RS_EXPERTS = 8;  // experts per workgroup: the matrix op's other 8 columns are zeros
 constexpr int RS_MAX_T = 64;  // token blocks of 16, at most four
 
 __global__ __launch_bounds__(256) void router_mfma_small_kernel(RouteArgs a) {
@@ -518,13 +521,14 @@ __global__ __launch_bounds__(256) void router_mfma_small_kernel(RouteArgs a) {
   const int T = a.T, H = a.H, MB = (T + 15) / 16;
   const int c0 = s * SLICE + wave * 256 + 8 * kq;  // + 32 j: 8 columns, all in or all out (H % 128 == 0)
   const uint16_t* xb = static_cast<const uint16_t*>(a.x);
-  const uint16_t* wr = a.router_w + (size_t)min(e0 + i16, a.E - 1) * H;
+  const bool col_ok = i16 < RS_EXPERTS;  // matrix-op columns past the workgroup's experts stay zero
+  const uint16_t* wr = a.router_w + (size_t)min(e0 + (col_ok ? i16 : 0), a.E - 1) * H;
   const bf16x8_t zero = bf16x8_t{};
   bf16x8_t bfr[8], afr[RS_MAX_T / 16][8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int c = c0 + 32 * j;
-    bfr[j] = c < H ? *reinterpret_cast<const bf16x8_t*>(wr + c) : zero;
+    bfr[j] = (col_ok && c < H) ? *reinterpret_cast<const bf16x8_t*>(wr + c) : zero;
   }
 #pragma unroll
   for (int mb = 0; mb < RS_MAX_T / 16; ++mb) {
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(256) void router_mfma_small_kernel(RouteArgs a) {
   for (int o = tid; o < MB * 256; o += 256) {
     const int mb = o >> 8, row = (o >> 4) & 15, col = o & 15;
     const int t = mb * 16 + row, e = e0 + col;
-    if (t < T && e < a.E) {
+    if (t < T && col < RS_EXPERTS && e < a.E) {
       const float v = ((red[0][mb][row][col] + red[1][mb][row][col]) + red[2][mb][row][col]) + red[3][mb][row][col];
       float* dst = a.logits + ((size_t)t * a.E + e) * KSP;
       dst[s] = v;
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(256) void router_mfma_small_kernel(RouteArgs a) {
     }
   }
   // the slice's staging, spread over the workgroups of the slice: at most one token per
-  // wave up to 4 * E / 16 tokens (each token is a memory round trip)
+  // wave up to 4 * E / RS_EXPERTS tokens (each token is a memory round trip)
   for (int t = blockIdx.x * 4 + wave; t < T; t += gridDim.x * 4) stage_x_row<false>(a, t, s, lane);
 }
 
