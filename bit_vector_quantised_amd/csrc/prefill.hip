@@ -207,8 +207,11 @@ struct PfTile {
 };
 
 // Main loop of one tile for one weight format.  rowf receives the factor of each of the
-// lane's output rows (MXFP4: 2^(e_row - 127); VQ2: 1).
-template <bool FC1, int FMT>
+// lane's output rows (MXFP4: 2^(e_row - 127); VQ2: 1).  NMB: the 16-token blocks of the
+// tile that hold tokens; the rest are neither staged, read nor multiplied (an expert's
+// last tile often holds a few tokens: with about 130 tokens per expert, tiles of 64, 64
+// and 2).
+template <bool FC1, int FMT, int NMB>
 __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>& tl, const uint2* tab,
                                         _Float16 (*As)[PF_BM * PF_AROW], f32x4_t (&acc)[PfGeom<FC1>::NM][PfGeom<FC1>::NB][4],
                                         const int* s_pair, const float* s_fac,
@@ -286,6 +289,7 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
   // the bf16 h that FC1 wrote, scaled by the pair's power-of-two factor into fp16)
   const int srow = tid >> 2, skq = (tid & 3) * 32;
   const int sp = s_pair[srow];  // -1 past the tile's tokens
+  const bool stage = srow < NMB * 16;  // (one wave stages 16 rows: uniform per wave)
   constexpr int AV = 4;         // 16-byte loads per thread per group
   auto a_load = [&](int g, uint4 (&v)[AV]) __attribute__((always_inline)) {
 #pragma unroll
@@ -298,6 +302,7 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
     }
   };
   auto a_store = [&](int buf, const uint4 (&v)[AV]) __attribute__((always_inline)) {
+    if (!stage) return;
     uint4* dst = reinterpret_cast<uint4*>(&As[buf][srow * PF_AROW + skq]);
     if (FC1) {
 #pragma unroll
@@ -367,7 +372,7 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
         constexpr int S = decltype(S_)::value;
         if constexpr (S < 4) {
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
+          for (int mb = 0; mb < NMB; ++mb)
             af[S & 1][mb] = *reinterpret_cast<const half8_t*>(&Ab[(mb * 16 + i16) * PF_AROW + 32 * kq + 8 * S]);
         }
       };
@@ -386,7 +391,7 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
         bf[0] = p0[0]; bf[1] = p0[1]; bf[2] = p1[0]; bf[3] = p1[1];
         bf[4] = p2[0]; bf[5] = p2[1]; bf[6] = p3[0]; bf[7] = p3[1];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < NMB; ++mb)
           acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[S & 1][mb], bf, acc[m][nb][mb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -396,9 +401,9 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
     }
     auto step = [&](auto S_) __attribute__((always_inline)) {
       constexpr int S = decltype(S_)::value;
-      half8_t af[4];
+      half8_t af[NMB];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < NMB; ++mb)
         af[mb] = *reinterpret_cast<const half8_t*>(&Ab[(mb * 16 + i16) * PF_AROW + 32 * kq + 8 * S]);
 #pragma unroll
       for (int m = 0; m < NM; ++m)
@@ -406,7 +411,7 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
         for (int nb = 0; nb < NB; ++nb) {
           const half8_t bf = pf_decode<FMT, S>(tab, cur[m][nb], laneoff, erow[m][nb]);
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
+          for (int mb = 0; mb < NMB; ++mb)
             acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf, acc[m][nb][mb], 0, 0, 0);
         }
     };
@@ -503,9 +508,18 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_fc_kernel(PrefillArgs a
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[m][nb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-  if (tl.fmt == MOE_VQ_FMT_VQ2) pf_tile<FC1, MOE_VQ_FMT_VQ2>(a, tl, tab, As, acc, s_pair, s_fac, rowf);
-  else if (tl.fmt == MOE_VQ_FMT_MXFP4) pf_tile<FC1, MOE_VQ_FMT_MXFP4>(a, tl, tab, As, acc, s_pair, s_fac, rowf);
   // (an absent expert keeps zeros; the worklist has set MOE_VQ_ENOTRESIDENT)
+  auto run = [&](auto NMB_) __attribute__((always_inline)) {
+    constexpr int NMB = decltype(NMB_)::value;
+    if (tl.fmt == MOE_VQ_FMT_VQ2) pf_tile<FC1, MOE_VQ_FMT_VQ2, NMB>(a, tl, tab, As, acc, s_pair, s_fac, rowf);
+    else if (tl.fmt == MOE_VQ_FMT_MXFP4) pf_tile<FC1, MOE_VQ_FMT_MXFP4, NMB>(a, tl, tab, As, acc, s_pair, s_fac, rowf);
+  };
+  switch ((tl.mcnt + 15) >> 4) {  // (a tile holds 1 .. PF_BM tokens)
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    default: run(std::integral_constant<int, 4>{}); break;
+  }
 
   // epilogue: D lane holds column i16 (output row) and token rows 4*kq + 0..3 of each block
 #pragma unroll

@@ -90,6 +90,28 @@ def test_prefill_mixed_formats(mini):
     compare(v, x, "bf16", g, MINI.top_k, check_h=False)
 
 
+def test_prefill_partly_filled_token_tiles(mini):
+    # A tile holds up to 64 tokens of one expert; the kernels multiply only its 16-token
+    # blocks that hold tokens.  Token counts chosen so that tiles with 1, 2, 3 and 4 such
+    # blocks occur for VQ2 and MXFP4 experts, every token compared with the oracle.
+    syn, _ = mini
+    fm = [synth.FMT_MXFP4 if e % 3 == 0 else synth.FMT_VQ2 for e in range(MINI.n_experts)]
+    v, dev = tiny_variant(syn, formats=fm)
+    seen = set()
+    for T in (40, 100, 170, 300):
+        x = syn.x(n=T, stream=110 + T)
+        say(f"prefill mini mixed T={T}")
+        g = run_prefill(dev, x, "bf16")
+        assert g["status"] == _lib.OK
+        compare(v, x, "bf16", g, MINI.top_k, check_h=False)
+        counts = np.bincount(g["ids"].reshape(-1), minlength=MINI.n_experts)
+        for e, c in enumerate(counts):
+            sizes = [64] * (int(c) // 64) + ([int(c) % 64] if c % 64 else [])
+            seen |= {(fm[e], -(-n // 16)) for n in sizes}
+    for f in (synth.FMT_VQ2, synth.FMT_MXFP4):
+        assert {b for (ff, b) in seen if ff == f} == {1, 2, 3, 4}
+
+
 def test_prefill_ragged_row_tiles(odd):
     # H=384: the FC2 tile of 256 rows is ragged; K=384 / 640 are not multiples of 1024
     syn, dev = odd
