@@ -503,13 +503,13 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
     const MfAddr dn = refill ? vq_addr(rn, rbn) : vq_addr(rcur, rbc);
     // (FC1 at K = 7168 has the 17 registers this takes: B32 FC1 201.7 -> 199.1 us)
     UDec cur = decode(0, dn);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
+    static_for<0, NU>([&](auto U_) __attribute__((always_inline)) {
+      constexpr int u = decltype(U_)::value;
       UDec nxt;
       if (u + 1 < NU) nxt = decode(u + 1, dn);
       unit_mma(u, cur);
       if (u + 1 < NU) cur = nxt;
-    }
+    });
   };
 
   // MXFP4 tile (not in the ring): the groups of the wave's part of K load in passes of up
@@ -559,8 +559,8 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
       }
     };
     if (DB) mx_load(0);
-#pragma unroll
-    for (int h = 0; h < NPASS; ++h) {
+    static_for<0, NPASS>([&](auto H_) __attribute__((always_inline)) {
+      constexpr int h = decltype(H_)::value;
       if (!DB) mx_load(h);
       else if (h + 1 < NPASS) mx_load(h + 1);
       const int b = DB ? (h & 1) : 0;
@@ -573,7 +573,7 @@ __global__ __launch_bounds__((MfGeom<CPL, FC1>::THREADS), 1) void fc_mfma_kernel
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) mx_unit(gi, mx[b][j][m][nb].q, mx[b][j][m][nb].e, m, nb);
       }
-    }
+    });
   };
 
   // End of a tile: the waves' partial sums meet in LDS, then the outputs.  LDS

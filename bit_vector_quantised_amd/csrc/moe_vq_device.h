@@ -1,6 +1,8 @@
 // Device helpers shared by the MoE-VQ kernels (gfx950, wave64).
 #pragma once
 
+#include <type_traits>
+
 #include "moe_vq_internal.h"
 
 namespace mvq {
@@ -209,5 +211,14 @@ __device__ __forceinline__ float swiglu(float g, float u, float lim) {
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// f(integral_constant<int, I>) for I = B .. N - 1, in order.
+template <int B, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < N) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, N>(f);
+  }
+}
 
 }  // namespace mvq

@@ -190,15 +190,6 @@ __device__ __forceinline__ half8_t pf_decode(const uint2* tab, const PfCodes& c,
   return b;
 }
 
-// f(integral_constant<int, I>) for I = B .. N - 1, in order.
-template <int B, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < N) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, N>(f);
-  }
-}
-
 template <bool FC1>
 struct PfTile {
   int p_lo, mcnt, nt;
