@@ -278,26 +278,31 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
 
   // staging: thread tid stages 32 consecutive k of token row tid/4 (FC1: fp16 x; FC2:
   // the bf16 h that FC1 wrote, scaled by the pair's power-of-two factor into fp16)
+  //
+  // Every global load of the main loop is issued on every path: a load skipped on some
+  // path (a guard on the group index, or a row past the tile's tokens) makes the compiler
+  // count the loads in flight as on the shortest path, i.e. wait at the top of each group
+  // for the loads just issued for two groups ahead.  Group indices past the end are
+  // clamped (the loads re-read the last group), rows past the tile's tokens read the
+  // tile's first row and are stored as zeros.
   const int srow = tid >> 2, skq = (tid & 3) * 32;
-  const int sp = s_pair[srow];  // -1 past the tile's tokens
-  const bool stage = srow < NMB * 16;  // (one wave stages 16 rows: uniform per wave)
-  constexpr int AV = 4;         // 16-byte loads per thread per group
+  const int sp = s_pair[srow];                 // -1 past the tile's tokens
+  const int sp_ld = sp >= 0 ? sp : s_pair[0];  // (a tile holds at least one token)
+  const bool stage = srow < NMB * 16;          // (one wave stages 16 rows: uniform per wave)
+  constexpr int AV = 4;                        // 16-byte loads per thread per group
   auto a_load = [&](int g, uint4 (&v)[AV]) __attribute__((always_inline)) {
+    const uint4* src = FC1 ? reinterpret_cast<const uint4*>(a.x16 + (size_t)(sp_ld / a.k) * K + g * PF_KG + skq)
+                           : reinterpret_cast<const uint4*>(a.h + (size_t)sp_ld * K + g * PF_KG + skq);
 #pragma unroll
-    for (int i = 0; i < AV; ++i) v[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (sp >= 0) {
-      const uint4* src = FC1 ? reinterpret_cast<const uint4*>(a.x16 + (size_t)(sp / a.k) * K + g * PF_KG + skq)
-                             : reinterpret_cast<const uint4*>(a.h + (size_t)sp * K + g * PF_KG + skq);
-#pragma unroll
-      for (int i = 0; i < AV; ++i) v[i] = src[i];
-    }
+    for (int i = 0; i < AV; ++i) v[i] = src[i];
   };
   auto a_store = [&](int buf, const uint4 (&v)[AV]) __attribute__((always_inline)) {
     if (!stage) return;
     uint4* dst = reinterpret_cast<uint4*>(&As[buf][srow * PF_AROW + skq]);
+    const uint32_t keep = sp >= 0 ? 0xFFFFFFFFu : 0u;  // (a mask, not a select of operands)
     if (FC1) {
 #pragma unroll
-      for (int i = 0; i < AV; ++i) dst[i] = v[i];
+      for (int i = 0; i < AV; ++i) dst[i] = make_uint4(v[i].x & keep, v[i].y & keep, v[i].z & keep, v[i].w & keep);
     } else {
       // bf16 h -> fp16 with the pair's power-of-two factor
       const float f = s_fac[srow];
@@ -311,7 +316,7 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
           ow[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x0) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x1) << 16);
         }
-        dst[i] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        dst[i] = make_uint4(ow[0] & keep, ow[1] & keep, ow[2] & keep, ow[3] & keep);
       }
     }
   };
@@ -328,19 +333,19 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
       for (int nb = 0; nb < NB; ++nb) c[m][nb] = pf_load_codes<FMT>(qb[m], sb[m], rows[nb], K, g, kq);
   };
   codes_load(0, cs0);
-  if (NG > 1) codes_load(1, cs1);
+  codes_load(min(1, NG - 1), cs1);
   a_load(0, as0);
-  if (NG > 1) a_load(1, as1);
+  a_load(min(1, NG - 1), as1);
   a_store(0, as0);
   __syncthreads();
 
-  // group g: issue group g + 2, multiply group g, stage group g + 1's activations
+  // group g: issue group g + 2, multiply group g, stage group g + 1's activations (after
+  // the last group that store goes to the buffer no group reads again)
   auto body = [&](int g, const PfCodes (&cur)[NM][NB], PfCodes (&c_ahead)[NM][NB], const uint4 (&a_next)[AV],
                   uint4 (&a_ahead)[AV]) __attribute__((always_inline)) {
-    if (g + 2 < NG) {
-      codes_load(g + 2, c_ahead);
-      a_load(g + 2, a_ahead);
-    }
+    const int ga = min(g + 2, NG - 1);
+    codes_load(ga, c_ahead);
+    a_load(ga, a_ahead);
     const _Float16* Ab = As[g & 1];
     if constexpr (FMT == MOE_VQ_FMT_VQ2) {
       // The group's B fragments j = (S, m, nb) in order.  Fragment j's two table lookups
@@ -386,7 +391,7 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
           acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[S & 1][mb], bf, acc[m][nb][mb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       });
-      if (g + 1 < NG) a_store((g + 1) & 1, a_next);
+      a_store((g + 1) & 1, a_next);
       __syncthreads();
       return;
     }
@@ -410,14 +415,18 @@ __device__ __forceinline__ void pf_tile(const PrefillArgs& a, const PfTile<FC1>&
     step(std::integral_constant<int, 1>{});
     step(std::integral_constant<int, 2>{});
     step(std::integral_constant<int, 3>{});
-    if (g + 1 < NG) a_store((g + 1) & 1, a_next);
+    a_store((g + 1) & 1, a_next);
     __syncthreads();
   };
-  for (int g = 0; g < NG; g += 3) {
+  // three groups per iteration with no guard inside (see above), then the one or two left
+  int g = 0;
+  for (; g + 3 <= NG; g += 3) {
     body(g, cs0, cs2, as1, as2);
-    if (g + 1 < NG) body(g + 1, cs1, cs0, as2, as0);
-    if (g + 2 < NG) body(g + 2, cs2, cs1, as0, as1);
+    body(g + 1, cs1, cs0, as2, as0);
+    body(g + 2, cs2, cs1, as0, as1);
   }
+  if (g < NG) body(g, cs0, cs2, as1, as2);
+  if (g + 1 < NG) body(g + 1, cs1, cs0, as2, as0);
 }
 
 template <bool FC1>
