@@ -472,7 +472,7 @@ def main():
         traffic_from(args.traffic_from, args.config)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the routed-expert step is measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 

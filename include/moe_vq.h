@@ -69,7 +69,7 @@ extern "C" {
 enum moe_vq_status {
   MOE_VQ_OK = 0,
   MOE_VQ_EINVAL = 1,        /* bad argument (null pointer, bad size, bad enum)            */
-  MOE_VQ_EUNSUPPORTED = 2,  /* shape or dtype this build does not implement               */
+  MOE_VQ_EUNSUPPORTED = 2,  /* shape or dtype the library does not implement             */
   MOE_VQ_ENOSPACE = 3,      /* workspace smaller than moe_vq_workspace_bytes()            */
   MOE_VQ_EHIP = 4,          /* a HIP runtime call or kernel launch failed                 */
   MOE_VQ_ENOTRESIDENT = 5   /* (device) a selected expert's slot is absent or out of pool */
