@@ -84,7 +84,7 @@ def test_packed_slot_reads_back(fmt):
 
 def test_pack_slot_refuses_arrays_of_another_format():
     # arrays of one format packed under another slot format would fill only part of
-    # the slot; the builder must refuse, and draw the expert in the slot's format instead
+    # the slot; the packer must refuse, and the layer draws the expert in the slot's format instead
     cfg = synth.PRESETS["tiny"]
     ex = synth.draw_expert(cfg, 1, synth.FMT_VQ2)
     with pytest.raises(ValueError):
