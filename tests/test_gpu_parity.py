@@ -13,7 +13,7 @@ import synth
 from bit_vector_quantised_amd import _lib
 from bit_vector_quantised_amd.layer import DeviceLayer, Step
 
-from gpu_util import bf16_rne_bits, compare, decode_on_gpu, run, say
+from gpu_util import bf16_rne_bits, compare, decode_on_gpu, run, run_prefill, say
 
 pytestmark = pytest.mark.gpu
 
@@ -262,6 +262,49 @@ def test_slot_outside_pool_is_reported(tiny):
     dev.set_slots(offs, dev.formats)
     g = run(dev, x, "f32")
     assert g["status"] == _lib.ENOTRESIDENT
+
+
+# ---------------------------------------------------------------------------------
+# The largest expert count and top-k the library takes (1024 experts, top-32), on a
+# narrow layer: the one-token worklist, the fused and the separate top-k, the
+# matrix-core router from 64 tokens on, and prefill
+# ---------------------------------------------------------------------------------
+
+MAXE = synth.Config("maxe", 5, 128, 128, 1024, 32, "bf16", "normal", seed=9191)
+
+
+@pytest.fixture(scope="module")
+def maxe():
+    syn = synth.SynthLayer(MAXE)
+    return syn, DeviceLayer.from_synth(syn)
+
+
+@pytest.mark.parametrize("T", [1, 5, 40, 80])
+def test_max_experts_and_top_k(maxe, T):
+    syn, dev = maxe
+    x = syn.x(n=T, stream=130 + T)
+    say(f"maxe step T={T}")
+    g = run(dev, x, "bf16")
+    assert g["status"] == _lib.OK
+    compare(syn, x, "bf16", g, MAXE.top_k)
+    info = g["step"].info(T)
+    assert info["n_pairs"] == T * MAXE.top_k
+    assert info["experts"] == sorted(set(g["ids"].reshape(-1).tolist()))
+
+
+def test_max_experts_and_top_k_mixed_formats_and_prefill(maxe):
+    syn, _ = maxe
+    fm = [synth.FMT_MXFP4 if e % 5 == 0 else synth.FMT_VQ2 for e in range(MAXE.n_experts)]
+    v, dev = tiny_variant(syn, formats=fm)
+    x = syn.x(n=70, stream=150)
+    say("maxe mixed T=70")
+    g = run(dev, x, "bf16")
+    assert g["status"] == _lib.OK
+    compare(v, x, "bf16", g, MAXE.top_k)
+    say("maxe mixed prefill T=70")
+    gp = run_prefill(dev, x, "bf16")
+    assert gp["status"] == _lib.OK
+    compare(v, x, "bf16", gp, MAXE.top_k, check_h=False)
 
 
 # ---------------------------------------------------------------------------------
