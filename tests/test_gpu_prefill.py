@@ -12,7 +12,7 @@ import synth
 from bit_vector_quantised_amd import _lib
 from bit_vector_quantised_amd.layer import DeviceLayer, Step
 
-from gpu_util import compare, run, run_prefill, say
+from gpu_util import compare, run, run_prefill, say, x_tensor
 from test_gpu_parity import MINI, tiny_variant
 
 pytestmark = pytest.mark.gpu
@@ -167,3 +167,48 @@ def test_p4096_prefill_sampled_tokens(p4096):
     assert len(tokens) >= 32
     res = compare(syn, x, "bf16", g, 8, tokens=tokens, check_h=False)
     say("p4096", {k: v for k, v in res.items() if k != "ref"})
+
+
+def test_max_tokens_decode_and_prefill(p4096):
+    # The largest token count a step takes (65536 tokens, 524288 routed pairs) at the full
+    # layer shape: per-pair outputs then hold 3.8e9 floats, past 32-bit indexing.  The
+    # decode path (route, FC1, FC2) and prefill run on all tokens; sampled tokens, the
+    # first and last among them, are compared with the oracle.
+    syn, dev = p4096
+    T = 65536
+    assert T == 65536 and T * 8 * 7168 > 2 ** 31
+    say("drawing 65536 tokens")
+    x = syn.x(n=T, stream=65536)
+    xt = x_tensor(x, "bf16")
+    st = Step(dev, T)
+    rng = np.random.default_rng(65536)
+    tokens = np.array(sorted({0, 1, T // 2, T - 2, T - 1} | {int(t) for t in rng.choice(T, 11, replace=False)}))
+    k = dev.top_k
+    ti = torch.from_numpy(tokens).cuda()
+    pi = (ti[:, None] * k + torch.arange(k, device=ti.device)[None, :]).reshape(-1)
+
+    def sampled(with_h):
+        torch.cuda.synchronize()
+        g = {"ids": st.ids[ti].cpu().numpy().astype(np.int64), "w": st.w[ti].cpu().numpy().astype(np.float64),
+             "y": st.y[ti].cpu().numpy().astype(np.float64)}
+        if with_h:
+            g["h"] = st.h[pi].cpu().numpy().astype(np.float64).reshape(len(tokens), k, -1)
+        return g
+
+    say("T=65536 decode")
+    st.forward(xt)
+    status, _ = st.check()
+    assert status == _lib.OK
+    assert st.info(T)["n_pairs"] == T * k
+    g = sampled(True)
+    compare(syn, x[tokens], "bf16", g, k)
+    say("T=65536 prefill")
+    st.route(xt)
+    st.prefill(xt)
+    status, _ = st.check()
+    assert status == _lib.OK
+    gp = sampled(False)
+    assert np.array_equal(gp["ids"], g["ids"])
+    compare(syn, x[tokens], "bf16", gp, k, check_h=False)
+    del st, xt
+    torch.cuda.empty_cache()
