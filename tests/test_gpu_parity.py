@@ -125,6 +125,29 @@ def test_tiny_bf16_activations(tiny):
     compare(syn, xb, "bf16", g, syn.cfg.top_k)
 
 
+def test_empty_batch_is_a_no_op(tiny):
+    """Zero tokens: every compute call returns OK without launching or writing anything
+    (null pointers are allowed then), and the next step is unaffected."""
+    syn, dev = tiny
+    st = Step(dev, 4)
+    bufs = (st.ids, st.w, st.h, st.y)
+    for b in bufs:
+        b.fill_(7)
+    L, s = dev.c, st.stream()
+    _lib.route_topk(L, 0, _lib.F32, 0, 0, 0, 0, 0, s)
+    _lib.fc1_silu(L, 0, _lib.BF16, 0, 0, 0, 0, s)
+    _lib.fc2_combine(L, 0, 0, 0, 0, 0, s)
+    _lib.prefill_gemm(L, 0, _lib.F32, 0, 0, 0, 0, s)
+    _lib.forward(L, 0, _lib.F32, 0, 0, 0, 0, 0, 0, 0, s)
+    _lib.forward_static(L, 0, _lib.BF16, 0, 0, 0, 0, 0, 0, s)
+    torch.cuda.synchronize()
+    assert all(bool((b == 7).all()) for b in bufs)
+    x = syn.x()
+    g = run(dev, x, "f32", step=st)
+    assert g["status"] == _lib.OK
+    compare(syn, x, "f32", g, syn.cfg.top_k)
+
+
 def test_zero_input_selects_lowest_ids(tiny):
     """x = 0: all logits tie, so the experts are 0..k-1 with weight 1/k, and y = 0."""
     syn, dev = tiny
