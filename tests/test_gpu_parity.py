@@ -398,6 +398,28 @@ def test_mini_fp32_activations(mini):
 WIDE = synth.Config("wide", 40, 7168, 2048, 4, 2, "bf16", "normal", seed=4343)
 
 
+def test_wide_fp32_activations_decode_and_prefill():
+    # fp32 x at the full hidden size (seven 1024-column slices, each with its own
+    # power-of-two factor when staged): the fp32 router, the one-token and the matrix-core
+    # FC1 at K = 7168, and prefill's fp32 staging.  x = bf16 values times 1.37, so the
+    # values are not bf16.
+    syn = synth.SynthLayer(WIDE, cache=False)
+    dev = DeviceLayer.from_synth(syn)
+    for T in (1, 17, 40):
+        x = oracle.x_value(syn.x(n=T, stream=160 + T), "bf16").astype(np.float32) * np.float32(1.37)
+        say(f"wide fp32 T={T}")
+        g = run(dev, x, "f32")
+        assert g["status"] == _lib.OK
+        compare(syn, x, "f32", g, WIDE.top_k)
+        if T == 40:
+            say("wide fp32 prefill T=40")
+            gp = run_prefill(dev, x, "f32")
+            assert gp["status"] == _lib.OK
+            compare(syn, x, "f32", gp, WIDE.top_k, check_h=False)
+    del dev
+    torch.cuda.empty_cache()
+
+
 def test_wide_experts_split_into_token_groups():
     syn = synth.SynthLayer(WIDE, cache=False)
     dev = DeviceLayer.from_synth(syn)
